@@ -1,0 +1,199 @@
+/*
+ * specverify.h -- C ABI of an MI355X (gfx950) library for batched
+ * speculative-decoding verification over full-vocabulary logits.
+ *
+ * The method comes from three pages:
+ *   [SD]  "Speculative Decoding: как черновая модель ускоряет генерацию LLM
+ *          без потери качества" (zer0kernel forum post): the draft/verify loop
+ *          and the lossless accept/resample rule, sections "Основная идея:
+ *          черновик и верификация" and "Математика верификации".
+ *   [FLy] "Training-Free Loosely Speculative Decoding: Accepting Semantically
+ *          Correct Drafts Beyond Exact Match" (gist.science summary): the
+ *          entropy gate and deferral window, section "2. Metodologia",
+ *          part "A. Mecanismo de Verificacao de Dois Niveis".
+ *   [AV]  "Verificacion Adaptativa sin una cabeza de confianza" (spke.com):
+ *          the online acceptance estimator sigmoid(omega*logit(q_max)+beta_i),
+ *          sections "Solucion", "Puntuar la Distribucion", "Ajuste de los
+ *          Coeficientes" and footnote 1 ("Notas al pie").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named as device pointers must point to HIP device memory (or
+ *    memory the device can read).  The library allocates nothing: every
+ *    buffer, including scratch ("workspace"), belongs to the caller.
+ *  - Logits are rows of `vocab` values, row r of a tensor starting at
+ *    base + r*row_stride elements.  dtype SPEC_DTYPE_F32 (float) or
+ *    SPEC_DTYPE_BF16 (bfloat16 bit patterns).  The base pointer must be
+ *    16-byte aligned and row_stride*sizeof(element) a multiple of 16.
+ *    Logits must be finite or -inf (a masked vocabulary entry); +inf and NaN
+ *    are not supported.  At least one entry per row must be finite.
+ *  - Every statistic is of the temperature-scaled distribution softmax(l/T).
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *    the null stream).  Arguments are validated on the host before anything
+ *    is enqueued: on any status other than SPEC_OK nothing was enqueued,
+ *    except SPEC_ERR_HIP, which reports a failed launch.
+ *  - Results are a pure function of the inputs, the seed and the parameters:
+ *    reductions run in a fixed order and no floating-point atomics are used.
+ *  - Calls on different streams may overlap if they share no output or
+ *    workspace memory.
+ *
+ * Randomness: Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit seed,
+ * counter (x>>2, position, sequence, stream tag), output word x&3; a draw r
+ * becomes u = (2*(r>>9)+1) * 2^-24.  The accept test at position j uses
+ * x = 0 and tag 1; the sampling race uses x = the vocabulary id and tag 2.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spec_status {
+    SPEC_OK = 0,
+    SPEC_ERR_ARG = -1,         /* invalid argument (null, range, alignment)   */
+    SPEC_ERR_UNSUPPORTED = -2, /* valid but outside what this build handles   */
+    SPEC_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
+    SPEC_ERR_HIP = -4          /* a HIP launch reported an error              */
+} spec_status;
+
+enum { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 };
+enum { SPEC_MODE_LOSSLESS = 0, SPEC_MODE_FLY = 1 };
+
+/* Problem description.  B sequences, each with K draft tokens, K draft rows
+ * and K+1 target rows (row K follows the last draft token). */
+typedef struct spec_params {
+    int32_t batch;      /* B >= 0                                            */
+    int32_t num_draft;  /* K, 1 <= K <= 64                                   */
+    int32_t vocab;      /* V >= 2                                            */
+    int32_t dtype;      /* SPEC_DTYPE_F32 or SPEC_DTYPE_BF16                 */
+    int64_t row_stride; /* elements between consecutive rows, >= V           */
+    float temperature;  /* T, 1e-4 <= T <= 1e4                               */
+    float fly_theta;    /* FLy entropy gate theta on h = H(p)/log V          */
+    int32_t fly_window; /* FLy deferral window W, 0 <= W <= 2^20             */
+    int32_t reserved;   /* must be 0                                         */
+} spec_params;
+
+/* Outputs of spec_verify.  accepted_len and tokens are required; every
+ * statistics pointer may be NULL.  Rows that a call does not read (target
+ * rows past kept_len, draft rows at or past kept_len) are reported as NaN
+ * and -1. */
+typedef struct spec_verify_out {
+    int32_t *accepted_len;   /* [B] draft tokens accepted, 0..kept_len          */
+    int32_t *tokens;         /* [B][K+1] emitted tokens: the accepted drafts,
+                                then one replacement or bonus token, then -1   */
+    float *target_lse;       /* [B][K+1] log-sum-exp of l/T                      */
+    float *target_entropy;   /* [B][K+1] normalised entropy h = H/log V          */
+    int32_t *target_argmax;  /* [B][K+1] top token, lowest id on ties            */
+    float *draft_lse;        /* [B][K] (only when spec_verify reads draft rows)  */
+    float *draft_qmax;       /* [B][K] probability of the draft's top token      */
+    float *draft_feat;       /* [B][K] logit(q_max), clamped to <= 126 log 2     */
+} spec_verify_out;
+
+/* Bytes of device workspace spec_verify needs for `params` (0 if invalid). */
+size_t spec_workspace_bytes(const spec_params *params);
+
+/* Bytes of the draft-statistics buffer that spec_av_score fills and
+ * spec_verify / spec_av_update read, for B sequences of K drafts.  Layout
+ * (n = B*K, entry b*K+j): double lse2[n] (log2-sum of 2^(l*c), c = log2(e)/T),
+ * double logq2[n] (log2 q(x_j)), float qmax[n], float feat[n]. */
+size_t spec_draft_stats_bytes(int32_t batch, int32_t num_draft);
+
+/*
+ * spec_verify -- verify K draft tokens per sequence against the target.
+ *
+ * target       device, [B][K+1] rows of logits.
+ * draft        device, [B][K] rows of draft logits.  Required in lossless
+ *              mode unless draft_stats is given; ignored in FLy mode.
+ * draft_tokens device, int32 [B][K].  A token outside [0, V) has p = q = 0:
+ *              it is rejected in lossless mode and counts as a deviation in
+ *              FLy mode.
+ * kept_len     device, int32 [B] or NULL (= K).  Number of leading drafts
+ *              that go to verification after adaptive-verification trimming;
+ *              values outside [0, K] are clamped.  Only target rows 0..L and
+ *              draft rows 0..L-1 are read.
+ * draft_stats  device or NULL: the buffer filled by spec_av_score for the
+ *              same drafts and temperature; then draft rows are not read.
+ * seed         key of every random draw.
+ * mode         SPEC_MODE_LOSSLESS: position by position accept x_j when
+ *              u_j < p(x_j)/q(x_j) (probability min(1, p/q), [SD] section
+ *              "Математика верификации"); at the first rejection emit a token
+ *              drawn from norm(max(0, p - q)); if all L verified drafts are
+ *              accepted emit a token drawn from p at row L (the bonus token
+ *              when L = K, the target's own sample at the trim point when
+ *              L < K, [AV] footnote 1).  Draws use the exponential race
+ *              argmax_x w(x)/E_x with E_x = -ln u_x.
+ *              SPEC_MODE_FLY: greedy exact match relaxed by FLy's entropy gate
+ *              and deferral window ([FLy] part A): a deviation (draft token !=
+ *              target top token) with h < theta is rejected; one with
+ *              h >= theta is accepted when the next W drafts all match and lie
+ *              inside the draft, else rejected.  The replacement / bonus token
+ *              is the target's top token at that row.  Deterministic.
+ * params       problem description (host pointer).
+ * out          output pointers (host struct of device pointers).
+ * workspace    device scratch of at least spec_workspace_bytes(params) bytes,
+ *              owned by the caller; its contents on entry do not matter.
+ * stream       hipStream_t to enqueue on.
+ */
+spec_status spec_verify(const void *target, const void *draft, const int32_t *draft_tokens,
+                        const int32_t *kept_len, const void *draft_stats, uint64_t seed,
+                        int32_t mode, const spec_params *params, const spec_verify_out *out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * spec_av_score -- adaptive-verification confidence and trimming ([AV]
+ * sections "Solucion" and "Puntuar la Distribucion"; survival as the running
+ * product over positions from section "Otras Caracteristicas Consideradas").
+ *
+ * Reads every draft row once and, per sequence b and position i < K:
+ *   c_i = sigmoid(omega * logit(q_max,i) + beta_i)   -> conf[b][i]
+ *   P_i = c_0 * ... * c_i;  keep while P_i >= tau     -> keep_mask, kept_len
+ * tau <= 0 keeps every position.  omega_beta: device float[K+1] =
+ * (omega, beta_0..beta_{K-1}).  conf (float [B][K]), keep_mask (uint8
+ * [B][K]) and kept_len (int32 [B]) may each be NULL.  draft_stats (device,
+ * spec_draft_stats_bytes) is required and receives the draft-row statistics
+ * for spec_verify and spec_av_update.  draft_tokens (device int32 [B][K]) is
+ * required.  params->fly_* are ignored.
+ */
+spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,
+                          const spec_params *params, const float *omega_beta, float tau,
+                          float *conf, uint8_t *keep_mask, int32_t *kept_len, void *draft_stats,
+                          void *stream);
+
+/*
+ * spec_av_update -- one online SGD step of the estimator ([AV] section
+ * "Ajuste de los Coeficientes" for the labels: drafts up to and including the
+ * first rejection; accepted = 1, the first rejected = 0, nothing else
+ * labelled).  With N labels over the batch and s_n the pre-step prediction:
+ *   omega  -= lr * (1/N) sum_n (s_n - y_n) feat_n
+ *   beta_i -= lr * (1/N) sum_{n at position i} (s_n - y_n)
+ * N = 0 leaves the parameters unchanged.  draft_stats: filled by
+ * spec_av_score; accepted_len: from spec_verify; kept_len: device int32 [B]
+ * or NULL (= K); omega_beta: device float[K+1], updated in place.  Single
+ * workgroup, fixed-order double-precision reduction.
+ */
+spec_status spec_av_update(const void *draft_stats, const int32_t *accepted_len,
+                           const int32_t *kept_len, int32_t batch, int32_t num_draft, float lr,
+                           float *omega_beta, void *stream);
+
+/*
+ * spec_row_stats -- the streaming row pass on its own: per row of V logits,
+ * log-sum-exp of l/T (lse), normalised entropy (entropy), top token (argmax,
+ * lowest id on ties), top-token probability (qmax) and its log-odds (feat,
+ * clamped to <= 126 log 2).  `rows` rows starting at `logits`; every output
+ * is a device array of `rows` entries and may be NULL.
+ */
+spec_status spec_row_stats(const void *logits, int64_t rows, int32_t vocab, int64_t row_stride,
+                           int32_t dtype, float temperature, float *lse, float *entropy,
+                           int32_t *argmax, float *qmax, float *feat, void *stream);
+
+/* Static description of a status code. */
+const char *spec_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
