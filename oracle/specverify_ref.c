@@ -115,29 +115,31 @@ static void row_stats_one(const void *row, int dtype, int64_t V, double T, row_s
             am = x;
         }
     }
-    /* lse = m + log sum_x exp(z_x - m) */
-    double s = 0.0;
-    for (int64_t x = 0; x < V; ++x) s += exp(load_logit(row, dtype, x) / T - m);
-    double lse = m + log(s);
-    /* H = -sum_x p_x log p_x with p_x = exp(z_x - lse); p_x = 0 adds nothing */
-    double H = 0.0;
-    for (int64_t x = 0; x < V; ++x) {
-        double lp = load_logit(row, dtype, x) / T - lse;
-        double p = exp(lp);
-        if (p > 0.0) H -= p * lp;
-    }
-    /* q_max = exp(m - lse); logit(q_max) = log q_max - log(1 - q_max)
-     *       = -log(sum over the other ids of exp(z_x - m)), an exact rewrite
-     * that avoids forming 1 - q_max. */
+    /* r = sum over the ids other than the argmax of exp(z_x - m); the argmax
+     * itself contributes exp(0) = 1, so sum_x exp(z_x - m) = 1 + r exactly.
+     * lse = m + log(1 + r), evaluated as m + log1p(r). */
     double r = 0.0;
     for (int64_t x = 0; x < V; ++x)
         if (x != am) r += exp(load_logit(row, dtype, x) / T - m);
+    const double l1p = log1p(r);
+    double lse = m + l1p;
+    /* H = -sum_x p_x log p_x with log p_x = z_x - lse, formed as
+     * (z_x - m) - log(1 + r) so that the argmax's log p = -log1p(r) keeps
+     * its precision when q_max is close to 1; p_x = 0 adds nothing. */
+    double H = 0.0;
+    for (int64_t x = 0; x < V; ++x) {
+        double lp = (load_logit(row, dtype, x) / T - m) - l1p;
+        double p = exp(lp);
+        if (p > 0.0) H -= p * lp;
+    }
+    /* q_max = exp(m - lse) = 1/(1 + r); logit(q_max) = log q_max - log(1 - q_max)
+     * = -log r, an exact rewrite that avoids forming 1 - q_max. */
     st->m = m;
     st->lse = lse;
     st->H = H;
     st->h = H / log((double)V);
     st->argmax = am;
-    st->qmax = exp(m - lse);
+    st->qmax = 1.0 / (1.0 + r);
     st->feat = -log(r > FEAT_CLAMP_R ? r : FEAT_CLAMP_R);
 }
 

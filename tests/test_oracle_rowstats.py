@@ -77,17 +77,43 @@ def test_random_rows_vs_scipy(oracle, T):
     assert np.allclose(st["feat"], special.logit(q), rtol=1e-9)
 
 
-def test_entropy_tiny_is_accurate(oracle):
-    # A very peaked row: H small; relative accuracy must hold, not just absolute.
+def _exact_stats(row, T):
+    """lse, H and logit(q_max) of one row in 60-digit decimal arithmetic."""
+    import decimal
+    D = decimal.Decimal
+    ctx = decimal.Context(prec=60)
+    z = [ctx.divide(D(float(v)), D(float(T))) for v in row if np.isfinite(v)]
+    m = max(z)
+    e = [ctx.exp(zi - m) for zi in z]
+    s = ctx.add(sum(e, D(0)), D(0))
+    r = s - 1  # the maximum contributes exp(0) = 1 (no tie at the top)
+    ln_s = ctx.ln(s)
+    H = sum((ei / s) * (ln_s - (zi - m)) for ei, zi in zip(e, z))
+    return float(m + ln_s), float(H), float(-ctx.ln(r))
+
+
+@pytest.mark.parametrize("peak,T", [(40.0, 1.0), (30.0, 0.7), (25.0, 1.0), (8.0, 1.0)])
+def test_entropy_of_peaked_rows_is_accurate(oracle, peak, T):
+    # Near-one-hot rows: H and 1 - q_max are ~1e-13; relative accuracy must hold.
+    rng = np.random.default_rng(int(peak))
+    x = (rng.standard_normal((1, 997)) * 3).astype(np.float32)
+    x[0, 17] += np.float32(peak)
+    st = oracle.rows_stats(x, temperature=T)
+    lse, H, feat = _exact_stats(x[0], T)
+    assert st["lse"][0] == pytest.approx(lse, rel=1e-14)
+    assert st["H"][0] == pytest.approx(H, rel=1e-9)
+    assert st["feat"][0] == pytest.approx(feat, rel=1e-12)
+
+
+def test_entropy_closed_form_near_one_hot(oracle):
+    # one logit 40, 999 logits 0: r = 999 e^-40, H = log1p(r) + 40 r / (1 + r)
     x = np.zeros((1, 1000), dtype=np.float32)
     x[0, 17] = 40.0
     st = oracle.rows_stats(x)
-    e = math.exp(-40.0)
-    Z = 1 + 999 * e
-    H = -(1 / Z) * math.log(1 / Z) - 999 * (e / Z) * math.log(e / Z)
-    assert st["H"][0] == pytest.approx(H, rel=1e-9)
-    # logit(q_max) = -log(999 e^-40) without cancellation
+    r = 999 * math.exp(-40.0)
+    assert st["H"][0] == pytest.approx(math.log1p(r) + 40.0 * r / (1 + r), rel=1e-12)
     assert st["feat"][0] == pytest.approx(40.0 - math.log(999), rel=1e-14)
+    assert st["lse"][0] == pytest.approx(40.0 + math.log1p(r), rel=1e-15)
 
 
 def test_bf16_decoding(oracle):
