@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of batched speculative-decoding verification on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one verification call over one batch of synthetic logits that
+already sits in HBM.  The headline workload is FLy loose-greedy verification
+of B=256 sequences x K=8 drafts over V=128256 bfloat16 logits (2304 target
+rows, 591 MB per call); two input sets alternate so that no call finds its
+rows in the 256 MB last-level cache.  Prints one JSON line.
+
+Besides the headline it reports:
+  roofline      the streaming row pass (the dominant kernel) timed per launch
+                with HIP events on the launch stream: algorithmic bytes /
+                kernel time against the 8 TB/s HBM peak; `traffic` comes from
+                rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded under
+                profiles/ for the same kernel source, else null;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
+  secondary     the other verification workloads (lossless with adaptive
+                verification, lossless at T=0.7 on V=152064, the full
+                adaptive-verification step loop, lossless at the headline
+                shape), each timed the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified logits rows/s and achieved HBM GB/s (% peak), V=128256 bf16, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+ROW_PASS_SOURCES = ["draft_token_verification_vocab_amd/csrc/sv_rowstats.hpp",
+                    "draft_token_verification_vocab_amd/csrc/sv_common.hpp",
+                    "draft_token_verification_vocab_amd/csrc/specverify.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_pass_fly_b256_k8_v128256_bf16.traffic.json")
+
+
+def row_pass_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in ROW_PASS_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verification hot path runs on a single MI355X "
+              "(multi-GPU sharding is a design note, not built); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import draft_token_verification_vocab_amd as sv
+    from draft_token_verification_vocab_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sv.load()
+
+    # ------------------------------------------------------------------ headline
+    cfg = W.CONFIGS[2]
+    B, K, V = cfg["B"], cfg["K"], cfg["V"]
+    log("generating two input sets of %s on the GPU" % cfg["name"])
+    sets = [W.make(2, device=dev, step=s) for s in range(2)]
+    rows = B * (K + 1)
+    row_bytes = V * 2
+    bytes_per_step = rows * row_bytes
+    ws = torch.empty(sv.workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    outs = [sv.VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                            torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+            for _ in sets]
+
+    def step(i):
+        b = sets[i % 2]
+        sv.verify(b.target, None, b.tokens, seed=0, mode=sv.MODE_FLY, fly_theta=cfg["theta"],
+                  fly_window=cfg["window"], workspace=ws, out=outs[i % 2])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    rows_per_s = rows / (ms * 1e-3)
+    gbps = bytes_per_step / (ms * 1e-3) / 1e9
+    acc_mean = float(torch.cat([o.accepted_len for o in outs]).float().mean().item())
+    log("headline: %.1f us/step, %.3g rows/s, %.0f GB/s" % (ms * 1e3, rows_per_s, gbps))
+
+    # ------------------------------------------------------------- roofline
+    # The same row-pass kernel and launch shape as the headline's first launch
+    # (target rows, entropy + argmax), timed launch by launch on its stream.
+    flat = [s.target.view(rows, V) for s in sets]
+    st_out = {k: torch.empty(rows, dtype=dt, device=dev) for k, dt in
+              (("lse", torch.float32), ("entropy", torch.float32), ("argmax", torch.int32))}
+    L = sv.load()
+    import ctypes
+
+    def row_launch(i):
+        x = flat[i % 2]
+        st = L.spec_row_stats(ctypes.c_void_p(x.data_ptr()), rows, V, V, sv.DTYPE_BF16, 1.0,
+                              ctypes.c_void_p(st_out["lse"].data_ptr()),
+                              ctypes.c_void_p(st_out["entropy"].data_ptr()),
+                              ctypes.c_void_p(st_out["argmax"].data_ptr()), None, None,
+                              ctypes.c_void_p(stream.cuda_stream))
+        assert st == 0
+
+    for i in range(args.warmup):
+        row_launch(i)
+    n_k = max(args.steps, 20)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_k)]
+    torch.cuda.synchronize()
+    for i in range(n_k):
+        evs[i][0].record(stream)
+        row_launch(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    achieved = bytes_per_step / (kms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == row_pass_source_hash():
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "row_stats_kernel<bf16,512,4,entropy>", "kernel_us": round(kms * 1e3, 2),
+                "algorithmic_bytes_per_launch": bytes_per_step,
+                "source_hash": row_pass_source_hash()}
+    log("row pass: %.1f us/launch, %.0f GB/s (%.1f%% of peak)" % (kms * 1e3, achieved,
+                                                                  100 * achieved / HBM_PEAK_GBPS))
+
+    # ---------------------------------------------------------- secondary
+    secondary = {}
+    if not args.no_secondary:
+        secondary = run_secondary(sv, W, dev, stream, args)
+
+    # -------------------------------------------------------- cpu baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(sets[0], cfg, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC, "value": round(rows_per_s, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "mode": "fly", "B": B, "K": K, "V": V,
+                   "logits": "bf16", "theta": cfg["theta"], "window": cfg["window"],
+                   "rows_per_step": rows, "bytes_per_step": bytes_per_step,
+                   "input_sets": 2},
+        "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "mean_accepted_len": round(acc_mean, 4),
+        "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def _timeit(fn, n, warm, stream, torch):
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def run_secondary(sv, W, dev, stream, args):
+    import torch
+    out = {}
+    n = max(5, min(args.steps, 20))
+
+    # lossless verification at the headline shape (target + draft rows)
+    b0 = W.gaussian(256, 8, 128256, "bf16", 1.0, seed=77, token_seed=0, device=dev)
+    b1 = W.gaussian(256, 8, 128256, "bf16", 1.0, seed=78, token_seed=1, device=dev)
+    bs = [b0, b1]
+    ws = torch.empty(sv.workspace_bytes(256, 8, 128256), dtype=torch.uint8, device=dev)
+    res = [None, None]
+
+    def f(i):
+        b = bs[i % 2]
+        res[i % 2] = sv.verify(b.target, b.draft, b.tokens, seed=i, workspace=ws)
+    ms = _timeit(f, n, 2, stream, torch)
+    rows = 256 * 17
+    byt = rows * 128256 * 2
+    out["lossless_b256_k8_v128256_bf16"] = _line(ms, rows, byt, res)
+    del bs, b0, b1
+
+    # c1: lossless + AV score + one SGD step, B=64 K=5
+    c = W.CONFIGS[1]
+    sets = [W.make(1, device=dev, step=s) for s in range(4)]
+    K = c["K"]
+    ob = torch.tensor(W.av_init(1), dtype=torch.float32, device=dev)
+    ws1 = torch.empty(sv.workspace_bytes(64, K, c["V"]), dtype=torch.uint8, device=dev)
+    res = [None] * 4
+
+    def f1(i):
+        b = sets[i % 4]
+        conf, mask, kept, ds = sv.av_score(b.draft, b.tokens, ob, c["av"]["tau"])
+        r = sv.verify(b.target, b.draft, b.tokens, seed=0, kept_len=kept, draft_stats=ds,
+                      workspace=ws1)
+        sv.av_update(ds, r.accepted_len, kept, ob, c["av"]["lr"], 64, K)
+        res[i % 4] = r
+    ms = _timeit(f1, n, 2, stream, torch)
+    rows = 64 * (2 * K + 1)
+    out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
+    del sets
+
+    # c3: lossless at T = 0.7 on V = 152064, B = 512 K = 4
+    c = W.CONFIGS[3]
+    sets = [W.make(3, device=dev, step=s) for s in range(2)]
+    ws3 = torch.empty(sv.workspace_bytes(512, 4, c["V"], temperature=0.7), dtype=torch.uint8,
+                      device=dev)
+    res = [None] * 2
+
+    def f3(i):
+        b = sets[i % 2]
+        res[i % 2] = sv.verify(b.target, b.draft, b.tokens, seed=0, temperature=0.7,
+                               workspace=ws3)
+    ms = _timeit(f3, n, 2, stream, torch)
+    rows = 512 * 9
+    out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
+    del sets
+
+    # c4: full AV pipeline step (score, trimmed verify, update), B=1024 K=8
+    c = W.CONFIGS[4]
+    sets = [W.make(4, device=dev, step=s) for s in range(2)]
+    K = c["K"]
+    ob = torch.tensor(W.av_init(4), dtype=torch.float32, device=dev)
+    ws4 = torch.empty(sv.workspace_bytes(1024, K, c["V"]), dtype=torch.uint8, device=dev)
+    res = [None] * 2
+    kept_hist = []
+
+    def f4(i):
+        b = sets[i % 2]
+        conf, mask, kept, ds = sv.av_score(b.draft, b.tokens, ob, c["av"]["tau"])
+        r = sv.verify(b.target, b.draft, b.tokens, seed=i, kept_len=kept, draft_stats=ds,
+                      workspace=ws4)
+        sv.av_update(ds, r.accepted_len, kept, ob, c["av"]["lr"], 1024, K)
+        res[i % 2] = r
+        kept_hist.append(kept)
+    ms = _timeit(f4, c["steps"], 2, stream, torch)
+    kept_all = torch.stack(kept_hist[-c["steps"]:]).float()
+    rows = 1024 * K + int((kept_all + 1).sum().item() / c["steps"])
+    line = _line(ms, rows, rows * c["V"] * 2, res)
+    line["mean_kept_len"] = round(float(kept_all.mean().item()), 4)
+    line["omega_beta_after"] = [round(v, 5) for v in ob.tolist()]
+    out[c["name"]] = line
+    del sets
+    torch.cuda.synchronize()
+    return out
+
+
+def _line(ms, rows, byt, res):
+    import torch
+    acc = torch.cat([r.accepted_len for r in res if r is not None]).float().mean().item()
+    return {"us_per_step": round(ms * 1e3, 2), "rows_per_step": rows,
+            "rows_per_s": round(rows / (ms * 1e-3), 1), "gbps": round(byt / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "mean_accepted_len": round(acc, 4)}
+
+
+def cpu_baseline(batch, cfg, budget_s):
+    """The CPU oracle (never tuned) on a bounded sample of the headline
+    workload: the first n sequences, grown until about budget_s of work."""
+    from oracle import ref
+    threads = ref.default_threads()
+    tgt = batch.target.cpu().view(__import__("torch").int16).numpy().view("uint16")
+    tok = batch.tokens.cpu().numpy()
+    n = 4
+    while True:
+        t = time.perf_counter()
+        ref.verify(tgt[:n], None, tok[:n], 0, ref.MODE_FLY, theta=cfg["theta"],
+                   window=cfg["window"], nthreads=threads)
+        dt = time.perf_counter() - t
+        if dt >= budget_s or n >= batch.target.shape[0]:
+            break
+        n = min(batch.target.shape[0], max(n * 2, int(n * budget_s / max(dt, 1e-3) * 0.9)))
+    rows = n * (cfg["K"] + 1)
+    return {"value": round(rows / dt, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d sequences (%d target rows) of %s, FLy mode, %.1f s" % (
+                n, batch.target.shape[0], rows, cfg["name"], dt)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,270 @@
+"""Batched speculative-decoding verification over full-vocabulary logits on
+AMD MI355X (gfx950).
+
+A thin ctypes binding of the HIP library ``libspecverify.so`` (C ABI in
+``include/specverify.h``).  This module only marshals arguments: it checks
+shapes, allocates outputs and workspace as torch tensors on the logits'
+device and passes raw device pointers plus the current HIP stream.  Every step
+of the computation runs in the library's kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "SpecVerifyError", "lib_path", "load", "verify", "av_score", "av_update", "row_stats",
+    "workspace_bytes", "draft_stats_bytes", "MODE_LOSSLESS", "MODE_FLY",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+MODE_LOSSLESS = 0
+MODE_FLY = 1
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_draft", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("row_stride", ctypes.c_int64), ("temperature", ctypes.c_float),
+                ("fly_theta", ctypes.c_float), ("fly_window", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class _VerifyOut(ctypes.Structure):
+    _fields_ = [("accepted_len", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
+                ("target_lse", ctypes.c_void_p), ("target_entropy", ctypes.c_void_p),
+                ("target_argmax", ctypes.c_void_p), ("draft_lse", ctypes.c_void_p),
+                ("draft_qmax", ctypes.c_void_p), ("draft_feat", ctypes.c_void_p)]
+
+
+# Every symbol the header declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "spec_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(_Params)]),
+    "spec_draft_stats_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
+    "spec_verify": (ctypes.c_int32, [_P, _P, _P, _P, _P, ctypes.c_uint64, ctypes.c_int32,
+                                     ctypes.POINTER(_Params), ctypes.POINTER(_VerifyOut), _P,
+                                     ctypes.c_size_t, _P]),
+    "spec_av_score": (ctypes.c_int32, [_P, _P, ctypes.POINTER(_Params), _P, ctypes.c_float,
+                                       _P, _P, _P, _P, _P]),
+    "spec_av_update": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_float, _P, _P]),
+    "spec_row_stats": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                        ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P, _P]),
+    "spec_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+}
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libspecverify.so")
+
+
+def load(path: Optional[str] = None):
+    """Load the HIP library (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or lib_path()
+    if not os.path.exists(p):
+        raise SpecVerifyError(
+            "%s is missing: build it with `python -m draft_token_verification_vocab_amd.build`"
+            % p)
+    L = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().spec_status_string(status).decode()
+        raise SpecVerifyError("%s failed: %s (status %d)" % (what, msg, status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError("logits must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _need_cuda(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _params(B, K, V, stride, dtype, temperature, theta=0.0, window=0) -> _Params:
+    return _Params(int(B), int(K), int(V), int(dtype), int(stride), float(temperature),
+                   float(theta), int(window), 0)
+
+
+def workspace_bytes(B, K, V, dtype=DTYPE_BF16, stride=None, temperature=1.0) -> int:
+    p = _params(B, K, V, stride or V, dtype, temperature)
+    return int(load().spec_workspace_bytes(ctypes.byref(p)))
+
+
+def draft_stats_bytes(B, K) -> int:
+    return int(load().spec_draft_stats_bytes(int(B), int(K)))
+
+
+@dataclass
+class VerifyResult:
+    accepted_len: torch.Tensor            # int32 [B]
+    tokens: torch.Tensor                  # int32 [B, K+1]
+    target_lse: Optional[torch.Tensor] = None
+    target_entropy: Optional[torch.Tensor] = None
+    target_argmax: Optional[torch.Tensor] = None
+    draft_lse: Optional[torch.Tensor] = None
+    draft_qmax: Optional[torch.Tensor] = None
+    draft_feat: Optional[torch.Tensor] = None
+
+
+def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+           seed: int, mode: int = MODE_LOSSLESS, *, temperature: float = 1.0,
+           fly_theta: float = 0.3, fly_window: int = 4, kept_len: Optional[torch.Tensor] = None,
+           draft_stats: Optional[torch.Tensor] = None, vocab: Optional[int] = None,
+           stats: bool = False, workspace: Optional[torch.Tensor] = None,
+           out: Optional[VerifyResult] = None) -> VerifyResult:
+    """Verify drafts.  target: [B, K+1, S] and draft: [B, K, S] logits (S >= V
+    is the row stride; V defaults to S), draft_tokens: int32 [B, K]."""
+    _need_cuda(target, "target")
+    B, K1, S = target.shape
+    K = K1 - 1
+    V = S if vocab is None else int(vocab)
+    dt = _dtype_code(target)
+    if draft is not None:
+        _need_cuda(draft, "draft")
+        if draft.shape != (B, K, S) or draft.dtype != target.dtype:
+            raise ValueError("draft must be [B, K, S] with the target's dtype")
+    _need_cuda(draft_tokens, "draft_tokens")
+    if draft_tokens.dtype != torch.int32 or draft_tokens.shape != (B, K):
+        raise ValueError("draft_tokens must be int32 [B, K]")
+    for t, n in ((kept_len, "kept_len"), (draft_stats, "draft_stats")):
+        if t is not None:
+            _need_cuda(t, n)
+    dev = target.device
+    p = _params(B, K, V, S, dt, temperature, fly_theta, fly_window)
+    L = load()
+    if out is None:
+        out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                           torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+        if stats:
+            out.target_lse = torch.empty(B, K + 1, dtype=torch.float32, device=dev)
+            out.target_entropy = torch.empty(B, K + 1, dtype=torch.float32, device=dev)
+            out.target_argmax = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+            if mode == MODE_LOSSLESS and draft_stats is None:
+                out.draft_lse = torch.empty(B, K, dtype=torch.float32, device=dev)
+                out.draft_qmax = torch.empty(B, K, dtype=torch.float32, device=dev)
+                out.draft_feat = torch.empty(B, K, dtype=torch.float32, device=dev)
+    o = _VerifyOut(*[None if t is None else t.data_ptr() for t in (
+        out.accepted_len, out.tokens, out.target_lse, out.target_entropy, out.target_argmax,
+        out.draft_lse, out.draft_qmax, out.draft_feat)])
+    need = int(L.spec_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(L.spec_verify(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(kept_len),
+                         _ptr(draft_stats), ctypes.c_uint64(int(seed) & (2**64 - 1)), int(mode),
+                         ctypes.byref(p), ctypes.byref(o), _ptr(workspace),
+                         workspace.numel(), _stream(dev)), "spec_verify")
+    return out
+
+
+def av_score(draft: torch.Tensor, draft_tokens: torch.Tensor, omega_beta: torch.Tensor,
+             tau: float, *, temperature: float = 1.0, vocab: Optional[int] = None,
+             draft_stats: Optional[torch.Tensor] = None):
+    """Adaptive-verification confidences.  Returns (conf [B,K] float,
+    keep_mask [B,K] uint8, kept_len [B] int32, draft_stats buffer)."""
+    _need_cuda(draft, "draft")
+    B, K, S = draft.shape
+    V = S if vocab is None else int(vocab)
+    dev = draft.device
+    _need_cuda(omega_beta, "omega_beta")
+    if omega_beta.dtype != torch.float32 or omega_beta.numel() != K + 1:
+        raise ValueError("omega_beta must be float32 [K+1]")
+    _need_cuda(draft_tokens, "draft_tokens")
+    if draft_tokens.dtype != torch.int32 or draft_tokens.shape != (B, K):
+        raise ValueError("draft_tokens must be int32 [B, K]")
+    p = _params(B, K, V, S, _dtype_code(draft), temperature)
+    L = load()
+    conf = torch.empty(B, K, dtype=torch.float32, device=dev)
+    mask = torch.empty(B, K, dtype=torch.uint8, device=dev)
+    kept = torch.empty(B, dtype=torch.int32, device=dev)
+    if draft_stats is None:
+        draft_stats = torch.empty(max(int(L.spec_draft_stats_bytes(B, K)), 16),
+                                  dtype=torch.uint8, device=dev)
+    _check(L.spec_av_score(_ptr(draft), _ptr(draft_tokens), ctypes.byref(p), _ptr(omega_beta),
+                           float(tau), _ptr(conf), _ptr(mask), _ptr(kept), _ptr(draft_stats),
+                           _stream(dev)), "spec_av_score")
+    return conf, mask, kept, draft_stats
+
+
+def draft_stats_view(draft_stats: torch.Tensor, B: int, K: int):
+    """Named views of the draft-statistics buffer (lse2, logq2, qmax, feat)."""
+    n = B * K
+    raw = draft_stats[:24 * n]
+    return {"lse2": raw[:8 * n].view(torch.float64), "logq2": raw[8 * n:16 * n].view(torch.float64),
+            "qmax": raw[16 * n:20 * n].view(torch.float32),
+            "feat": raw[20 * n:24 * n].view(torch.float32)}
+
+
+def av_update(draft_stats: torch.Tensor, accepted_len: torch.Tensor,
+              kept_len: Optional[torch.Tensor], omega_beta: torch.Tensor, lr: float, B: int,
+              K: int) -> torch.Tensor:
+    """One SGD step of the estimator; omega_beta (float32 [K+1]) is updated in place."""
+    for t, n in ((draft_stats, "draft_stats"), (accepted_len, "accepted_len"),
+                 (omega_beta, "omega_beta")):
+        _need_cuda(t, n)
+    if kept_len is not None:
+        _need_cuda(kept_len, "kept_len")
+    _check(load().spec_av_update(_ptr(draft_stats), _ptr(accepted_len), _ptr(kept_len), int(B),
+                                 int(K), float(lr), _ptr(omega_beta),
+                                 _stream(omega_beta.device)), "spec_av_update")
+    return omega_beta
+
+
+def row_stats(logits: torch.Tensor, *, temperature: float = 1.0, vocab: Optional[int] = None,
+              lse: bool = True, entropy: bool = True, argmax: bool = True, qmax: bool = False,
+              feat: bool = False) -> dict:
+    """Per-row statistics of a [rows, S] logits tensor (first V columns)."""
+    _need_cuda(logits, "logits")
+    x = logits.reshape(-1, logits.shape[-1])
+    rows, S = x.shape
+    V = S if vocab is None else int(vocab)
+    dev = x.device
+    res = {}
+    for k, want, dt in (("lse", lse, torch.float32), ("entropy", entropy, torch.float32),
+                        ("argmax", argmax, torch.int32), ("qmax", qmax, torch.float32),
+                        ("feat", feat, torch.float32)):
+        res[k] = torch.empty(rows, dtype=dt, device=dev) if want else None
+    _check(load().spec_row_stats(_ptr(x), rows, V, S, _dtype_code(x), float(temperature),
+                                 _ptr(res["lse"]), _ptr(res["entropy"]), _ptr(res["argmax"]),
+                                 _ptr(res["qmax"]), _ptr(res["feat"]), _stream(dev)),
+           "spec_row_stats")
+    return {k: v for k, v in res.items() if v is not None}

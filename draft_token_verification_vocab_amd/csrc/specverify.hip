@@ -1,0 +1,367 @@
+// specverify.hip -- host side of the C ABI declared in include/specverify.h:
+// argument validation, workspace layout, kernel selection and launches on
+// the caller's stream.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "specverify.h"
+#include "sv_av.hpp"
+#include "sv_common.hpp"
+#include "sv_finish.hpp"
+#include "sv_rowstats.hpp"
+
+namespace {
+
+using namespace sv;
+
+// Row pass shape: threads per workgroup and 16-byte vectors per thread per
+// chunk (one chunk = UNROLL*8 bfloat16 or UNROLL*4 float logits).
+constexpr int kRowBlock = 512;
+constexpr int kRowUnroll = 4;
+// Race shape and the number of race workgroups to aim for per launch.
+constexpr int kRaceBlock = 256;
+constexpr int kRaceTargetBlocks = 2048;
+constexpr int kMaxSegs = 64;
+constexpr int kSmallBlock = 64;
+
+size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+int elem_size(int32_t dtype) { return dtype == SPEC_DTYPE_F32 ? 4 : 2; }
+int elems_per_vec(int32_t dtype) { return 16 / elem_size(dtype); }
+
+int race_segments(int32_t B, int32_t V, int32_t dtype) {
+    if (B <= 0) return 1;
+    const int nvec = (V + elems_per_vec(dtype) - 1) / elems_per_vec(dtype);
+    int segs = (kRaceTargetBlocks + B - 1) / B;
+    const int max_by_len = nvec / kRaceBlock;  // keep at least one vector per thread
+    if (segs > max_by_len) segs = max_by_len;
+    if (segs > kMaxSegs) segs = kMaxSegs;
+    return segs < 1 ? 1 : segs;
+}
+
+struct WsLayout {
+    size_t t_lse2, t_logp2, t_h, t_am, dstats, cand, total;
+};
+
+WsLayout layout_for(int32_t B, int32_t K, int32_t V, int32_t dtype) {
+    const size_t rows_t = static_cast<size_t>(B) * (K + 1);
+    const size_t n = static_cast<size_t>(B) * K;
+    WsLayout w;
+    size_t off = 0;
+    w.t_lse2 = off;
+    off = align_up(off + 8 * rows_t);
+    w.t_logp2 = off;
+    off = align_up(off + 8 * n);
+    w.t_h = off;
+    off = align_up(off + 4 * rows_t);
+    w.t_am = off;
+    off = align_up(off + 4 * rows_t);
+    w.dstats = off;
+    off = align_up(off + 24 * n);
+    w.cand = off;
+    off = align_up(off + sizeof(RaceCand) * static_cast<size_t>(B) * race_segments(B, V, dtype));
+    w.total = off;
+    return w;
+}
+
+// Draft-statistics buffer views (see spec_draft_stats_bytes).
+struct DraftStats {
+    double *lse2, *logq2;
+    float *qmax, *feat;
+};
+DraftStats draft_stats_view(void *p, size_t n) {
+    char *c = static_cast<char *>(p);
+    return DraftStats{reinterpret_cast<double *>(c), reinterpret_cast<double *>(c + 8 * n),
+                      reinterpret_cast<float *>(c + 16 * n), reinterpret_cast<float *>(c + 20 * n)};
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+spec_status check_logits_shape(int32_t V, int64_t stride, int32_t dtype, float temperature) {
+    if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return SPEC_ERR_ARG;
+    if (V < 2 || stride < V) return SPEC_ERR_ARG;
+    if ((stride * elem_size(dtype)) % 16 != 0) return SPEC_ERR_ARG;
+    if (!(temperature >= 1e-4f && temperature <= 1e4f)) return SPEC_ERR_ARG;
+    return SPEC_OK;
+}
+
+spec_status check_params(const spec_params *p) {
+    if (!p) return SPEC_ERR_ARG;
+    if (p->batch < 0 || p->num_draft < 1 || p->reserved != 0) return SPEC_ERR_ARG;
+    if (p->num_draft > 64) return SPEC_ERR_UNSUPPORTED;
+    const spec_status s = check_logits_shape(p->vocab, p->row_stride, p->dtype, p->temperature);
+    if (s != SPEC_OK) return s;
+    // all row indices and b*(K+1)+j products must fit in int32
+    if (static_cast<int64_t>(p->batch) * (2 * p->num_draft + 1) > INT32_MAX) return SPEC_ERR_UNSUPPORTED;
+    return SPEC_OK;
+}
+
+spec_status launch_status() {
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Row-pass dispatch over (dtype, entropy for group 0).  Group 1 (draft rows)
+// never needs the entropy numerator.
+// ---------------------------------------------------------------------------
+template <typename T, bool E0>
+void launch_rows_t(const RowArgs &a, int nblocks, hipStream_t st) {
+    row_stats_kernel<T, kRowBlock, kRowUnroll, E0><<<dim3(nblocks), dim3(kRowBlock), 0, st>>>(a);
+}
+
+void launch_rows(int32_t dtype, const RowArgs &a, int nblocks, bool e0, hipStream_t st) {
+    if (nblocks <= 0) return;
+    if (dtype == SPEC_DTYPE_BF16) {
+        if (e0)
+            launch_rows_t<uint16_t, true>(a, nblocks, st);
+        else
+            launch_rows_t<uint16_t, false>(a, nblocks, st);
+    } else {
+        if (e0)
+            launch_rows_t<float, true>(a, nblocks, st);
+        else
+            launch_rows_t<float, false>(a, nblocks, st);
+    }
+}
+
+RowGroup empty_group() {
+    RowGroup g{};
+    g.rows_per_seq = 1;
+    return g;
+}
+
+float log2e_over(float temperature) { return kLog2e / temperature; }
+
+}  // namespace
+
+extern "C" {
+
+const char *spec_status_string(int32_t status) {
+    switch (status) {
+        case SPEC_OK: return "ok";
+        case SPEC_ERR_ARG: return "invalid argument";
+        case SPEC_ERR_UNSUPPORTED: return "unsupported configuration";
+        case SPEC_ERR_WORKSPACE: return "workspace missing or too small";
+        case SPEC_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t spec_workspace_bytes(const spec_params *p) {
+    if (check_params(p) != SPEC_OK) return 0;
+    return layout_for(p->batch, p->num_draft, p->vocab, p->dtype).total;
+}
+
+size_t spec_draft_stats_bytes(int32_t batch, int32_t num_draft) {
+    if (batch < 0 || num_draft < 1) return 0;
+    return 24 * static_cast<size_t>(batch) * static_cast<size_t>(num_draft);
+}
+
+spec_status spec_verify(const void *target, const void *draft, const int32_t *draft_tokens,
+                        const int32_t *kept_len, const void *draft_stats, uint64_t seed,
+                        int32_t mode, const spec_params *params, const spec_verify_out *out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    spec_status s = check_params(params);
+    if (s != SPEC_OK) return s;
+    if (mode != SPEC_MODE_LOSSLESS && mode != SPEC_MODE_FLY) return SPEC_ERR_ARG;
+    if (!out) return SPEC_ERR_ARG;
+    const spec_params &p = *params;
+    if (mode == SPEC_MODE_FLY && (p.fly_window < 0 || p.fly_window > (1 << 20) ||
+                                  std::isnan(p.fly_theta)))
+        return SPEC_ERR_ARG;
+    if (p.batch == 0) return SPEC_OK;
+    if (!target || !aligned16(target) || !draft_tokens || !out->accepted_len || !out->tokens)
+        return SPEC_ERR_ARG;
+    const bool lossless = mode == SPEC_MODE_LOSSLESS;
+    const bool own_draft = lossless && draft_stats == nullptr;
+    // Lossless mode re-reads the draft row of a rejected position, so the
+    // draft logits are needed even when their statistics are supplied.
+    if (lossless && (!draft || !aligned16(draft))) return SPEC_ERR_ARG;
+    if (draft_stats && !aligned16(draft_stats)) return SPEC_ERR_ARG;
+    const int32_t B = p.batch, K = p.num_draft, V = p.vocab;
+    const WsLayout ws = layout_for(B, K, V, p.dtype);
+    if (!workspace || workspace_bytes < ws.total) return SPEC_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SPEC_ERR_ARG;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(workspace);
+    double *t_lse2 = reinterpret_cast<double *>(w + ws.t_lse2);
+    double *t_logp2 = reinterpret_cast<double *>(w + ws.t_logp2);
+    float *t_h = reinterpret_cast<float *>(w + ws.t_h);
+    int32_t *t_am = reinterpret_cast<int32_t *>(w + ws.t_am);
+    const size_t n = static_cast<size_t>(B) * K;
+    DraftStats ds = draft_stats_view(
+        own_draft ? static_cast<void *>(w + ws.dstats) : const_cast<void *>(draft_stats), n);
+
+    const float c = log2e_over(p.temperature);
+    RowArgs ra{};
+    RowGroup &gt = ra.g[0];
+    gt.base = target;
+    gt.stride = p.row_stride;
+    gt.rows_per_seq = K + 1;
+    gt.active_extra = 1;
+    gt.gather_rows = lossless ? K : 0;
+    gt.lse = out->target_lse;
+    gt.entropy = out->target_entropy;
+    gt.argmax = out->target_argmax;
+    gt.lse2 = t_lse2;
+    gt.logtok2 = t_logp2;
+    gt.h_int = t_h;
+    gt.am_int = t_am;
+    RowGroup &gd = ra.g[1];
+    gd = empty_group();
+    if (own_draft) {
+        gd.base = draft;
+        gd.stride = p.row_stride;
+        gd.rows_per_seq = K;
+        gd.active_extra = 0;
+        gd.gather_rows = K;
+        gd.lse = out->draft_lse;
+        gd.qmax = out->draft_qmax;
+        gd.feat = out->draft_feat;
+        gd.lse2 = ds.lse2;
+        gd.logtok2 = ds.logq2;
+        gd.qmax_int = ds.qmax;
+        gd.feat_int = ds.feat;
+    }
+    ra.nrows0 = B * (K + 1);
+    ra.V = V;
+    ra.K = K;
+    ra.tokens = draft_tokens;
+    ra.kept_len = kept_len;
+    ra.c = c;
+    const int nrows = ra.nrows0 + (own_draft ? B * K : 0);
+    const bool ent0 = !lossless || out->target_entropy != nullptr;
+    launch_rows(p.dtype, ra, nrows, ent0, st);
+    if ((s = launch_status()) != SPEC_OK) return s;
+
+    if (!lossless) {
+        fly_kernel<<<dim3((B + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock), 0, st>>>(
+            draft_tokens, kept_len, t_am, t_h, B, K, p.fly_theta, p.fly_window,
+            out->accepted_len, out->tokens);
+        return launch_status();
+    }
+
+    RaceArgs rg{};
+    rg.target = target;
+    rg.draft = draft;
+    rg.stride = p.row_stride;
+    rg.V = V;
+    rg.K = K;
+    rg.kept_len = kept_len;
+    rg.t_lse2 = t_lse2;
+    rg.t_logp2 = t_logp2;
+    rg.d_lse2 = ds.lse2;
+    rg.d_logq2 = ds.logq2;
+    rg.c = c;
+    rg.inv_t = 1.0 / static_cast<double>(p.temperature);
+    rg.seed = seed;
+    rg.segs = race_segments(B, V, p.dtype);
+    const int nvec = (V + elems_per_vec(p.dtype) - 1) / elems_per_vec(p.dtype);
+    rg.seg_vecs = (nvec + rg.segs - 1) / rg.segs;
+    rg.cand = reinterpret_cast<RaceCand *>(w + ws.cand);
+    const dim3 grid(rg.segs, B);
+    if (p.dtype == SPEC_DTYPE_BF16) {
+        race_kernel<uint16_t, kRaceBlock><<<grid, dim3(kRaceBlock), 0, st>>>(rg);
+        race_combine_kernel<uint16_t, kSmallBlock><<<dim3(B), dim3(kSmallBlock), 0, st>>>(
+            rg, draft_tokens, out->accepted_len, out->tokens);
+    } else {
+        race_kernel<float, kRaceBlock><<<grid, dim3(kRaceBlock), 0, st>>>(rg);
+        race_combine_kernel<float, kSmallBlock><<<dim3(B), dim3(kSmallBlock), 0, st>>>(
+            rg, draft_tokens, out->accepted_len, out->tokens);
+    }
+    return launch_status();
+}
+
+spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,
+                          const spec_params *params, const float *omega_beta, float tau,
+                          float *conf, uint8_t *keep_mask, int32_t *kept_len, void *draft_stats,
+                          void *stream) {
+    spec_status s = check_params(params);
+    if (s != SPEC_OK) return s;
+    const spec_params &p = *params;
+    if (std::isnan(tau)) return SPEC_ERR_ARG;
+    if (p.batch == 0) return SPEC_OK;
+    if (!draft || !aligned16(draft) || !draft_tokens || !omega_beta || !draft_stats ||
+        !aligned16(draft_stats))
+        return SPEC_ERR_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int32_t B = p.batch, K = p.num_draft;
+    const size_t n = static_cast<size_t>(B) * K;
+    DraftStats ds = draft_stats_view(draft_stats, n);
+    RowArgs ra{};
+    RowGroup &gd = ra.g[0];
+    gd.base = draft;
+    gd.stride = p.row_stride;
+    gd.rows_per_seq = K;
+    gd.active_extra = 0;
+    gd.gather_rows = K;
+    gd.lse2 = ds.lse2;
+    gd.logtok2 = ds.logq2;
+    gd.qmax_int = ds.qmax;
+    gd.feat_int = ds.feat;
+    ra.g[1] = empty_group();
+    ra.nrows0 = B * K;
+    ra.V = p.vocab;
+    ra.K = K;
+    ra.tokens = draft_tokens;
+    ra.kept_len = nullptr;
+    ra.c = log2e_over(p.temperature);
+    launch_rows(p.dtype, ra, B * K, false, st);
+    if ((s = launch_status()) != SPEC_OK) return s;
+    av_score_kernel<<<dim3((B + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock), 0, st>>>(
+        ds.feat, B, K, omega_beta, tau, conf, keep_mask, kept_len);
+    return launch_status();
+}
+
+spec_status spec_av_update(const void *draft_stats, const int32_t *accepted_len,
+                           const int32_t *kept_len, int32_t batch, int32_t num_draft, float lr,
+                           float *omega_beta, void *stream) {
+    if (batch < 0 || num_draft < 1) return SPEC_ERR_ARG;
+    if (num_draft > 64) return SPEC_ERR_UNSUPPORTED;
+    if (!std::isfinite(lr)) return SPEC_ERR_ARG;
+    if (batch == 0) return SPEC_OK;
+    if (!draft_stats || !aligned16(draft_stats) || !accepted_len || !omega_beta)
+        return SPEC_ERR_ARG;
+    const size_t n = static_cast<size_t>(batch) * num_draft;
+    DraftStats ds = draft_stats_view(const_cast<void *>(draft_stats), n);
+    av_update_kernel<256><<<dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        ds.feat, accepted_len, kept_len, batch, num_draft, lr, omega_beta);
+    return launch_status();
+}
+
+spec_status spec_row_stats(const void *logits, int64_t rows, int32_t vocab, int64_t row_stride,
+                           int32_t dtype, float temperature, float *lse, float *entropy,
+                           int32_t *argmax, float *qmax, float *feat, void *stream) {
+    spec_status s = check_logits_shape(vocab, row_stride, dtype, temperature);
+    if (s != SPEC_OK) return s;
+    if (rows < 0) return SPEC_ERR_ARG;
+    if (rows > INT32_MAX) return SPEC_ERR_UNSUPPORTED;
+    if (rows == 0) return SPEC_OK;
+    if (!logits || !aligned16(logits)) return SPEC_ERR_ARG;
+    RowArgs ra{};
+    RowGroup &g = ra.g[0];
+    g.base = logits;
+    g.stride = row_stride;
+    g.rows_per_seq = static_cast<int32_t>(rows);
+    g.active_extra = 0;
+    g.gather_rows = 0;
+    g.lse = lse;
+    g.entropy = entropy;
+    g.argmax = argmax;
+    g.qmax = qmax;
+    g.feat = feat;
+    ra.g[1] = empty_group();
+    ra.nrows0 = static_cast<int32_t>(rows);
+    ra.V = vocab;
+    ra.K = 1;
+    ra.c = log2e_over(temperature);
+    launch_rows(dtype, ra, static_cast<int>(rows), entropy != nullptr,
+                static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// sv_common.hpp -- shared device helpers of the specverify HIP library:
+// element traits for 16-byte row loads, the Philox4x32-10 counter-based
+// generator and the fast transcendental wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr double kLn2 = 0.69314718055994530942;
+constexpr double kLog2eD = 1.44269504088896340736;
+constexpr float kLog2e = 1.44269504088896340736f;
+// Finite stand-in for "no maximum yet"; |l * log2(e)/T| stays far below it
+// for the supported temperature range.
+constexpr float kNoMax = -1.0e30f;
+// Terms 2^d with d below this are exactly zero in float; clamping d keeps the
+// entropy accumulator free of 0 * (-inf) for masked (-inf) logits.
+constexpr float kMinExp2 = -200.0f;
+
+// Raw hardware transcendentals (v_exp_f32 / v_log_f32: base 2, ~1 ulp).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// --------------------------------------------------------------------------
+// Element traits: one 16-byte vector holds 8 bfloat16 or 4 float logits.
+// --------------------------------------------------------------------------
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<uint16_t> {  // bfloat16 bit patterns
+    static constexpr int kPerVec = 8;
+    static constexpr uint32_t kNegInfPair = 0xFF80FF80u;
+    __device__ static __forceinline__ void unpack(const uint4 &v, float *x) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+    __device__ static __forceinline__ float at(const uint16_t *row, int i) {
+        return __uint_as_float(static_cast<uint32_t>(row[i]) << 16);
+    }
+    // Vector `vi` of a row whose last vector is only partly inside V.
+    __device__ static __forceinline__ uint4 partial(const uint16_t *row, int vi, int V) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int e0 = vi * 8 + 2 * i, e1 = e0 + 1;
+            uint32_t lo = e0 < V ? row[e0] : 0xFF80u;
+            uint32_t hi = e1 < V ? row[e1] : 0xFF80u;
+            w[i] = lo | (hi << 16);
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    static constexpr uint32_t neg_inf_word() { return kNegInfPair; }
+};
+
+template <>
+struct Elem<float> {
+    static constexpr int kPerVec = 4;
+    __device__ static __forceinline__ void unpack(const uint4 &v, float *x) {
+        x[0] = __uint_as_float(v.x);
+        x[1] = __uint_as_float(v.y);
+        x[2] = __uint_as_float(v.z);
+        x[3] = __uint_as_float(v.w);
+    }
+    __device__ static __forceinline__ float at(const float *row, int i) { return row[i]; }
+    __device__ static __forceinline__ uint4 partial(const float *row, int vi, int V) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int e = vi * 4 + i;
+            w[i] = e < V ? __float_as_uint(row[e]) : 0xFF800000u;
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    static constexpr uint32_t neg_inf_word() { return 0xFF800000u; }
+};
+
+// --------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies by fixed odd multipliers on counter words 0 and 2,
+// with the products' high halves mixed into the other two words and the
+// round key; the key advances by two Weyl constants after every round.
+// --------------------------------------------------------------------------
+struct PhiloxKey {
+    uint32_t lo, hi;
+};
+
+__device__ __forceinline__ PhiloxKey philox_key(uint64_t seed) {
+    return PhiloxKey{static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32)};
+}
+
+__device__ __forceinline__ uint4 philox10(uint4 c, PhiloxKey k) {
+    uint32_t k0 = k.lo, k1 = k.hi;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t a = static_cast<uint64_t>(0xD2511F53u) * c.x;
+        const uint64_t b = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
+        c = make_uint4(static_cast<uint32_t>(b >> 32) ^ c.y ^ k0, static_cast<uint32_t>(b),
+                       static_cast<uint32_t>(a >> 32) ^ c.w ^ k1, static_cast<uint32_t>(a));
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// Stream tags (fourth counter word).
+constexpr uint32_t kTagAccept = 1u;
+constexpr uint32_t kTagRace = 2u;
+
+__device__ __forceinline__ uint32_t pick_word(const uint4 &r, uint32_t w) {
+    return w == 0 ? r.x : (w == 1 ? r.y : (w == 2 ? r.z : r.w));
+}
+
+// One draw for vocabulary id x at (position, sequence, tag).
+__device__ __forceinline__ uint32_t draw_u32(PhiloxKey k, uint32_t x, uint32_t pos, uint32_t seq,
+                                             uint32_t tag) {
+    return pick_word(philox10(make_uint4(x >> 2, pos, seq, tag), k), x & 3u);
+}
+
+// The 23 leading bits on the odd points of the 2^-24 grid: (2k+1) 2^-24,
+// exact in float and double, never 0 or 1.
+__device__ __forceinline__ float lattice_u32f(uint32_t r) {
+    return fmaf(static_cast<float>(r >> 9), 0x1.0p-23f, 0x1.0p-24f);
+}
+__device__ __forceinline__ double lattice_u64(uint32_t r) {
+    return (2.0 * static_cast<double>(r >> 9) + 1.0) * 0x1.0p-24;
+}
+
+__device__ __forceinline__ int clamp_len(int L, int K) { return L < 0 ? 0 : (L > K ? K : L); }
+
+}  // namespace sv

@@ -1,0 +1,305 @@
+// sv_finish.hpp -- per-sequence decisions after the row pass.
+//
+// Lossless (page "Speculative Decoding: как черновая модель ускоряет
+// генерацию LLM без потери качества", sections "Основная идея: черновик и
+// верификация" and "Математика верификации"): accept draft x_j while
+// u_j < p(x_j)/q(x_j); at the first rejection j* draw from
+// norm(max(0, p - q)); if all L verified drafts pass, draw from p at row L
+// (row K is the bonus row; L < K is the trim point of adaptive verification,
+// where the target samples its own distribution -- page "Verificacion
+// Adaptativa sin una cabeza de confianza", footnote 1).  Draws are the
+// exponential race argmax_x w(x)/E_x, E_x = -ln u_x, with per-id Philox u_x.
+//
+// The race re-streams one (target, draft) row pair per sequence; rows are
+// split into segments so that small batches still fill the GPU.  Each
+// segment screens keys in float (log2 domain), re-evaluates every candidate
+// within a margin of the segment's best in double, and reports its best
+// double key; a combine kernel takes the best segment.
+//
+// FLy (page "Training-Free Loosely Speculative Decoding...", section
+// "2. Metodologia", part A): one thread per sequence scans the flags.
+#pragma once
+
+#include "sv_common.hpp"
+
+namespace sv {
+
+struct RaceCand {
+    double key;
+    int32_t x;      // -1: no candidate in this segment
+    int32_t jstar;  // verified position the race ran at
+};
+
+struct RaceArgs {
+    const void *target;
+    const void *draft;
+    int64_t stride;
+    int32_t V, K;
+    const int32_t *kept_len;  // [B] or null
+    const double *t_lse2;     // [B*(K+1)]
+    const double *t_logp2;    // [B*K]
+    const double *d_lse2;     // [B*K]
+    const double *d_logq2;    // [B*K]
+    float c;                  // log2(e)/T (float, as in the row pass)
+    double inv_t;             // 1/T in double
+    uint64_t seed;
+    int32_t segs;             // segments per row
+    int32_t seg_vecs;         // 16-byte vectors per segment
+    RaceCand *cand;           // [B][segs]
+};
+
+// Screening margin in log2 units.  Float screening keys carry errors of a
+// few 1e-6; every thread best within the margin is re-evaluated in double.
+constexpr float kScreenMargin = 1e-3f;
+
+// First rejected position of sequence b (L when all verified drafts pass),
+// computed by the first wave; every workgroup of the sequence agrees.
+__device__ __forceinline__ int decide_lossless(const RaceArgs &a, int b, int L, PhiloxKey key) {
+    __shared__ int s_jstar;
+    const int tid = threadIdx.x;
+    if (tid < kWave) {
+        bool rej = false;
+        if (tid < L) {
+            const double u = lattice_u64(draw_u32(key, 0u, tid, b, kTagAccept));
+            const int i = b * a.K + tid;
+            const double ratio = exp2(a.t_logp2[i] - a.d_logq2[i]);  // p(x_j)/q(x_j)
+            rej = !(u < ratio);
+        }
+        const unsigned long long m = __ballot(rej);
+        if (tid == 0) s_jstar = m ? __ffsll(m) - 1 : L;
+    }
+    __syncthreads();
+    return s_jstar;
+}
+
+// Race over vectors [v_lo, v_hi) of one row (pair) with NT threads.
+// residual: w = max(0, p - q) from the target and draft rows; otherwise
+// w = p of the target row.  Returns (in thread 0) the best double key and id.
+template <typename T, int NT>
+__device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo, int v_hi, int V,
+                           float c, double cd, double inv_t, double lse2_t, double lse2_d,
+                           PhiloxKey key, uint32_t pos, uint32_t seq, double *out_key,
+                           int *out_x) {
+    using E = Elem<T>;
+    constexpr int EPV = E::kPerVec;
+    constexpr int NW = NT / kWave;
+    const int tid = threadIdx.x;
+    const int nfull = V / EPV;
+    const uint4 *tv = reinterpret_cast<const uint4 *>(trow);
+    const uint4 *dv = reinterpret_cast<const uint4 *>(drow);
+    const float lt2 = static_cast<float>(lse2_t);
+    const float ld2 = static_cast<float>(lse2_d);
+
+    float best = -__builtin_inff();
+    int bx = INT_MAX;
+    for (int vi = v_lo + tid; vi < v_hi; vi += NT) {
+        const uint4 tq = vi < nfull ? tv[vi] : E::partial(trow, vi, V);
+        float xt[EPV], xd[EPV];
+        E::unpack(tq, xt);
+        if (residual) {
+            const uint4 dq = vi < nfull ? dv[vi] : E::partial(drow, vi, V);
+            E::unpack(dq, xd);
+        }
+#pragma unroll
+        for (int blk = 0; blk < EPV / 4; ++blk) {
+            const uint32_t base = static_cast<uint32_t>(vi) * EPV + blk * 4;
+            const uint4 r = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
+            const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int k = blk * 4 + q;
+                const float e2 = -hw_log2(lattice_u32f(w4[q]));  // E / ln 2 > 0
+                const float lg = hw_log2(e2);
+                float g;
+                if (residual) {
+                    const float p = hw_exp2(fmaf(xt[k], c, -lt2));
+                    const float qq = hw_exp2(fmaf(xd[k], c, -ld2));
+                    const float w = p - qq;
+                    g = w > 0.f ? hw_log2(w) - lg : -__builtin_inff();
+                } else {
+                    g = xt[k] * c - lg;  // log2 p + log2-normaliser, which all ids share
+                }
+                const int x = static_cast<int>(base) + q;
+                if (g > best && x < V) {
+                    best = g;
+                    bx = x;
+                }
+            }
+        }
+    }
+
+    // Workgroup maximum of the screening keys.
+    __shared__ float sh_best[NW];
+    __shared__ double sh_key[NW];
+    __shared__ int sh_x[NW];
+    float m = best;
+#pragma unroll
+    for (int msk = kWave / 2; msk > 0; msk >>= 1) m = fmaxf(m, __shfl_xor(m, msk, kWave));
+    const int lane = tid & (kWave - 1), wv = tid / kWave;
+    if (lane == 0) sh_best[wv] = m;
+    __syncthreads();
+    float g1 = sh_best[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) g1 = fmaxf(g1, sh_best[w]);
+
+    // Double-precision keys of the candidates within the margin.
+    double k64 = -__builtin_inf();
+    int kx = INT_MAX;
+    if (best > -__builtin_inff() && best >= g1 - kScreenMargin) {
+        const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(bx), pos, seq, kTagRace));
+        const double lnE = log(-log(u));
+        const double lt = static_cast<double>(E::at(trow, bx));
+        if (residual) {
+            const double ld = static_cast<double>(E::at(drow, bx));
+            const double w = exp2(lt * cd - lse2_t) - exp2(ld * cd - lse2_d);
+            if (w > 0.0) {
+                k64 = log(w) - lnE;
+                kx = bx;
+            }
+        } else {
+            k64 = lt * inv_t - lnE;  // ln p(x) + lse: the same for every id
+            kx = bx;
+        }
+    }
+#pragma unroll
+    for (int msk = kWave / 2; msk > 0; msk >>= 1) {
+        const double ok = __shfl_xor(k64, msk, kWave);
+        const int ox = __shfl_xor(kx, msk, kWave);
+        if (ok > k64 || (ok == k64 && ox < kx)) {
+            k64 = ok;
+            kx = ox;
+        }
+    }
+    __syncthreads();  // sh_best reads are done before thread 0 reuses shared state
+    if (lane == 0) {
+        sh_key[wv] = k64;
+        sh_x[wv] = kx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double bk = sh_key[0];
+        int bxx = sh_x[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            if (sh_key[w] > bk || (sh_key[w] == bk && sh_x[w] < bxx)) {
+                bk = sh_key[w];
+                bxx = sh_x[w];
+            }
+        *out_key = bk;
+        *out_x = bxx == INT_MAX ? -1 : bxx;
+    }
+    __syncthreads();
+}
+
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
+    const int seg = blockIdx.x;
+    const int b = blockIdx.y;
+    const PhiloxKey key = philox_key(a.seed);
+    const int L = a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K;
+    const int jstar = decide_lossless(a, b, L, key);
+    const bool residual = jstar < L;
+    const T *trow = static_cast<const T *>(a.target) +
+                    (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
+    const T *drow = residual ? static_cast<const T *>(a.draft) +
+                                   (static_cast<int64_t>(b) * a.K + jstar) * a.stride
+                             : nullptr;
+    const double lt = a.t_lse2[b * (a.K + 1) + jstar];
+    const double ld = residual ? a.d_lse2[b * a.K + jstar] : 0.0;
+    const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
+    const int v_lo = seg * a.seg_vecs;
+    const int v_hi = min(nvec, v_lo + a.seg_vecs);
+    double k;
+    int x;
+    race_range<T, NT>(trow, drow, residual, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
+                      a.inv_t, lt, ld, key, jstar, b, &k, &x);
+    if (threadIdx.x == 0) a.cand[b * a.segs + seg] = RaceCand{k, x, jstar};
+}
+
+// Best segment per sequence; writes accepted_len and the emitted tokens.  A
+// residual that vanished in floating point (only possible within rounding of
+// u_j = p/q) falls back to a race over p at the same row.
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int32_t *tokens,
+                                                         int32_t *accepted_len,
+                                                         int32_t *out_tokens) {
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    __shared__ int s_y;
+    __shared__ int s_j;
+    if (tid == 0) {
+        double bk = -__builtin_inf();
+        int bx = INT_MAX;
+        for (int s = 0; s < a.segs; ++s) {
+            const RaceCand cnd = a.cand[b * a.segs + s];
+            if (cnd.x >= 0 && (cnd.key > bk || (cnd.key == bk && cnd.x < bx))) {
+                bk = cnd.key;
+                bx = cnd.x;
+            }
+        }
+        s_y = bx == INT_MAX ? -1 : bx;
+        s_j = a.cand[b * a.segs].jstar;
+    }
+    __syncthreads();
+    const int jstar = s_j;
+    if (s_y < 0) {
+        const T *trow = static_cast<const T *>(a.target) +
+                        (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
+        const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
+        double k;
+        int x;
+        race_range<T, NT>(trow, nullptr, false, 0, nvec, a.V, a.c, static_cast<double>(a.c),
+                          a.inv_t, a.t_lse2[b * (a.K + 1) + jstar], 0.0, philox_key(a.seed),
+                          jstar, b, &k, &x);
+        if (tid == 0) s_y = x;
+        __syncthreads();
+    }
+    if (tid == 0) accepted_len[b] = jstar;
+    for (int j = tid; j <= a.K; j += NT) {
+        int v = -1;
+        if (j < jstar)
+            v = tokens[b * a.K + j];
+        else if (j == jstar)
+            v = s_y;
+        out_tokens[b * (a.K + 1) + j] = v;
+    }
+}
+
+// FLy: a deviation is a draft token different from the target's top token.
+// Deviations with h < theta are rejected at once; others are accepted only
+// when the next W drafts exist and all match (else rejected, retroactively
+// when the target deviates again inside the window).  The replacement or
+// bonus token is the target's top token at the stopping row.
+__global__ void fly_kernel(const int32_t *tokens, const int32_t *kept_len, const int32_t *am,
+                           const float *h, int B, int K, float theta, int W,
+                           int32_t *accepted_len, int32_t *out_tokens) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int L = kept_len ? clamp_len(kept_len[b], K) : K;
+    const int32_t *tok = tokens + b * K;
+    const int32_t *top = am + b * (K + 1);
+    const float *hb = h + b * (K + 1);
+    int j = 0, jstar = L;
+    while (j < L) {
+        if (tok[j] == top[j]) {
+            ++j;
+            continue;
+        }
+        if (!(hb[j] >= theta) || j + W > L - 1) {
+            jstar = j;
+            break;
+        }
+        bool again = false;
+        for (int k = j + 1; k <= j + W; ++k) again |= tok[k] != top[k];
+        if (again) {
+            jstar = j;
+            break;
+        }
+        j += W + 1;
+    }
+    accepted_len[b] = jstar;
+    int32_t *ot = out_tokens + b * (K + 1);
+    for (int k = 0; k <= K; ++k) ot[k] = k < jstar ? tok[k] : (k == jstar ? top[jstar] : -1);
+}
+
+}  // namespace sv

@@ -1,0 +1,139 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+public header declares, and rejects bad arguments on the host before any GPU
+work (so no GPU is needed for these calls)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+import torch
+
+import draft_token_verification_vocab_amd as sv
+
+# These calls hand the library fake device addresses that host-side
+# validation must reject; never let them reach a real GPU.
+host_only = pytest.mark.skipif(torch.cuda.is_available(),
+                               reason="fake device pointers: host-only validation test")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \t\*]*?\b(spec_\w+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sv.lib_path()):
+        from draft_token_verification_vocab_amd import build
+        build.build()
+    return sv.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("spec_verify", "spec_av_score", "spec_av_update", "spec_row_stats",
+              "spec_workspace_bytes", "spec_draft_stats_bytes", "spec_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+        assert n in sv._SIGNATURES, "binding lacks a signature for %s" % n
+
+
+def _params(**kw):
+    base = dict(batch=4, num_draft=4, vocab=1024, dtype=1, row_stride=1024, temperature=1.0,
+                fly_theta=0.3, fly_window=4, reserved=0)
+    base.update(kw)
+    return sv._Params(**base)
+
+
+def test_workspace_query(L):
+    p = _params()
+    n = L.spec_workspace_bytes(ctypes.byref(p))
+    assert n > 0 and n % 256 == 0
+    big = _params(batch=1024, num_draft=8, vocab=128256, row_stride=128256)
+    assert L.spec_workspace_bytes(ctypes.byref(big)) > n
+    assert L.spec_workspace_bytes(ctypes.byref(_params(num_draft=0))) == 0
+    assert L.spec_draft_stats_bytes(64, 5) == 24 * 64 * 5
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_draft=0), -1), (dict(num_draft=65), -2), (dict(vocab=1), -1),
+    (dict(row_stride=1000), -1), (dict(row_stride=1028), -1), (dict(dtype=7), -1),
+    (dict(temperature=0.0), -1), (dict(temperature=float("nan")), -1), (dict(batch=-1), -1),
+    (dict(reserved=1), -1)])
+def test_verify_rejects_bad_params_on_host(L, kw, status):
+    p = _params(**kw)
+    out = sv._VerifyOut()
+    st = L.spec_verify(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16), None, None,
+                       0, 0, ctypes.byref(p), ctypes.byref(out), ctypes.c_void_p(16), 1 << 20,
+                       None)
+    assert st == status
+
+
+@host_only
+def test_verify_rejects_bad_pointers_and_modes(L):
+    p = _params()
+    out = sv._VerifyOut(16, 16, None, None, None, None, None, None)
+    args = dict(target=16, draft=16, tokens=16)
+
+    def call(mode=0, target=16, draft=16, tokens=16, ws=16, ws_bytes=1 << 30, o=out):
+        return L.spec_verify(ctypes.c_void_p(target), ctypes.c_void_p(draft),
+                             ctypes.c_void_p(tokens), None, None, 0, mode, ctypes.byref(p),
+                             ctypes.byref(o) if o is not None else None, ctypes.c_void_p(ws),
+                             ws_bytes, None)
+    assert call(mode=5) == -1
+    assert call(target=8) == -1                # misaligned logits
+    assert call(draft=0) == -1                 # lossless needs draft logits
+    assert call(tokens=0) == -1
+    assert call(ws=0) == -3                    # no workspace
+    assert call(ws_bytes=16) == -3             # workspace too small
+    assert call(o=None) == -1
+    bad = sv._VerifyOut(0, 16, None, None, None, None, None, None)
+    assert call(o=bad) == -1
+    fly = _params(fly_window=-1)
+    assert L.spec_verify(ctypes.c_void_p(16), None, ctypes.c_void_p(16), None, None, 0, 1,
+                         ctypes.byref(fly), ctypes.byref(out), ctypes.c_void_p(16), 1 << 30,
+                         None) == -1
+
+
+@host_only
+def test_empty_inputs_are_noops_on_host(L):
+    p = _params(batch=0)
+    out = sv._VerifyOut()
+    assert L.spec_verify(None, None, None, None, None, 0, 0, ctypes.byref(p), ctypes.byref(out),
+                         None, 0, None) == 0
+    assert L.spec_row_stats(None, 0, 1024, 1024, 1, 1.0, None, None, None, None, None,
+                            None) == 0
+    assert L.spec_av_update(None, None, None, 0, 4, 0.05, None, None) == 0
+
+
+@host_only
+def test_other_entry_points_validate(L):
+    p = _params()
+    assert L.spec_av_score(None, ctypes.c_void_p(16), ctypes.byref(p), ctypes.c_void_p(16), 0.2,
+                           None, None, None, ctypes.c_void_p(16), None) == -1
+    assert L.spec_av_score(ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.byref(p),
+                           ctypes.c_void_p(16), float("nan"), None, None, None,
+                           ctypes.c_void_p(16), None) == -1
+    assert L.spec_av_update(ctypes.c_void_p(16), None, None, 4, 4, 0.05, ctypes.c_void_p(16),
+                            None) == -1
+    assert L.spec_av_update(ctypes.c_void_p(16), ctypes.c_void_p(16), None, 4, 65, 0.05,
+                            ctypes.c_void_p(16), None) == -2
+    assert L.spec_row_stats(ctypes.c_void_p(16), 4, 1024, 1020, 1, 1.0, None, None, None, None,
+                            None, None) == -1
+    assert L.spec_row_stats(ctypes.c_void_p(16), -1, 1024, 1024, 1, 1.0, None, None, None, None,
+                            None, None) == -1
+    for s in (0, -1, -2, -3, -4, 99):
+        assert isinstance(L.spec_status_string(s), bytes)

@@ -1,0 +1,282 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.  Small sizes span several tiles and a ragged tail;
+the workload sizes are checked on oracle-computed samples and by properties
+that hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_vocab_amd as sv
+from draft_token_verification_vocab_amd import workloads as W
+from oracle import ref
+from parity_util import (REL_TOL, assert_close, check_token_layout, compare_decisions, f32,
+                         host_logits, oracle_threads)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NT = oracle_threads()
+ALL_NEAR = ref.NEAR_ACCEPT | ref.NEAR_RACE | ref.RESIDUAL_EMPTY | ref.NEAR_GATE | ref.NEAR_TRIM
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the GPU tests need an MI355X"
+    sv.load()
+    ref.lib()
+
+
+def np_(t):
+    return t.detach().cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# Row statistics
+# ---------------------------------------------------------------------------
+def _special_rows(V, dtype, stride, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(10, V, generator=g) * 3.0
+    x[0, ::5] = -float("inf")                      # masked vocabulary
+    x[1, 77 % V] += 30.0                           # very peaked (tiny entropy)
+    x[2] = 0.5                                     # uniform: all tied
+    x[3, [V - 1, V // 2]] = x[3].max() + 1.0       # two maxima far apart
+    x[4] = -float("inf")
+    x[4, V - 1] = 1.0                              # one finite entry, at the tail
+    x[5] = torch.linspace(-5, 5, V)                # maximum at the last id
+    x[6, :min(V, 3)] = 40.0                        # tie at the very front
+    xd = torch.full((10, stride), float("nan"))
+    xd[:, :V] = x
+    return xd.to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("V,stride", [(2, 8), (9, 16), (1003, 1008), (4097, 4104),
+                                      (32000, 32000), (128256, 128256), (152064, 152064)])
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_row_stats_parity(dtype, V, stride, T):
+    xh = _special_rows(V, dtype, stride, seed=V + int(T * 10))
+    x = xh.to(DEV)
+    r = sv.row_stats(x, vocab=V, temperature=T, qmax=True, feat=True)
+    torch.cuda.synchronize()
+    o = ref.rows_stats(host_logits(xh), temperature=f32(T), V=V, nthreads=NT)
+    rel = REL_TOL[dtype]
+    assert np.array_equal(np_(r["argmax"]), o["argmax"])
+    assert_close(np_(r["lse"]), o["lse"], rel, "lse")
+    assert_close(np_(r["entropy"]), o["h"], rel, "entropy", abs_floor=1e-12)
+    assert_close(np_(r["qmax"]), o["qmax"], rel, "qmax")
+    # logit(q_max) passes through 0: relative to max(|feat|, 1)
+    assert_close(np_(r["feat"]), o["feat"], rel, "feat", abs_floor=rel)
+
+
+def test_row_stats_reproducible_and_ordered_ties():
+    x = torch.zeros(3, 40000, device=DEV, dtype=torch.bfloat16)
+    x[0, [39999, 12345, 20000]] = 1.0
+    x[1, 1] = -1.0
+    a = sv.row_stats(x)
+    b = sv.row_stats(x)
+    assert torch.equal(a["lse"], b["lse"]) and torch.equal(a["entropy"], b["entropy"])
+    assert np_(a["argmax"]).tolist() == [12345, 0, 0]
+
+
+# ---------------------------------------------------------------------------
+# FLy
+# ---------------------------------------------------------------------------
+def _fly_check(batch, theta=0.3, window=4, kept=None):
+    t = batch.target.to(DEV)
+    tok = batch.tokens.to(DEV)
+    kept_d = None if kept is None else kept.to(DEV)
+    r = sv.verify(t, None, tok, seed=0, mode=sv.MODE_FLY, fly_theta=theta, fly_window=window,
+                  vocab=batch.V, kept_len=kept_d, stats=True)
+    torch.cuda.synchronize()
+    o = ref.verify(host_logits(batch.target), None, np_(batch.tokens), 0, ref.MODE_FLY,
+                   theta=f32(theta), window=window, V=batch.V,
+                   kept_len=None if kept is None else np_(kept), nthreads=NT)
+    nm, nb = compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ref.NEAR_GATE, "fly")
+    rel = REL_TOL[batch.target.dtype]
+    assert np.array_equal(np_(r.target_argmax), o["t_argmax"])
+    assert_close(np_(r.target_lse), o["t_lse"], rel, "target lse")
+    assert_close(np_(r.target_entropy), o["t_h"], rel, "target entropy", abs_floor=1e-12)
+    check_token_layout(np_(r.accepted_len), np_(r.tokens), np_(batch.tokens),
+                       None if kept is None else np_(kept))
+    return r, o, nm, nb
+
+
+@pytest.mark.parametrize("B,K,V,stride", [(24, 8, 128256, 128256), (16, 4, 5003, 5008),
+                                          (8, 1, 1000, 1000)])
+def test_fly_parity(B, K, V, stride):
+    batch = W.make(2, B=B, K=K, V=V, stride=stride)
+    _fly_check(batch)
+
+
+def test_fly_gate_branches():
+    # peaks of +16 make confident rows (h ~ 0.03): the reject-now branch
+    batch = W.fly(32, 8, 20000, seed=5, peak=16.0)
+    r, o, _, _ = _fly_check(batch)
+    assert (o["accepted_len"] < 8).any() and (o["accepted_len"] == 8).any()
+    # theta > 1 is strict greedy, W = 0 with theta <= 0 accepts everything
+    _fly_check(batch, theta=1.5, window=4)
+    r, o, _, _ = _fly_check(batch, theta=0.0, window=0)
+    assert np.all(o["accepted_len"] == 8)
+    kept = torch.randint(0, 9, (32,), generator=torch.Generator().manual_seed(1), dtype=torch.int32)
+    _fly_check(batch, kept=kept)
+
+
+# ---------------------------------------------------------------------------
+# Lossless
+# ---------------------------------------------------------------------------
+def _lossless_check(batch, seed, kept=None, draft_stats_path=False):
+    t = batch.target.to(DEV)
+    d = batch.draft.to(DEV)
+    tok = batch.tokens.to(DEV)
+    kept_d = None if kept is None else kept.to(DEV)
+    T = batch.temperature
+    ds = None
+    if draft_stats_path:
+        K = tok.shape[1]
+        ob = torch.zeros(K + 1, device=DEV)
+        _, _, _, ds = sv.av_score(d, tok, ob, 0.0, temperature=T, vocab=batch.V)
+    r = sv.verify(t, d, tok, seed=seed, temperature=T, vocab=batch.V, kept_len=kept_d,
+                  draft_stats=ds, stats=True)
+    torch.cuda.synchronize()
+    o = ref.verify(host_logits(batch.target), host_logits(batch.draft), np_(batch.tokens), seed,
+                   temperature=f32(T), V=batch.V, kept_len=None if kept is None else np_(kept),
+                   nthreads=NT)
+    nm, nb = compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ALL_NEAR, "lossless")
+    rel = REL_TOL[batch.target.dtype]
+    assert np.array_equal(np_(r.target_argmax), o["t_argmax"])
+    assert_close(np_(r.target_lse), o["t_lse"], rel, "target lse")
+    assert_close(np_(r.target_entropy), o["t_h"], rel, "target entropy", abs_floor=1e-12)
+    if not draft_stats_path:
+        assert_close(np_(r.draft_lse), o["d_lse"], rel, "draft lse")
+        assert_close(np_(r.draft_qmax), o["d_qmax"], rel, "draft qmax")
+        assert_close(np_(r.draft_feat), o["d_feat"], rel, "draft feat", abs_floor=rel)
+    check_token_layout(np_(r.accepted_len), np_(r.tokens), np_(batch.tokens),
+                       None if kept is None else np_(kept))
+    return r, o, nm, nb
+
+
+def test_lossless_c0_full_size():
+    batch = W.make(0)
+    _lossless_check(batch, seed=0)
+    for s in range(1, 40):  # more seeds of the same rows: many residual races
+        _lossless_check(batch, seed=s)
+
+
+@pytest.mark.parametrize("cfg,B,K,V,stride", [(1, 12, 5, 128256, 128256), (3, 12, 4, 152064, 152064),
+                                              (1, 16, 3, 7001, 7008), (0, 32, 4, 32000, 32000),
+                                              (3, 8, 2, 1003, 1008)])
+def test_lossless_parity(cfg, B, K, V, stride):
+    batch = W.make(cfg, B=B, K=K, V=V, stride=stride)
+    _, o, nm, nb = _lossless_check(batch, seed=7)
+    _lossless_check(batch, seed=8, draft_stats_path=True)
+
+
+def test_lossless_kept_len_and_bad_tokens():
+    batch = W.make(1, B=20, K=5, V=3001, stride=3008)
+    batch.tokens[3, 1] = 3001       # outside V: rejected
+    batch.tokens[4, 0] = -7
+    kept = torch.tensor([0, 1, 2, 3, 4, 5] * 3 + [0, 5], dtype=torch.int32)
+    r, o, _, _ = _lossless_check(batch, seed=3, kept=kept)
+    assert np_(r.accepted_len)[4] == 0
+
+
+def test_lossless_masked_vocab():
+    batch = W.make(1, B=16, K=3, V=4000)
+    batch.target[:, :, ::3] = -float("inf")
+    batch.draft[:, :, 1::3] = -float("inf")
+    r, o, _, _ = _lossless_check(batch, seed=11)
+    tok = np_(r.tokens)
+    acc = np_(r.accepted_len)
+    for b in range(16):  # an emitted replacement / bonus token never has p = 0
+        assert tok[b, acc[b]] % 3 != 0
+
+
+def test_lossless_deterministic_across_streams():
+    batch = W.make(3, B=16, K=4, V=20000)
+    t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
+    a = sv.verify(t, d, tok, seed=5, temperature=0.7)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = sv.verify(t, d, tok, seed=5, temperature=0.7)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(a.tokens, b.tokens) and torch.equal(a.accepted_len, b.accepted_len)
+    c = sv.verify(t, d, tok, seed=6, temperature=0.7)
+    torch.cuda.synchronize()
+    assert not torch.equal(a.tokens, c.tokens)
+
+
+# ---------------------------------------------------------------------------
+# Adaptive verification
+# ---------------------------------------------------------------------------
+def _av_step(batch, ob_host, tau, lr, seed):
+    """One GPU step (score, verify, update) and the oracle's step on the same
+    inputs and the same starting parameters."""
+    K = batch.tokens.shape[1]
+    T = batch.temperature
+    t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
+    ob = torch.tensor(ob_host, dtype=torch.float32, device=DEV)
+    conf, mask, kept, ds = sv.av_score(d, tok, ob, tau, temperature=T, vocab=batch.V)
+    r = sv.verify(t, d, tok, seed=seed, temperature=T, vocab=batch.V, kept_len=kept,
+                  draft_stats=ds)
+    sv.av_update(ds, r.accepted_len, kept, ob, lr, tok.shape[0], K)
+    torch.cuda.synchronize()
+    dh = host_logits(batch.draft)
+    B = dh.shape[0]
+    st = ref.rows_stats(dh.reshape(B * K, -1), temperature=f32(T), V=batch.V, nthreads=NT)
+    feat = st["feat"].reshape(B, K)
+    ob64 = np.asarray(ob_host, dtype=np.float32).astype(np.float64)
+    oconf, omask, okept, onear = ref.av_score(feat, ob64, f32(tau))
+    o = ref.verify(host_logits(batch.target), dh, np_(batch.tokens), seed, temperature=f32(T),
+                   V=batch.V, kept_len=okept, nthreads=NT)
+    o["boundary"] |= onear
+    rel = REL_TOL[batch.target.dtype]
+    assert_close(np_(conf), oconf, rel, "confidence")
+    kept_ok = (np_(kept) == okept) | ((onear & ref.NEAR_TRIM) != 0)
+    assert kept_ok.all(), "kept_len differs outside the trim boundary set"
+    same = np_(kept) == okept
+    compare_decisions(np_(r.accepted_len)[same], np_(r.tokens)[same],
+                      {k: (v[same] if hasattr(v, "shape") and v.shape[:1] == (B,) else v)
+                       for k, v in o.items()}, ALL_NEAR, "av verify")
+    new = ref.av_update(feat, o["accepted_len"], okept, ob64, f32(lr))
+    return np_(ob), new, o, okept
+
+
+def test_av_score_update_parity_c1_recipe():
+    batch = W.make(1, B=24)
+    ob0 = W.av_init(1)
+    got, want, _, okept = _av_step(batch, ob0, tau=0.0, lr=0.05, seed=0)
+    assert np.all(okept == 5)
+    assert np.allclose(got, want, rtol=0, atol=1e-5), (got, want)
+
+
+def test_av_pipeline_c4_recipe_steps():
+    ob = W.av_init(4)
+    for step in range(3):
+        batch = W.make(4, B=24, step=step)
+        got, want, o, okept = _av_step(batch, ob, tau=0.2, lr=0.05, seed=step)
+        assert np.allclose(got, want, rtol=0, atol=1e-5), (step, got, want)
+        ob = got.tolist()  # carry the GPU's parameters forward, as the pipeline does
+
+
+# ---------------------------------------------------------------------------
+# Edge cases at the boundary
+# ---------------------------------------------------------------------------
+def test_empty_batch_is_a_noop():
+    t = torch.zeros(0, 5, 64, device=DEV)
+    tok = torch.zeros(0, 4, dtype=torch.int32, device=DEV)
+    r = sv.verify(t, torch.zeros(0, 4, 64, device=DEV), tok, seed=0)
+    assert r.accepted_len.numel() == 0
+
+
+def test_invalid_arguments_raise():
+    t = torch.zeros(2, 3, 64, device=DEV)
+    d = torch.zeros(2, 2, 64, device=DEV)
+    tok = torch.zeros(2, 2, dtype=torch.int32, device=DEV)
+    with pytest.raises(sv.SpecVerifyError):
+        sv.verify(t, None, tok, seed=0)                       # lossless needs the draft
+    with pytest.raises(sv.SpecVerifyError):
+        sv.verify(t, d, tok, seed=0, temperature=0.0)
+    with pytest.raises(sv.SpecVerifyError):
+        sv.verify(t, d, tok, seed=0, vocab=65)                # V > stride
+    with pytest.raises(sv.SpecVerifyError):
+        sv.verify(t[:, :, :62].contiguous(), d[:, :, :62].contiguous(), tok, seed=0)  # 248 B rows
