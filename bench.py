@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy three times (a known-size "
+                         "kernel for calibrating hardware byte counters)")
     return ap.parse_args()
 
 
@@ -84,6 +87,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sv.load()
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------------------------ headline
     cfg = W.CONFIGS[2]
@@ -160,7 +170,7 @@ def main():
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "row_stats_kernel<bf16,512,4,entropy>", "kernel_us": round(kms * 1e3, 2),
+                "kernel": "row_stats_kernel<bf16,256,4,entropy>", "kernel_us": round(kms * 1e3, 2),
                 "algorithmic_bytes_per_launch": bytes_per_step,
                 "source_hash": row_pass_source_hash()}
     log("row pass: %.1f us/launch, %.0f GB/s (%.1f%% of peak)" % (kms * 1e3, achieved,
@@ -303,24 +313,35 @@ def _line(ms, rows, byt, res):
 
 def cpu_baseline(batch, cfg, budget_s):
     """The CPU oracle (never tuned) on a bounded sample of the headline
-    workload: the first n sequences, grown until about budget_s of work."""
+    workload: the first n sequences, grown (and then repeated) until about
+    budget_s seconds of work."""
+    import torch
     from oracle import ref
     threads = ref.default_threads()
-    tgt = batch.target.cpu().view(__import__("torch").int16).numpy().view("uint16")
+    tgt = batch.target.cpu().view(torch.int16).numpy().view("uint16")
     tok = batch.tokens.cpu().numpy()
+    Btot = batch.target.shape[0]
     n = 4
-    while True:
+    while True:  # grow the sample up to the whole batch
         t = time.perf_counter()
         ref.verify(tgt[:n], None, tok[:n], 0, ref.MODE_FLY, theta=cfg["theta"],
                    window=cfg["window"], nthreads=threads)
         dt = time.perf_counter() - t
-        if dt >= budget_s or n >= batch.target.shape[0]:
+        if dt >= budget_s or n >= Btot:
             break
-        n = min(batch.target.shape[0], max(n * 2, int(n * budget_s / max(dt, 1e-3) * 0.9)))
+        n = min(Btot, max(n * 2, int(n * budget_s / max(dt, 1e-3) * 0.9)))
+    reps, total = 1, dt
+    while total < budget_s:  # repeat whole passes until the budget is spent
+        t = time.perf_counter()
+        ref.verify(tgt[:n], None, tok[:n], 0, ref.MODE_FLY, theta=cfg["theta"],
+                   window=cfg["window"], nthreads=threads)
+        total += time.perf_counter() - t
+        reps += 1
     rows = n * (cfg["K"] + 1)
-    return {"value": round(rows / dt, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d sequences (%d target rows) of %s, FLy mode, %.1f s" % (
-                n, batch.target.shape[0], rows, cfg["name"], dt)}
+    return {"value": round(rows * reps / total, 1), "unit": "rows/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d sequences (%d target rows) of %s, FLy mode, %d pass(es), %.1f s"
+                      % (n, Btot, rows, cfg["name"], reps, total)}
 
 
 if __name__ == "__main__":

@@ -19,7 +19,7 @@ using namespace sv;
 
 // Row pass shape: threads per workgroup and 16-byte vectors per thread per
 // chunk (one chunk = UNROLL*8 bfloat16 or UNROLL*4 float logits).
-constexpr int kRowBlock = 512;
+constexpr int kRowBlock = 256;
 constexpr int kRowUnroll = 4;
 // Race shape and the number of race workgroups to aim for per launch.
 constexpr int kRaceBlock = 256;

@@ -136,4 +136,67 @@ __device__ __forceinline__ double lattice_u64(uint32_t r) {
 
 __device__ __forceinline__ int clamp_len(int L, int K) { return L < 0 ? 0 : (L > K ? K : L); }
 
+// --------------------------------------------------------------------------
+// Wave-wide reductions with DPP row shifts and row broadcasts (a
+// Hillis-Steele scan inside each 16-lane row, then rows 0..3 folded with
+// row_bcast15 / row_bcast31).  The total lands in lane 63 and is returned to
+// every lane.  Lanes without a source read the identity (0 bits).
+// --------------------------------------------------------------------------
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_pull(uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, false));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_pull64(uint64_t v) {
+    const uint32_t lo = dpp_pull<CTRL, ROWS>(static_cast<uint32_t>(v));
+    const uint32_t hi = dpp_pull<CTRL, ROWS>(static_cast<uint32_t>(v >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t lane63_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), 63);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Maximum of an unsigned 64-bit key over the wave.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t o;
+    o = dpp_pull64<0x111, 0xF>(v); v = o > v ? o : v;  // row_shr:1
+    o = dpp_pull64<0x112, 0xF>(v); v = o > v ? o : v;  // row_shr:2
+    o = dpp_pull64<0x114, 0xF>(v); v = o > v ? o : v;  // row_shr:4
+    o = dpp_pull64<0x118, 0xF>(v); v = o > v ? o : v;  // row_shr:8
+    o = dpp_pull64<0x142, 0xA>(v); v = o > v ? o : v;  // row_bcast15
+    o = dpp_pull64<0x143, 0xC>(v); v = o > v ? o : v;  // row_bcast31
+    return lane63_u64(v);
+}
+
+// Sum of a double over the wave, in a fixed order.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+    uint64_t v = static_cast<uint64_t>(__double_as_longlong(x));
+    auto add = [](uint64_t a, uint64_t b) {
+        return static_cast<uint64_t>(__double_as_longlong(
+            __longlong_as_double(static_cast<long long>(a)) +
+            __longlong_as_double(static_cast<long long>(b))));
+    };
+    v = add(v, dpp_pull64<0x111, 0xF>(v));
+    v = add(v, dpp_pull64<0x112, 0xF>(v));
+    v = add(v, dpp_pull64<0x114, 0xF>(v));
+    v = add(v, dpp_pull64<0x118, 0xF>(v));
+    v = add(v, dpp_pull64<0x142, 0xA>(v));
+    v = add(v, dpp_pull64<0x143, 0xC>(v));
+    return __longlong_as_double(static_cast<long long>(lane63_u64(v)));
+}
+
+// Order-preserving map of a float onto unsigned integers.
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
 }  // namespace sv

@@ -1,19 +1,24 @@
 // sv_rowstats.hpp -- the streaming row pass: one workgroup per logits row,
-// 16-byte loads, a single pass that keeps an online (max, sum, entropy
-// numerator, argmax) state per thread, merged across the wave with shuffles
-// and across waves through LDS.
+// 16-byte loads, a single pass with an online (max, sum, entropy numerator,
+// argmax) state per thread, then a short epilogue of DPP wave reductions and
+// one LDS exchange.
 //
 // Per row it yields the quantities the verification rules read: the
 // log-normaliser, the normalised entropy h = H(p)/log V that the FLy gate
 // compares with theta (page "Training-Free Loosely Speculative Decoding...",
 // section "2. Metodologia", part A), the top token, the probability of the
-// drafted token, and for draft rows q_max and logit(q_max), the feature of the
+// drafted token, and q_max with its log-odds logit(q_max), the feature of the
 // adaptive-verification estimator (page "Verificacion Adaptativa sin una
 // cabeza de confianza", section "Puntuar la Distribucion").
 //
 // Arithmetic is in base 2: with c = log2(e)/T every term is 2^(l*c - mc),
-// where mc = m*c and m is the running maximum of the raw logits.  Terms are
-// summed in float within a chunk of UNROLL vectors and chunk sums in double.
+// where mc = m*c and m is the running maximum of the raw logits.  A thread
+// reads its share of the row in chunks of UNROLL vectors (UNROLL*8 bfloat16
+// or UNROLL*4 float logits); terms are summed in float inside a chunk and
+// chunk sums in double.  Each thread keeps the chunk that holds its maximum
+// apart (its sums and its raw data in registers), so the end can replace that
+// chunk by its terms other than the argmax and form 1 - q_max without
+// cancellation, however peaked the row.
 #pragma once
 
 #include "sv_common.hpp"
@@ -36,7 +41,7 @@ struct RowGroup {
     float *qmax;
     float *feat;
     // internal results, nullable
-    double *lse2;     // [rows] log2 normaliser: mc + log2(s)
+    double *lse2;     // [rows] log2 normaliser: log2 sum_x 2^(l_x c)
     double *logtok2;  // [B*K]  log2 probability of the gathered token
     float *h_int;     // [rows]
     int32_t *am_int;  // [rows]
@@ -54,46 +59,6 @@ struct RowArgs {
     const int32_t *kept_len;  // [B] or null
     float c;                  // log2(e) / T
 };
-
-// Per-thread (and merged) state.  s and t hold every term except those of
-// the chunk that holds the current argmax, whose float sums cs / ct ride
-// alongside; keeping them apart lets the final step replace that chunk by its
-// non-argmax terms without cancellation, however peaked the row.
-struct RowState {
-    float m;    // running maximum of the raw logits
-    float mc;   // m * c: every term is 2^(l*c - mc)
-    double s;   // sum of the terms outside the argmax chunk
-    double t;   // sum of term * (l*c - mc) outside the argmax chunk
-    float cs;   // sum of the argmax chunk's terms
-    float ct;   // sum of the argmax chunk's term * (l*c - mc)
-    int pos;    // first id attaining m (INT_MAX: none)
-};
-
-__device__ __forceinline__ RowState merge_states(const RowState &a, const RowState &b) {
-    const bool bw = (b.m > a.m) || (b.m == a.m && b.pos < a.pos);
-    const RowState &hi = bw ? b : a;
-    const RowState &lo = bw ? a : b;
-    const float dl = lo.mc - hi.mc;  // <= 0
-    const double al = static_cast<double>(hw_exp2(dl));
-    const double ls = lo.s + static_cast<double>(lo.cs);
-    const double lt = lo.t + static_cast<double>(lo.ct);
-    RowState r = hi;
-    r.s = hi.s + al * ls;
-    r.t = hi.t + al * (lt + static_cast<double>(dl) * ls);
-    return r;
-}
-
-__device__ __forceinline__ RowState shfl_state(const RowState &s, int mask) {
-    RowState o;
-    o.m = __shfl_xor(s.m, mask, kWave);
-    o.mc = __shfl_xor(s.mc, mask, kWave);
-    o.s = __shfl_xor(s.s, mask, kWave);
-    o.t = __shfl_xor(s.t, mask, kWave);
-    o.cs = __shfl_xor(s.cs, mask, kWave);
-    o.ct = __shfl_xor(s.ct, mask, kWave);
-    o.pos = __shfl_xor(s.pos, mask, kWave);
-    return o;
-}
 
 template <typename T, int BLOCK, int UNROLL, bool ENT>
 __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int64_t row) {
@@ -134,16 +99,14 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     const int nvec = (V + EPV - 1) / EPV;
     const uint4 *vrow = reinterpret_cast<const uint4 *>(rp);
 
-    RowState st;
-    st.m = kNoMax;
-    st.mc = kNoMax * c;
-    st.s = 0.0;
-    st.t = 0.0;
-    st.cs = 0.f;
-    st.ct = 0.f;
-    st.pos = INT_MAX;
+    // Thread state.  s, t: sums outside the chunk that holds the maximum;
+    // cs, ct: that chunk's sums; saved / v0b: that chunk's data and position.
+    float m = kNoMax, mc = kNoMax * c, cs = 0.f, ct = 0.f;
+    double s = 0.0, t = 0.0;
+    int v0b = -1;
     uint4 saved[UNROLL];
-    int saved_v0 = -1;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) saved[u] = make_uint4(0u, 0u, 0u, 0u);
 
     auto consume = [&](const uint4 (&buf)[UNROLL], int v0) {
         float x[N];
@@ -152,59 +115,51 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
         float cm = x[0];
 #pragma unroll
         for (int k = 1; k < N; ++k) cm = fmaxf(cm, x[k]);
-        const bool up = cm > st.m;
-        const float mn = up ? cm : st.m;
+        const bool up = cm > m;
+        const float mn = fmaxf(cm, m);
         const float mcn = mn * c;
-        float cs[4] = {0.f, 0.f, 0.f, 0.f}, ct[4] = {0.f, 0.f, 0.f, 0.f};
+        float s4[4] = {0.f, 0.f, 0.f, 0.f}, t4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             float d = fmaf(x[k], c, -mcn);
             if (ENT) d = fmaxf(d, kMinExp2);
             const float e = hw_exp2(d);
-            cs[k & 3] += e;
-            if (ENT) ct[k & 3] = fmaf(e, d, ct[k & 3]);
+            s4[k & 3] += e;
+            if (ENT) t4[k & 3] = fmaf(e, d, t4[k & 3]);
         }
-        const float csum = (cs[0] + cs[1]) + (cs[2] + cs[3]);
-        const float ctsum = ENT ? (ct[0] + ct[1]) + (ct[2] + ct[3]) : 0.f;
-        if (up) {
-            // the old argmax chunk joins the rest; everything rescales to mn
-            const float dl = st.mc - mcn;
-            const double al = static_cast<double>(hw_exp2(dl));
-            const double stot = st.s + static_cast<double>(st.cs);
-            if (ENT) st.t = al * (st.t + static_cast<double>(st.ct) + static_cast<double>(dl) * stot);
-            st.s = al * stot;
-            st.cs = csum;
-            st.ct = ctsum;
-            st.m = mn;
-            st.mc = mcn;
-            saved_v0 = v0;
+        const float csum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        const float ctsum = ENT ? (t4[0] + t4[1]) + (t4[2] + t4[3]) : 0.f;
+        // Branch-free update: if the maximum moved, the previous max chunk
+        // joins the rest and everything is rescaled to the new maximum
+        // (factor 2^dl); otherwise this chunk joins the rest (dl = 0).
+        const float dl = mc - mcn;
+        const double al = static_cast<double>(hw_exp2(dl));
+        const double stot = s + static_cast<double>(up ? cs : csum);
+        if (ENT) {
+            const double ttot = t + static_cast<double>(up ? ct : ctsum);
+            t = al * (ttot + static_cast<double>(dl) * (up ? stot : 0.0));
+        }
+        s = al * stot;
+        cs = up ? csum : cs;
+        ct = up ? ctsum : ct;
+        m = mn;
+        mc = mcn;
+        v0b = up ? v0 : v0b;
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) saved[u] = buf[u];
-        } else {
-            st.s += static_cast<double>(csum);
-            if (ENT) st.t += static_cast<double>(ctsum);
+        for (int u = 0; u < UNROLL; ++u) {
+            saved[u].x = up ? buf[u].x : saved[u].x;
+            saved[u].y = up ? buf[u].y : saved[u].y;
+            saved[u].z = up ? buf[u].z : saved[u].z;
+            saved[u].w = up ? buf[u].w : saved[u].w;
         }
     };
 
     int v = tid;
-    if (v + (UNROLL - 1) * BLOCK < nfull) {
-        uint4 cur[UNROLL];
+    for (; v + (UNROLL - 1) * BLOCK < nfull; v += UNROLL * BLOCK) {
+        uint4 buf[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) cur[u] = vrow[v + u * BLOCK];
-        for (;;) {
-            const int vn = v + UNROLL * BLOCK;
-            const bool more = vn + (UNROLL - 1) * BLOCK < nfull;
-            uint4 nxt[UNROLL];
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < UNROLL; ++u) nxt[u] = vrow[vn + u * BLOCK];
-            }
-            consume(cur, v);
-            v = vn;
-            if (!more) break;
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) cur[u] = nxt[u];
-        }
+        for (int u = 0; u < UNROLL; ++u) buf[u] = vrow[v + u * BLOCK];
+        consume(buf, v);
     }
     if (v < nvec) {  // last, partly filled chunk of this thread
         uint4 buf[UNROLL];
@@ -222,80 +177,91 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
         consume(buf, v);
     }
 
-    // Exact argmax of this thread: first element of the saved chunk equal to
-    // the thread's maximum (element order: vector u-major, lane k-minor).
-    if (saved_v0 >= 0) {
-        float x[N];
+    // First id attaining the thread maximum (element order inside the saved
+    // chunk: vector u-major, lane k-minor).
+    float xs[N];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) E::unpack(saved[u], x + u * EPV);
+    for (int u = 0; u < UNROLL; ++u) E::unpack(saved[u], xs + u * EPV);
+    int pos = INT_MAX;
+    if (v0b >= 0) {
 #pragma unroll
         for (int k = N - 1; k >= 0; --k)
-            if (x[k] == st.m) st.pos = (saved_v0 + (k / EPV) * BLOCK) * EPV + (k % EPV);
+            if (xs[k] == m) pos = (v0b + (k / EPV) * BLOCK) * EPV + (k % EPV);
     }
-    const int own_pos = st.pos;
 
-    // Wave, then workgroup reduction in a fixed order.
-#pragma unroll
-    for (int msk = kWave / 2; msk > 0; msk >>= 1) st = merge_states(st, shfl_state(st, msk));
-    __shared__ RowState sh[NW];
-    __shared__ RowState total;
-    __shared__ float others_s, others_t;  // the argmax chunk's other terms
+    // (1) Row maximum and its first id in one key: (ordered max, -id).
+    __shared__ uint64_t sh_key[NW];
+    __shared__ double sh_s[NW], sh_t[NW];
     const int lane = tid & (kWave - 1), wv = tid / kWave;
-    if (lane == 0) sh[wv] = st;
+    const uint64_t key =
+        (static_cast<uint64_t>(ordered_bits(m)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(pos));
+    const uint64_t wkey = wave_max_u64(key);
+    if (lane == 0) sh_key[wv] = wkey;
     __syncthreads();
-    if (tid == 0) {
-        RowState acc = sh[0];
+    uint64_t bkey = sh_key[0];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) acc = merge_states(acc, sh[w]);
-        total = acc;
-        others_s = 0.f;
-        others_t = 0.f;
-    }
-    __syncthreads();
-    const RowState fin = total;
+    for (int w = 1; w < NW; ++w) bkey = sh_key[w] > bkey ? sh_key[w] : bkey;
+    const float M = from_ordered_bits(static_cast<uint32_t>(bkey >> 32));
+    const int P = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(bkey));
+    const float Mc = M * c;
 
-    // Replace the argmax chunk by its terms other than the argmax itself,
-    // recomputed by the thread that holds it: r = sum_{x != argmax} terms and
-    // t_o = sum_{x != argmax} term * exponent, free of cancellation.
-    if (own_pos == fin.pos && fin.pos != INT_MAX) {
-        float x[N];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) E::unpack(saved[u], x + u * EPV);
+    // (2) Every thread rescales its sums to M.  The thread holding the
+    // argmax swaps its max chunk for that chunk's other terms, so the block
+    // sums are r = sum_{x != argmax} 2^(l_x c - Mc) and the matching entropy
+    // numerator t_o.
+    double X, Y = 0.0;
+    if (pos == P && P != INT_MAX) {
         float os = 0.f, ot = 0.f;
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            const int id = (saved_v0 + (k / EPV) * BLOCK) * EPV + (k % EPV);
-            if (id != fin.pos) {
-                float d = fmaf(x[k], c, -fin.mc);
+            const int id = (v0b + (k / EPV) * BLOCK) * EPV + (k % EPV);
+            if (id != P) {
+                float d = fmaf(xs[k], c, -Mc);
                 if (ENT) d = fmaxf(d, kMinExp2);
                 const float e = hw_exp2(d);
                 os += e;
                 if (ENT) ot = fmaf(e, d, ot);
             }
         }
-        others_s = os;
-        others_t = ot;
+        X = s + static_cast<double>(os);
+        if (ENT) Y = t + static_cast<double>(ot);
+    } else {
+        const float dl = mc - Mc;
+        const double al = static_cast<double>(hw_exp2(dl));
+        const double st = s + static_cast<double>(cs);
+        X = al * st;
+        if (ENT) Y = al * (t + static_cast<double>(ct) + static_cast<double>(dl) * st);
+    }
+    const double wx = wave_sum_f64(X);
+    const double wy = ENT ? wave_sum_f64(Y) : 0.0;
+    if (lane == 0) {
+        sh_s[wv] = wx;
+        sh_t[wv] = wy;
     }
     __syncthreads();
 
     if (tid == 0) {
-        // The argmax term is 2^r0 with r0 = m*c - mc, the rounding residue of
-        // mc (exact in float); the row's sum is 2^r0 + r.
-        const double r0 = static_cast<double>(fmaf(fin.m, c, -fin.mc));
+        double r = 0.0, to = 0.0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            r += sh_s[w];
+            to += sh_t[w];
+        }
+        // The argmax term is 2^r0 with r0 = M*c - Mc, the rounding residue of
+        // Mc (exact in float); the row's sum of terms is 2^r0 + r.
+        const double r0 = static_cast<double>(fmaf(M, c, -Mc));
         const double e0 = exp2(r0);
-        const double r = fin.s + static_cast<double>(others_s);
-        const double rho = r / e0;        // (1 - q_max) / q_max
-        const double l1p = log1p(rho);    // ln(sum / 2^r0)
-        const double lse2 = static_cast<double>(fin.mc) + r0 + l1p * kLog2eD;
+        const double rho = r / e0;      // (1 - q_max) / q_max
+        const double l1p = log1p(rho);  // ln(sum / 2^r0)
+        const double lse2 = static_cast<double>(Mc) + r0 + l1p * kLog2eD;
         if (g.lse2) g.lse2[row] = lse2;
         if (g.lse) g.lse[row] = static_cast<float>(lse2 * kLn2);
-        const int am = fin.pos == INT_MAX ? -1 : fin.pos;
+        const int am = P == INT_MAX ? -1 : P;
         if (g.argmax) g.argmax[row] = am;
         if (g.am_int) g.am_int[row] = am;
         if (ENT) {
-            // H = ln(sum) - ln2 * t_all / sum, rewritten around the argmax term:
-            // H = ln(1 + rho) + ln2 (r0 r - t_o) / (2^r0 + r).
-            const double to = fin.t + static_cast<double>(others_t);
+            // H = ln(sum) - ln2 * (sum of term*exponent) / sum, rewritten
+            // around the argmax term: H = ln(1 + rho) + ln2 (r0 r - t_o) / (2^r0 + r).
             const double H = l1p + kLn2 * (r0 * r - to) / (e0 + r);
             const float h = static_cast<float>(H / log(static_cast<double>(V)));
             if (g.entropy) g.entropy[row] = h;
