@@ -170,7 +170,7 @@ def main():
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "row_stats_kernel<bf16,256,4,entropy>", "kernel_us": round(kms * 1e3, 2),
+                "kernel": "row_stats_kernel<bf16,512,2,entropy>", "kernel_us": round(kms * 1e3, 2),
                 "algorithmic_bytes_per_launch": bytes_per_step,
                 "source_hash": row_pass_source_hash()}
     log("row pass: %.1f us/launch, %.0f GB/s (%.1f%% of peak)" % (kms * 1e3, achieved,

@@ -18,9 +18,18 @@ namespace {
 using namespace sv;
 
 // Row pass shape: threads per workgroup and 16-byte vectors per thread per
-// chunk (one chunk = UNROLL*8 bfloat16 or UNROLL*4 float logits).
-constexpr int kRowBlock = 256;
-constexpr int kRowUnroll = 4;
+// chunk.  A chunk holds 16 bfloat16 or 16 float logits.
+constexpr int kRowBlock = 512;
+template <typename T>
+struct RowUnroll;
+template <>
+struct RowUnroll<uint16_t> {
+    static constexpr int value = 2;
+};
+template <>
+struct RowUnroll<float> {
+    static constexpr int value = 4;
+};
 // Race shape and the number of race workgroups to aim for per launch.
 constexpr int kRaceBlock = 256;
 constexpr int kRaceTargetBlocks = 2048;
@@ -109,7 +118,8 @@ spec_status launch_status() {
 // ---------------------------------------------------------------------------
 template <typename T, bool E0>
 void launch_rows_t(const RowArgs &a, int nblocks, hipStream_t st) {
-    row_stats_kernel<T, kRowBlock, kRowUnroll, E0><<<dim3(nblocks), dim3(kRowBlock), 0, st>>>(a);
+    row_stats_kernel<T, kRowBlock, RowUnroll<T>::value, E0>
+        <<<dim3(nblocks), dim3(kRowBlock), 0, st>>>(a);
 }
 
 void launch_rows(int32_t dtype, const RowArgs &a, int nblocks, bool e0, hipStream_t st) {

@@ -11,6 +11,8 @@
 // adaptive-verification estimator (page "Verificacion Adaptativa sin una
 // cabeza de confianza", section "Puntuar la Distribucion").
 //
+// Rows are streamed with non-temporal 16-byte loads.
+//
 // Arithmetic is in base 2: with c = log2(e)/T every term is 2^(l*c - mc),
 // where mc = m*c and m is the running maximum of the raw logits.  A thread
 // reads its share of the row in chunks of UNROLL vectors (UNROLL*8 bfloat16
@@ -158,7 +160,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     for (; v + (UNROLL - 1) * BLOCK < nfull; v += UNROLL * BLOCK) {
         uint4 buf[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) buf[u] = vrow[v + u * BLOCK];
+        for (int u = 0; u < UNROLL; ++u) buf[u] = load_stream(vrow + v + u * BLOCK);
         consume(buf, v);
     }
     if (v < nvec) {  // last, partly filled chunk of this thread

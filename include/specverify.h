@@ -107,7 +107,8 @@ size_t spec_draft_stats_bytes(int32_t batch, int32_t num_draft);
  *
  * target       device, [B][K+1] rows of logits.
  * draft        device, [B][K] rows of draft logits.  Required in lossless
- *              mode unless draft_stats is given; ignored in FLy mode.
+ *              mode (a rejected position re-reads its draft row even when
+ *              draft_stats is given); ignored in FLy mode.
  * draft_tokens device, int32 [B][K].  A token outside [0, V) has p = q = 0:
  *              it is rejected in lossless mode and counts as a deviation in
  *              FLy mode.
