@@ -11,10 +11,13 @@ rows in the 256 MB last-level cache.  Prints one JSON line.
 
 Besides the headline it reports:
   roofline      the streaming row pass (the dominant kernel), launched back to
-                back between two HIP events on its stream: algorithmic bytes /
-                mean launch time against the 8 TB/s HBM peak; `traffic` comes from
+                back with HIP events on its stream: algorithmic bytes / mean
+                launch time against the 8 TB/s HBM peak; `traffic` comes from
                 rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded under
                 profiles/ for the same kernel source, else null;
+  read_ceiling  the row pass's load-only twin (same grid, loads and shape) on
+                the same rows: the bandwidth this access pattern reaches on the
+                machine, next to the nominal 8 TB/s;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
   secondary     the other verification workloads (lossless with adaptive
                 verification, lossless at T=0.7 on V=152064, the full
@@ -162,6 +165,31 @@ def main():
     torch.cuda.synchronize()
     kms = k0.elapsed_time(k1) / n_k  # back-to-back launches on the launch stream
     achieved = bytes_per_step / (kms * 1e-3) / 1e9
+
+    # Same-shape ceiling: the load-only twin of the row pass (same grid, loads
+    # and workgroup shape) over the same rows, timed the same way.
+    sink = torch.empty(rows, dtype=torch.int32, device=dev)
+    for i in range(args.warmup):
+        sv.read_probe(flat[i % 2], sink=sink)
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    pev[0].record(stream)
+    for i in range(n_k):
+        sv.read_probe(flat[i % 2], sink=sink)
+    pev[1].record(stream)
+    torch.cuda.synchronize()
+    pms = pev[0].elapsed_time(pev[1]) / n_k
+    ceiling = {"kernel": "read_probe_kernel<512,2> (load-only twin of the row pass)",
+               "kernel_us": round(pms * 1e3, 2),
+               "gbps": round(bytes_per_step / (pms * 1e-3) / 1e9, 1),
+               "row_pass_frac_of_ceiling": round(pms / kms, 4)}
+    log("read ceiling: %.1f us/launch, %.0f GB/s" % (pms * 1e3, ceiling["gbps"]))
+
+    # Spread: the headline step and the row pass again, with an event between
+    # consecutive calls.  Each event leaves the queue idle for a few us before
+    # the next kernel, so these figures sit above the back-to-back means.
+    step_us = _evented(step, args.steps, stream, torch)
+    launch_us = _evented(row_launch, n_k, stream, torch)
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -172,6 +200,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": "row_stats_kernel<bf16,512,2,entropy>", "kernel_us": round(kms * 1e3, 2),
                 "algorithmic_bytes_per_launch": bytes_per_step,
+                "evented_launch_us_p10_p50_p90": _pcts(launch_us),
                 "source_hash": row_pass_source_hash()}
     log("row pass: %.1f us/launch, %.0f GB/s (%.1f%% of peak)" % (kms * 1e3, achieved,
                                                                   100 * achieved / HBM_PEAK_GBPS))
@@ -196,10 +225,30 @@ def main():
                    "rows_per_step": rows, "bytes_per_step": bytes_per_step,
                    "input_sets": 2},
         "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "evented_step_us_p10_p50_p90": _pcts(step_us),
         "mean_accepted_len": round(acc_mean, 4),
-        "roofline": roofline, "cpu_baseline": cpu, "secondary": secondary,
+        "roofline": roofline, "read_ceiling": ceiling, "cpu_baseline": cpu,
+        "secondary": secondary,
     }
     print(json.dumps(res), flush=True)
+
+
+def _pcts(xs):
+    """p10, p50, p90 of a sorted list (nearest rank)."""
+    n = len(xs)
+    return [round(xs[min(n - 1, int(q * n))], 2) for q in (0.1, 0.5, 0.9)]
+
+
+def _evented(fn, n, stream, torch):
+    """Sorted per-call durations (us) of n calls with an event between each."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        fn(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n))
 
 
 def _timeit(fn, n, warm, stream, torch):

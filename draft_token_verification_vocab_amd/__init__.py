@@ -61,6 +61,8 @@ _SIGNATURES = {
                                         ctypes.c_float, _P, _P]),
     "spec_row_stats": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
                                         ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P, _P]),
+    "spec_read_probe": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                         _P, _P]),
     "spec_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 
@@ -268,3 +270,20 @@ def row_stats(logits: torch.Tensor, *, temperature: float = 1.0, vocab: Optional
                                  _ptr(res["qmax"]), _ptr(res["feat"]), _stream(dev)),
            "spec_row_stats")
     return {k: v for k, v in res.items() if v is not None}
+
+
+def read_probe(logits: torch.Tensor, *, row_bytes: Optional[int] = None,
+               sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Load-only pass over the rows of a [rows, S] tensor with the row pass's
+    loads and grid (a bandwidth ceiling for it); returns the XOR of each
+    row's 32-bit words (the first row_bytes bytes, default all S)."""
+    _need_cuda(logits, "logits")
+    x = logits.reshape(-1, logits.shape[-1])
+    rows, S = x.shape
+    stride_b = S * x.element_size()
+    rb = stride_b if row_bytes is None else int(row_bytes)
+    if sink is None:
+        sink = torch.empty(rows, dtype=torch.int32, device=x.device)
+    _check(load().spec_read_probe(_ptr(x), rows, rb, stride_b, _ptr(sink), _stream(x.device)),
+           "spec_read_probe")
+    return sink

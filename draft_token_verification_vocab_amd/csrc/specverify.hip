@@ -35,6 +35,8 @@ constexpr int kRaceBlock = 256;
 constexpr int kRaceTargetBlocks = 2048;
 constexpr int kMaxSegs = 64;
 constexpr int kSmallBlock = 64;
+// FLy resolver: one wave per sequence.
+constexpr int kFlyBlock = 256;
 
 size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -249,7 +251,9 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     if ((s = launch_status()) != SPEC_OK) return s;
 
     if (!lossless) {
-        fly_kernel<<<dim3((B + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock), 0, st>>>(
+        constexpr int seqs_per_block = kFlyBlock / kWave;
+        fly_kernel<kFlyBlock><<<dim3((B + seqs_per_block - 1) / seqs_per_block), dim3(kFlyBlock), 0,
+                                st>>>(
             draft_tokens, kept_len, t_am, t_h, B, K, p.fly_theta, p.fly_window,
             out->accepted_len, out->tokens);
         return launch_status();
@@ -371,6 +375,20 @@ spec_status spec_row_stats(const void *logits, int64_t rows, int32_t vocab, int6
     ra.c = log2e_over(temperature);
     launch_rows(dtype, ra, static_cast<int>(rows), entropy != nullptr,
                 static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+spec_status spec_read_probe(const void *logits, int64_t rows, int64_t row_bytes,
+                            int64_t row_stride_bytes, uint32_t *sink, void *stream) {
+    if (rows < 0 || row_bytes < 0 || row_bytes % 16 != 0 || row_stride_bytes % 16 != 0 ||
+        row_bytes > row_stride_bytes)
+        return SPEC_ERR_ARG;
+    if (rows > INT32_MAX) return SPEC_ERR_UNSUPPORTED;
+    if (rows == 0) return SPEC_OK;
+    if (!logits || !aligned16(logits) || !sink) return SPEC_ERR_ARG;
+    read_probe_kernel<kRowBlock, RowUnroll<uint16_t>::value>
+        <<<dim3(static_cast<unsigned>(rows)), dim3(kRowBlock), 0, static_cast<hipStream_t>(stream)>>>(
+            logits, row_bytes / 16, row_stride_bytes / 16, sink);
     return launch_status();
 }
 

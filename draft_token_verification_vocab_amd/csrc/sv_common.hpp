@@ -29,6 +29,11 @@ __device__ __forceinline__ uint4 load_stream(const uint4 *p) {
     const v4u32 r = __builtin_nontemporal_load(reinterpret_cast<const v4u32 *>(p));
     return make_uint4(r.x, r.y, r.z, r.w);
 }
+// The same load at a wave-uniform base plus a 32-bit per-lane byte offset,
+// the form the hardware addresses with a scalar base register.
+__device__ __forceinline__ uint4 load_stream_at(const void *base, uint32_t byte_off) {
+    return load_stream(reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + byte_off));
+}
 
 // Raw hardware transcendentals (v_exp_f32 / v_log_f32: base 2, ~1 ulp).
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

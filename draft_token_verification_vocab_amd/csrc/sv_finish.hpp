@@ -270,36 +270,54 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
 // when the next W drafts exist and all match (else rejected, retroactively
 // when the target deviates again inside the window).  The replacement or
 // bonus token is the target's top token at the stopping row.
-__global__ void fly_kernel(const int32_t *tokens, const int32_t *kept_len, const int32_t *am,
-                           const float *h, int B, int K, float theta, int W,
-                           int32_t *accepted_len, int32_t *out_tokens) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+template <int NT>
+__global__ __launch_bounds__(NT) void fly_kernel(const int32_t *tokens, const int32_t *kept_len,
+                                                 const int32_t *am, const float *h, int B, int K,
+                                                 float theta, int W, int32_t *accepted_len,
+                                                 int32_t *out_tokens) {
+    // One wave per sequence: lane k holds position k (K <= 64), the
+    // deviation and gate tests become two ballots, and the scan runs on
+    // wave-uniform bit masks.
+    const int lane = threadIdx.x & (kWave - 1);
+    const int b = __builtin_amdgcn_readfirstlane(
+        static_cast<int>((blockIdx.x * NT + threadIdx.x) / kWave));
     if (b >= B) return;
-    const int L = kept_len ? clamp_len(kept_len[b], K) : K;
-    const int32_t *tok = tokens + b * K;
-    const int32_t *top = am + b * (K + 1);
-    const float *hb = h + b * (K + 1);
+    const int L = kept_len ? __builtin_amdgcn_readfirstlane(clamp_len(kept_len[b], K)) : K;
+    const int32_t *tok = tokens + static_cast<int64_t>(b) * K;
+    const int32_t *top = am + static_cast<int64_t>(b) * (K + 1);
+    const float *hb = h + static_cast<int64_t>(b) * (K + 1);
+    const bool live = lane < L;
+    const int32_t tk = live ? tok[lane] : 0;
+    const int32_t tp = lane < K + 1 ? top[lane] : 0;
+    const float hv = live ? hb[lane] : 0.f;
+    const uint64_t dev = __ballot(live && tk != tp);
+    const uint64_t gate = __ballot(live && hv >= theta);  // NaN entropy fails the gate
+
     int j = 0, jstar = L;
-    while (j < L) {
-        if (tok[j] == top[j]) {
-            ++j;
-            continue;
-        }
-        if (!(hb[j] >= theta) || j + W > L - 1) {
+    uint64_t rest = dev;  // deviations at positions >= j
+    while (rest != 0) {
+        j = __builtin_ctzll(rest);
+        if (!((gate >> j) & 1ull) || j + W > L - 1) {
             jstar = j;
             break;
         }
-        bool again = false;
-        for (int k = j + 1; k <= j + W; ++k) again |= tok[k] != top[k];
-        if (again) {
+        // here 0 <= W <= L-1-j <= 63: the window is positions j+1 .. j+W
+        const uint64_t win = W == 0 ? 0ull : (((1ull << W) - 1ull) << (j + 1));
+        if (dev & win) {
             jstar = j;
             break;
         }
-        j += W + 1;
+        const int nj = j + W + 1;
+        rest = nj >= 64 ? 0ull : (dev & (~0ull << nj));
     }
-    accepted_len[b] = jstar;
-    int32_t *ot = out_tokens + b * (K + 1);
-    for (int k = 0; k <= K; ++k) ot[k] = k < jstar ? tok[k] : (k == jstar ? top[jstar] : -1);
+    if (lane == 0) accepted_len[b] = jstar;
+    // the stopping row may be row K = 64, which no lane holds
+    const int32_t topj = jstar < kWave ? __shfl(tp, jstar) : top[jstar];
+    int32_t *ot = out_tokens + static_cast<int64_t>(b) * (K + 1);
+    for (int k = lane; k <= K; k += kWave) {
+        // k < jstar <= L <= 64 only on the first pass, where k == lane
+        ot[k] = k < jstar ? tk : (k == jstar ? topj : -1);
+    }
 }
 
 }  // namespace sv

@@ -102,15 +102,17 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     const uint4 *vrow = reinterpret_cast<const uint4 *>(rp);
 
     // Thread state.  s, t: sums outside the chunk that holds the maximum;
-    // cs, ct: that chunk's sums; saved / v0b: that chunk's data and position.
+    // cs, ct: that chunk's sums; saved / itb: that chunk's data and index.
     float m = kNoMax, mc = kNoMax * c, cs = 0.f, ct = 0.f;
     double s = 0.0, t = 0.0;
-    int v0b = -1;
+    int itb = -1;
     uint4 saved[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) saved[u] = make_uint4(0u, 0u, 0u, 0u);
 
-    auto consume = [&](const uint4 (&buf)[UNROLL], int v0) {
+    // it: the chunk's index; thread tid's chunk `it` starts at vector
+    // it*UNROLL*BLOCK + tid.
+    auto consume = [&](const uint4 (&buf)[UNROLL], int it) {
         float x[N];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) E::unpack(buf[u], x + u * EPV);
@@ -118,52 +120,85 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
 #pragma unroll
         for (int k = 1; k < N; ++k) cm = fmaxf(cm, x[k]);
         const bool up = cm > m;
-        const float mn = fmaxf(cm, m);
-        const float mcn = mn * c;
-        float s4[4] = {0.f, 0.f, 0.f, 0.f}, t4[4] = {0.f, 0.f, 0.f, 0.f};
+        const float mcn = up ? cm * c : mc;
+        // Terms of this chunk against the (possibly new) maximum.
+        float s4[4], t4[4];
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            float d = fmaf(x[k], c, -mcn);
-            if (ENT) d = fmaxf(d, kMinExp2);
+            const float d = fmaf(x[k], c, -mcn);
             const float e = hw_exp2(d);
-            s4[k & 3] += e;
-            if (ENT) t4[k & 3] = fmaf(e, d, t4[k & 3]);
+            if (k < 4) {
+                s4[k] = e;
+                if (ENT) t4[k] = e * d;
+            } else {
+                s4[k & 3] += e;
+                if (ENT) t4[k & 3] = fmaf(e, d, t4[k & 3]);
+            }
         }
         const float csum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-        const float ctsum = ENT ? (t4[0] + t4[1]) + (t4[2] + t4[3]) : 0.f;
-        // Branch-free update: if the maximum moved, the previous max chunk
-        // joins the rest and everything is rescaled to the new maximum
-        // (factor 2^dl); otherwise this chunk joins the rest (dl = 0).
-        const float dl = mc - mcn;
-        const double al = static_cast<double>(hw_exp2(dl));
-        const double stot = s + static_cast<double>(up ? cs : csum);
+        float ctsum = 0.f;
         if (ENT) {
-            const double ttot = t + static_cast<double>(up ? ct : ctsum);
-            t = al * (ttot + static_cast<double>(dl) * (up ? stot : 0.0));
-        }
-        s = al * stot;
-        cs = up ? csum : cs;
-        ct = up ? ctsum : ct;
-        m = mn;
-        mc = mcn;
-        v0b = up ? v0 : v0b;
+            ctsum = (t4[0] + t4[1]) + (t4[2] + t4[3]);
+            // A -inf logit gives the term 0 * -inf = NaN; such chunks (masked
+            // vocabulary, padding) are summed again with exponents clamped
+            // where 2^d is zero anyway.
+            if (!(ctsum == ctsum)) {
+                ctsum = 0.f;
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            saved[u].x = up ? buf[u].x : saved[u].x;
-            saved[u].y = up ? buf[u].y : saved[u].y;
-            saved[u].z = up ? buf[u].z : saved[u].z;
-            saved[u].w = up ? buf[u].w : saved[u].w;
+                for (int k = 0; k < N; ++k) {
+                    const float d = fmaxf(fmaf(x[k], c, -mcn), kMinExp2);
+                    ctsum = fmaf(hw_exp2(d), d, ctsum);
+                }
+            }
+        }
+        if (up) {
+            // A new thread maximum (rare after the first chunks): the old max
+            // chunk joins the rest, which is rescaled to the new maximum by
+            // 2^dl, and this chunk becomes the max chunk.
+            const float dl = mc - mcn;
+            const double al = static_cast<double>(hw_exp2(dl));
+            const double stot = s + static_cast<double>(cs);
+            if (ENT) t = al * (t + static_cast<double>(ct) + static_cast<double>(dl) * stot);
+            s = al * stot;
+            cs = csum;
+            ct = ctsum;
+            m = cm;
+            mc = mcn;
+            itb = it;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) saved[u] = buf[u];
+        } else {
+            s += static_cast<double>(csum);
+            if (ENT) t += static_cast<double>(ctsum);
         }
     };
 
-    int v = tid;
-    for (; v + (UNROLL - 1) * BLOCK < nfull; v += UNROLL * BLOCK) {
+    // Full chunks for every thread: a wave-uniform trip count and a uniform
+    // base address, so the loop control and addressing stay scalar.
+    constexpr int kChunkVecs = UNROLL * BLOCK;
+    const int nit = nfull / kChunkVecs;
+    // The next chunk's loads are issued before this chunk's arithmetic, so
+    // every wave keeps a chunk in flight while it computes.
+    uint4 nxt[UNROLL];
+    if (nit > 0) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            nxt[u] = load_stream_at(vrow, static_cast<uint32_t>(tid + u * BLOCK) * 16u);
+    }
+    for (int it = 0; it < nit; ++it) {
         uint4 buf[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) buf[u] = load_stream(vrow + v + u * BLOCK);
-        consume(buf, v);
+        for (int u = 0; u < UNROLL; ++u) buf[u] = nxt[u];
+        if (it + 1 < nit) {
+            const uint4 *cp = vrow + static_cast<int64_t>(it + 1) * kChunkVecs;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                nxt[u] = load_stream_at(cp, static_cast<uint32_t>(tid + u * BLOCK) * 16u);
+        }
+        consume(buf, it);
     }
-    if (v < nvec) {  // last, partly filled chunk of this thread
+    const int v = nit * kChunkVecs + tid;
+    if (v < nvec) {  // the last, partly filled chunk of this thread
         uint4 buf[UNROLL];
         const uint32_t ni = E::neg_inf_word();
 #pragma unroll
@@ -176,11 +211,12 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
             else
                 buf[u] = make_uint4(ni, ni, ni, ni);
         }
-        consume(buf, v);
+        consume(buf, nit);
     }
 
     // First id attaining the thread maximum (element order inside the saved
     // chunk: vector u-major, lane k-minor).
+    const int v0b = itb < 0 ? -1 : itb * kChunkVecs + tid;  // first vector of the max chunk
     float xs[N];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) E::unpack(saved[u], xs + u * EPV);
@@ -287,6 +323,39 @@ __global__ __launch_bounds__(BLOCK) void row_stats_kernel(RowArgs a) {
         row_one<T, BLOCK, UNROLL, ENT0>(a, a.g[0], blk);
     else
         row_one<T, BLOCK, UNROLL, false>(a, a.g[1], blk - a.nrows0);
+}
+
+// Load-only twin of the row pass: the same grid (a workgroup per row), the
+// same workgroup shape and the same non-temporal 16-byte loads, with the data
+// folded by XOR so that nothing is optimised away.
+template <int BLOCK, int UNROLL>
+__global__ __launch_bounds__(BLOCK) void read_probe_kernel(const void *base, int64_t row_vecs,
+                                                          int64_t stride_vecs, uint32_t *sink) {
+    const uint4 *row = static_cast<const uint4 *>(base) + blockIdx.x * stride_vecs;
+    const int tid = threadIdx.x;
+    uint32_t acc = 0;
+    for (int64_t v = tid; v < row_vecs; v += static_cast<int64_t>(UNROLL) * BLOCK) {
+        uint4 b[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t j = v + static_cast<int64_t>(u) * BLOCK;
+            b[u] = j < row_vecs ? load_stream(row + j) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) acc ^= b[u].x ^ b[u].y ^ b[u].z ^ b[u].w;
+    }
+    // XOR over the workgroup: lanes through shuffles, waves through LDS
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o /= 2) acc ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc), o));
+    __shared__ uint32_t sh[BLOCK / kWave];
+    if ((tid & (kWave - 1)) == 0) sh[tid / kWave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t r = 0;
+#pragma unroll
+        for (int w = 0; w < BLOCK / kWave; ++w) r ^= sh[w];
+        sink[blockIdx.x] = r;
+    }
 }
 
 }  // namespace sv

@@ -40,7 +40,8 @@ def L():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_av_score", "spec_av_update", "spec_row_stats",
-              "spec_workspace_bytes", "spec_draft_stats_bytes", "spec_status_string"):
+              "spec_workspace_bytes", "spec_draft_stats_bytes", "spec_status_string",
+              "spec_read_probe"):
         assert n in names
 
 
@@ -135,5 +136,9 @@ def test_other_entry_points_validate(L):
                             None, None) == -1
     assert L.spec_row_stats(ctypes.c_void_p(16), -1, 1024, 1024, 1, 1.0, None, None, None, None,
                             None, None) == -1
+    assert L.spec_read_probe(ctypes.c_void_p(16), 4, 24, 32, ctypes.c_void_p(16), None) == -1
+    assert L.spec_read_probe(ctypes.c_void_p(16), 4, 48, 32, ctypes.c_void_p(16), None) == -1
+    assert L.spec_read_probe(ctypes.c_void_p(16), 4, 32, 32, None, None) == -1
+    assert L.spec_read_probe(None, 0, 32, 32, None, None) == 0
     for s in (0, -1, -2, -3, -4, 99):
         assert isinstance(L.spec_status_string(s), bytes)

@@ -77,6 +77,16 @@ def test_row_stats_reproducible_and_ordered_ties():
     assert np_(a["argmax"]).tolist() == [12345, 0, 0]
 
 
+def test_read_probe_folds_every_word():
+    # the load-only ceiling kernel reads each row's bytes exactly: XOR per row
+    g = torch.Generator().manual_seed(3)
+    for rows, S, rb in ((7, 2056, 4112), (3, 128256, 256512), (5, 64, 96)):
+        xh = torch.randint(-2**15, 2**15, (rows, S), generator=g, dtype=torch.int16)
+        got = np_(sv.read_probe(xh.to(DEV), row_bytes=rb)).view(np.uint32)
+        words = xh.numpy().view(np.uint32)[:, :rb // 4]
+        assert np.array_equal(got, np.bitwise_xor.reduce(words, axis=1))
+
+
 # ---------------------------------------------------------------------------
 # FLy
 # ---------------------------------------------------------------------------
@@ -118,6 +128,27 @@ def test_fly_gate_branches():
     assert np.all(o["accepted_len"] == 8)
     kept = torch.randint(0, 9, (32,), generator=torch.Generator().manual_seed(1), dtype=torch.int32)
     _fly_check(batch, kept=kept)
+
+
+@pytest.mark.parametrize("window", [0, 1, 3, 62, 63, 64, 1 << 20])
+def test_fly_max_drafts_and_windows(window):
+    # K = 64, the largest draft length: every lane of the resolver's wave holds
+    # a position and the stopping row may be row 64.  High match rates make
+    # long windows pass; mixed entropies exercise both gate outcomes.
+    batch = W.fly(40, 64, 300, seed=11 + window % 7, stride=304, peak=9.0, p_match=0.97)
+    kept = torch.randint(0, 65, (40,), generator=torch.Generator().manual_seed(window % 5),
+                         dtype=torch.int32)
+    kept[:4] = 64
+    for theta in (0.2, 0.6):
+        _fly_check(batch, theta=theta, window=window)
+        _fly_check(batch, theta=theta, window=window, kept=kept)
+
+
+def test_fly_headline_full_size():
+    # the benchmarked FLy workload at its full size, every output checked
+    batch = W.make(2)
+    r, o, _, _ = _fly_check(batch)
+    assert r.accepted_len.shape[0] == 256 and batch.V == 128256
 
 
 # ---------------------------------------------------------------------------
