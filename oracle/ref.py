@@ -79,6 +79,16 @@ def lib():
         L.ref_av_loss.argtypes = [P, P, P, i32, i32, P, P]
         L.ref_av_loss.restype = f64
         L.ref_av_update.argtypes = [P, P, P, i32, i32, f64, P]
+        L.ref_irls_accumulate.argtypes = [P, P, P, i32, i32, P, P, P, P]
+        L.ref_irls_accumulate.restype = None
+        L.ref_irls_solve.argtypes = [i32, f64, P, P, P, P]
+        L.ref_irls_solve.restype = ctypes.c_int
+        L.ref_av_diagnostics.argtypes = [P, P, P, i32, i32, P, i32, P, P]
+        L.ref_av_diagnostics.restype = None
+        L.ref_av_budget.argtypes = [P, i32, i32, P, f64, P, P, P, P]
+        L.ref_av_budget.restype = i64
+        L.ref_ngram_propose.argtypes = [P, P, i32, i64, i32, i32, i32, P, P, P, P]
+        L.ref_ngram_propose.restype = None
         L.ref_av_update.restype = None
         _lib = L
     return _lib
@@ -234,3 +244,77 @@ def av_update(feat, accepted_len, kept_len, omega_beta, lr):
     ob = np.array(omega_beta, dtype=np.float64, copy=True)
     lib().ref_av_update(_ptr(feat), _ptr(acc), _ptr(kl), B, K, float(lr), _ptr(ob))
     return ob
+
+
+class IrlsState:
+    """Round accumulators of the IRLS refit: gradient, dense Hessian and the
+    label count behind each coefficient (all zero at the start of a round)."""
+
+    def __init__(self, K):
+        self.K = K
+        self.g = np.zeros(K + 1)
+        self.H = np.zeros((K + 1, K + 1))
+        self.cnt = np.zeros(K + 1, dtype=np.int64)
+
+
+def irls_accumulate(state, feat, accepted_len, kept_len, omega_beta):
+    f = np.ascontiguousarray(feat, dtype=np.float64)
+    B, K = f.shape
+    assert K == state.K
+    a = np.ascontiguousarray(accepted_len, dtype=np.int32)
+    kl = None if kept_len is None else np.ascontiguousarray(kept_len, dtype=np.int32)
+    ob = np.ascontiguousarray(omega_beta, dtype=np.float64)
+    lib().ref_irls_accumulate(_ptr(f), _ptr(a), _ptr(kl), B, K, _ptr(ob), _ptr(state.g),
+                              _ptr(state.H), _ptr(state.cnt))
+
+
+def irls_solve(state, omega_beta, c_damp):
+    """Solve the round's Newton system and update (a copy of) omega_beta.
+    Returns (new omega_beta, flags); the state is reset."""
+    ob = np.array(omega_beta, dtype=np.float64)
+    flags = lib().ref_irls_solve(state.K, float(c_damp), _ptr(state.g), _ptr(state.H),
+                                 _ptr(state.cnt), _ptr(ob))
+    return ob, int(flags)
+
+
+def av_diagnostics(feat, accepted_len, kept_len, omega_beta, nbins=10):
+    f = np.ascontiguousarray(feat, dtype=np.float64)
+    B, K = f.shape
+    a = np.ascontiguousarray(accepted_len, dtype=np.int32)
+    kl = None if kept_len is None else np.ascontiguousarray(kept_len, dtype=np.int32)
+    ob = np.ascontiguousarray(omega_beta, dtype=np.float64)
+    out = np.zeros(4)
+    near = ctypes.c_int32(0)
+    lib().ref_av_diagnostics(_ptr(f), _ptr(a), _ptr(kl), B, K, _ptr(ob), int(nbins), _ptr(out),
+                             ctypes.byref(near))
+    return {"auc": out[0], "logloss": out[1], "ece": out[2], "n": int(out[3]),
+            "near_bin_edge": bool(near.value)}
+
+
+def av_budget(conf, cost, n_requests=None):
+    c = np.ascontiguousarray(conf, dtype=np.float32)
+    B, K = c.shape
+    cs = np.ascontiguousarray(cost, dtype=np.float64)
+    assert cs.shape == (B * K + 1,)
+    kept = np.zeros(B, dtype=np.int32)
+    mask = np.zeros((B, K), dtype=np.uint8)
+    best = ctypes.c_double(0.0)
+    near = ctypes.c_int32(0)
+    nr = float(B if n_requests is None else n_requests)
+    k = lib().ref_av_budget(_ptr(c), B, K, _ptr(cs), nr, _ptr(kept), _ptr(mask),
+                            ctypes.byref(best), ctypes.byref(near))
+    return {"budget": int(k), "kept_len": kept, "mask": mask, "best_ratio": best.value,
+            "near": bool(near.value)}
+
+
+def ngram_propose(ctx, lengths, n_min, n_max, K):
+    c = np.ascontiguousarray(ctx, dtype=np.int32)
+    B, S = c.shape
+    ln = np.ascontiguousarray(lengths, dtype=np.int32)
+    draft = np.zeros((B, K), dtype=np.int32)
+    dl = np.zeros(B, dtype=np.int32)
+    mp = np.zeros(B, dtype=np.int32)
+    mn = np.zeros(B, dtype=np.int32)
+    lib().ref_ngram_propose(_ptr(c), _ptr(ln), B, S, int(n_min), int(n_max), int(K), _ptr(draft),
+                            _ptr(dl), _ptr(mp), _ptr(mn))
+    return {"draft": draft, "draft_len": dl, "match_pos": mp, "match_n": mn}

@@ -546,3 +546,290 @@ void ref_av_update(const double *feat, const int32_t *accepted_len, const int32_
     }
     free(g_beta);
 }
+
+/* ------------------------------------------------------------------------
+ * Newton (IRLS) refit of the scorer over rounds ([AV] "Ajuste de los
+ * Coeficientes").  Per step the labelled drafts of the batch add to the
+ * gradient g and Hessian H of the summed log-loss at the current
+ * coefficients theta = (omega, beta_0..beta_{K-1}); x_n = (f_n, e_{i_n}):
+ *   g += (s_n - y_n) x_n,   H += s_n (1 - s_n) x_n x_n^T,
+ * and cnt counts the labels behind each coefficient (all labels for omega,
+ * the labels at position i for beta_i).  At the round's end the system
+ * H dtheta = -g is solved and each coefficient moves by dtheta_k scaled by
+ * cnt_k / (cnt_k + c_damp).
+ * ------------------------------------------------------------------------ */
+void ref_irls_accumulate(const double *feat, const int32_t *accepted_len, const int32_t *kept_len,
+                         int32_t B, int32_t K, const double *omega_beta, double *g, double *H,
+                         int64_t *cnt) {
+    const int32_t D = K + 1;
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t n = n_labels_of(accepted_len, kept_len, K, b);
+        for (int32_t i = 0; i < n; ++i) {
+            double y = i < accepted_len[b] ? 1.0 : 0.0;
+            double f = feat[b * K + i];
+            double s = sigmoid(omega_beta[0] * f + omega_beta[1 + i]);
+            double x[2] = {f, 1.0};
+            int32_t idx[2] = {0, 1 + i};
+            for (int r = 0; r < 2; ++r) {
+                g[idx[r]] += (s - y) * x[r];
+                for (int q = 0; q < 2; ++q) H[idx[r] * D + idx[q]] += s * (1.0 - s) * x[r] * x[q];
+            }
+            cnt[0] += 1;
+            cnt[1 + i] += 1;
+        }
+    }
+}
+
+/* Cholesky solve of the n x n system A x = rhs (A symmetric, row-major, the
+ * lower triangle is overwritten).  Returns -1 when a pivot is at most
+ * tol (the system is treated as singular). */
+static int chol_solve(double *A, int n, double *rhs, double tol) {
+    for (int j = 0; j < n; ++j) {
+        double d = A[j * n + j];
+        for (int k = 0; k < j; ++k) d -= A[j * n + k] * A[j * n + k];
+        if (!(d > tol)) return -1;
+        double l = sqrt(d);
+        A[j * n + j] = l;
+        for (int i = j + 1; i < n; ++i) {
+            double v = A[i * n + j];
+            for (int k = 0; k < j; ++k) v -= A[i * n + k] * A[j * n + k];
+            A[i * n + j] = v / l;
+        }
+    }
+    for (int i = 0; i < n; ++i) { /* L y = rhs */
+        double v = rhs[i];
+        for (int k = 0; k < i; ++k) v -= A[i * n + k] * rhs[k];
+        rhs[i] = v / A[i * n + i];
+    }
+    for (int i = n - 1; i >= 0; --i) { /* L^T x = y */
+        double v = rhs[i];
+        for (int k = i + 1; k < n; ++k) v -= A[k * n + i] * rhs[k];
+        rhs[i] = v / A[i * n + i];
+    }
+    return 0;
+}
+
+int ref_irls_solve(int32_t K, double c_damp, double *g, double *H, int64_t *cnt,
+                   double *omega_beta) {
+    const int32_t D = K + 1;
+    int flags = 0;
+    if (cnt[0] > 0) {
+        /* coefficients with evidence; the system over the others is empty */
+        int act[65], na = 0;
+        double hmax = 0.0;
+        for (int32_t k = 0; k < D; ++k)
+            if (cnt[k] > 0 && H[k * D + k] > 0.0) {
+                act[na++] = k;
+                if (H[k * D + k] > hmax) hmax = H[k * D + k];
+            }
+        double A[65 * 65], x[65];
+        int ok = -1;
+        if (na > 0 && act[0] == 0) {
+            for (int r = 0; r < na; ++r) {
+                x[r] = -g[act[r]];
+                for (int q = 0; q < na; ++q) A[r * na + q] = H[act[r] * D + act[q]];
+            }
+            ok = chol_solve(A, na, x, 1e-12 * hmax);
+        }
+        if (ok != 0) {
+            /* no curvature left for the slope (e.g. every feature equal):
+             * hold omega and give each intercept its own Newton step */
+            flags |= 2;
+            int nb = 0;
+            for (int r = 0; r < na; ++r)
+                if (act[r] != 0) act[nb++] = act[r];
+            na = nb;
+            for (int r = 0; r < na; ++r) x[r] = -g[act[r]] / H[act[r] * D + act[r]];
+        }
+        for (int r = 0; r < na; ++r) {
+            int k = act[r];
+            double n = (double)cnt[k];
+            omega_beta[k] += x[r] * (n / (n + c_damp));
+        }
+        flags |= 1;
+    }
+    for (int32_t k = 0; k < D; ++k) {
+        g[k] = 0.0;
+        cnt[k] = 0;
+        for (int32_t q = 0; q < D; ++q) H[k * D + q] = 0.0;
+    }
+    return flags;
+}
+
+/* ------------------------------------------------------------------------
+ * Estimator diagnostics over one batch's labels ([AV] "Otras
+ * Caracteristicas Consideradas", the AUC / log-loss / ECE axes).  With
+ * z_n = omega f_n + beta_{i_n} and s_n = sigmoid(z_n):
+ *   AUC     = P(z of a random accepted draft > z of a random rejected one),
+ *             ties counting one half (NaN without both classes);
+ *   logloss = mean of -log s_n (accepted) and -log(1 - s_n) (rejected);
+ *   ECE     = sum over nbins equal-width bins of s of
+ *             (n_bin / N) |mean s - mean y| over the bin.
+ * out = {auc, logloss, ece, N}.  near (nullable): 1 when some s_n lies
+ * within 1e-9 of a bin edge.
+ * ------------------------------------------------------------------------ */
+void ref_av_diagnostics(const double *feat, const int32_t *accepted_len, const int32_t *kept_len,
+                        int32_t B, int32_t K, const double *omega_beta, int32_t nbins,
+                        double *out, int32_t *near) {
+    int64_t N = 0;
+    for (int32_t b = 0; b < B; ++b) N += n_labels_of(accepted_len, kept_len, K, b);
+    double *z = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    int8_t *y = (int8_t *)malloc((size_t)(N > 0 ? N : 1));
+    int64_t t = 0;
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t n = n_labels_of(accepted_len, kept_len, K, b);
+        for (int32_t i = 0; i < n; ++i) {
+            z[t] = omega_beta[0] * feat[b * K + i] + omega_beta[1 + i];
+            y[t] = (int8_t)(i < accepted_len[b]);
+            ++t;
+        }
+    }
+    /* AUC by counting every (accepted, rejected) pair */
+    double pairs_won = 0.0;
+    int64_t npos = 0, nneg = 0;
+    for (int64_t a = 0; a < N; ++a) {
+        if (y[a]) ++npos; else ++nneg;
+    }
+    for (int64_t a = 0; a < N; ++a) {
+        if (!y[a]) continue;
+        for (int64_t r = 0; r < N; ++r) {
+            if (y[r]) continue;
+            if (z[a] > z[r]) pairs_won += 1.0;
+            else if (z[a] == z[r]) pairs_won += 0.5;
+        }
+    }
+    double auc = (npos > 0 && nneg > 0) ? pairs_won / ((double)npos * (double)nneg) : NAN;
+    double loss = 0.0;
+    double *bs = (double *)calloc((size_t)(nbins > 0 ? nbins : 1), sizeof(double));
+    int nearb = 0;
+    for (int64_t a = 0; a < N; ++a) {
+        loss += y[a] ? softplus(-z[a]) : softplus(z[a]);
+        double s = sigmoid(z[a]);
+        double sm = s * nbins;
+        int bin = (int)floor(sm);
+        if (bin > nbins - 1) bin = nbins - 1;
+        if (bin < 0) bin = 0;
+        if (fabs(sm - floor(sm + 0.5)) < 1e-9 * nbins) nearb = 1;
+        bs[bin] += s - (double)y[a];
+    }
+    double ece = 0.0;
+    for (int q = 0; q < nbins; ++q) ece += fabs(bs[q]);
+    out[0] = auc;
+    out[1] = N > 0 ? loss / (double)N : NAN;
+    out[2] = N > 0 ? ece / (double)N : NAN;
+    out[3] = (double)N;
+    if (near) *near = nearb;
+    free(z);
+    free(y);
+    free(bs);
+}
+
+/* ------------------------------------------------------------------------
+ * Budgeted trimming ([AV] "Otras Caracteristicas Consideradas", the
+ * survival / top-k and budget snippets).  Survival of draft (b, i) is the
+ * running product of the confidences along the sequence, formed in float
+ * as the device forms it.  With the B*K survivals sorted in decreasing order
+ * (ties: lower flat index b*K+i first), the expected emitted tokens for a
+ * budget of k drafts are n_requests + (sum of the first k survivals), and
+ * the budget is the k in 0..B*K maximising that over cost[k] (the first
+ * maximum).  The kept drafts are the first `budget` in that order; since
+ * survival never grows along a sequence they form a prefix of each.
+ * Returns the budget; near (nullable) is 1 when the best two ratios are
+ * within 1e-12 relative.
+ * ------------------------------------------------------------------------ */
+static const float *g_sort_keys;
+static int cmp_survival(const void *pa, const void *pb) {
+    int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+    float sa = g_sort_keys[a], sb = g_sort_keys[b];
+    if (sa > sb) return -1;
+    if (sa < sb) return 1;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+int64_t ref_av_budget(const float *conf, int32_t B, int32_t K, const double *cost,
+                      double n_requests, int32_t *kept_len, uint8_t *mask, double *best_ratio,
+                      int32_t *near) {
+    const int64_t M = (int64_t)B * K;
+    float *surv = (float *)malloc((size_t)(M > 0 ? M : 1) * sizeof(float));
+    int64_t *ord = (int64_t *)malloc((size_t)(M > 0 ? M : 1) * sizeof(int64_t));
+    for (int32_t b = 0; b < B; ++b) {
+        float P = 1.0f;
+        for (int32_t i = 0; i < K; ++i) {
+            P = P * conf[(int64_t)b * K + i];
+            surv[(int64_t)b * K + i] = P;
+        }
+    }
+    for (int64_t t = 0; t < M; ++t) ord[t] = t;
+    g_sort_keys = surv;
+    qsort(ord, (size_t)M, sizeof(int64_t), cmp_survival);
+    double est = n_requests, best = est / cost[0], second = -INFINITY;
+    int64_t budget = 0;
+    for (int64_t k = 1; k <= M; ++k) {
+        est += (double)surv[ord[k - 1]];
+        double r = est / cost[k];
+        if (r > best) {
+            second = best;
+            best = r;
+            budget = k;
+        } else if (r > second) {
+            second = r;
+        }
+    }
+    for (int32_t b = 0; b < B; ++b) kept_len[b] = 0;
+    if (mask) memset(mask, 0, (size_t)M);
+    for (int64_t t = 0; t < budget; ++t) {
+        int64_t f = ord[t];
+        kept_len[f / K] += 1;
+        if (mask) mask[f] = 1;
+    }
+    if (best_ratio) *best_ratio = best;
+    if (near) *near = (second > -INFINITY && best - second <= 1e-12 * fabs(best)) ? 1 : 0;
+    free(surv);
+    free(ord);
+    return budget;
+}
+
+/* ------------------------------------------------------------------------
+ * Prompt-lookup drafting ([SD] "N-gram (prompt lookup)"; [FLy] "B.
+ * Aceleracao Multinivel"): for each sequence, the longest suffix n-gram
+ * (n from n_max down to n_min) that also occurs earlier in the context; of
+ * its earlier occurrences the latest (closest to the end) is taken, and the
+ * up to K tokens that followed it are the draft.  ctx: [B][stride] tokens,
+ * len: [B] context lengths.  draft: [B][K] (-1 after draft_len), draft_len
+ * [B], match_pos [B] (start of the matched occurrence, -1 when none), match_n
+ * [B] (its length, 0 when none).
+ * ------------------------------------------------------------------------ */
+void ref_ngram_propose(const int32_t *ctx, const int32_t *len, int32_t B, int64_t stride,
+                       int32_t n_min, int32_t n_max, int32_t K, int32_t *draft,
+                       int32_t *draft_len, int32_t *match_pos, int32_t *match_n) {
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t *c = ctx + (int64_t)b * stride;
+        const int32_t n = len[b];
+        int32_t pos = -1, gfound = 0;
+        for (int32_t g = n_max; g >= n_min && pos < 0; --g) {
+            if (g < 1 || g >= n) continue;
+            for (int32_t p = n - g - 1; p >= 0; --p) {
+                int32_t same = 1;
+                for (int32_t q = 0; q < g; ++q)
+                    if (c[p + q] != c[n - g + q]) {
+                        same = 0;
+                        break;
+                    }
+                if (same) {
+                    pos = p;
+                    gfound = g;
+                    break;
+                }
+            }
+        }
+        int32_t dl = 0;
+        if (pos >= 0) {
+            dl = n - (pos + gfound);
+            if (dl > K) dl = K;
+        }
+        for (int32_t k = 0; k < K; ++k) draft[(int64_t)b * K + k] = k < dl ? c[pos + gfound + k] : -1;
+        draft_len[b] = dl;
+        if (match_pos) match_pos[b] = pos;
+        if (match_n) match_n[b] = gfound;
+    }
+}

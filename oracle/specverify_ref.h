@@ -113,6 +113,37 @@ double ref_av_loss(const double *feat, const int32_t *accepted_len, const int32_
 void ref_av_update(const double *feat, const int32_t *accepted_len, const int32_t *kept_len,
                    int32_t B, int32_t K, double lr, double *omega_beta);
 
+/* IRLS refit ([AV] "Ajuste de los Coeficientes").  Accumulate one step's
+ * labels into g [K+1], H [(K+1)*(K+1)] (dense, row-major) and cnt [K+1] at
+ * the current coefficients; solve at the round's end: H dtheta = -g over the
+ * coefficients with labels (Cholesky; a pivot <= 1e-12 x the largest
+ * diagonal entry holds omega and solves the intercepts alone), damped by
+ * cnt/(cnt + c_damp) per coefficient.  The solve zeroes g, H and cnt.
+ * Returns bit 0 = coefficients updated, bit 1 = slope held. */
+void ref_irls_accumulate(const double *feat, const int32_t *accepted_len, const int32_t *kept_len,
+                         int32_t B, int32_t K, const double *omega_beta, double *g, double *H,
+                         int64_t *cnt);
+int ref_irls_solve(int32_t K, double c_damp, double *g, double *H, int64_t *cnt,
+                   double *omega_beta);
+
+/* Scorer diagnostics over one batch's labels: out = {AUC, mean log-loss,
+ * ECE over nbins equal-width bins of s, number of labels}. */
+void ref_av_diagnostics(const double *feat, const int32_t *accepted_len, const int32_t *kept_len,
+                        int32_t B, int32_t K, const double *omega_beta, int32_t nbins,
+                        double *out, int32_t *near);
+
+/* Budgeted trimming: returns the budget (number of kept drafts) and fills
+ * kept_len [B] and mask [B*K] (nullable).  conf: float [B][K]; cost: [B*K+1]
+ * (cost of verifying a budget of k drafts). */
+int64_t ref_av_budget(const float *conf, int32_t B, int32_t K, const double *cost,
+                      double n_requests, int32_t *kept_len, uint8_t *mask, double *best_ratio,
+                      int32_t *near);
+
+/* Prompt-lookup drafting over contexts ctx [B][stride] of lengths len [B]. */
+void ref_ngram_propose(const int32_t *ctx, const int32_t *len, int32_t B, int64_t stride,
+                       int32_t n_min, int32_t n_max, int32_t K, int32_t *draft,
+                       int32_t *draft_len, int32_t *match_pos, int32_t *match_n);
+
 #ifdef __cplusplus
 }
 #endif
