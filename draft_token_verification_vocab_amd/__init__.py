@@ -63,6 +63,20 @@ _SIGNATURES = {
                                         ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P, _P]),
     "spec_read_probe": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                          _P, _P]),
+    "spec_irls_state_bytes": (ctypes.c_size_t, [ctypes.c_int32]),
+    "spec_irls_reset": (ctypes.c_int32, [_P, ctypes.c_int32, _P]),
+    "spec_irls_accumulate": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                              _P]),
+    "spec_irls_solve": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_double, _P, _P, _P]),
+    "spec_av_diagnostics_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32,
+                                                              ctypes.c_int32]),
+    "spec_av_diagnostics": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P,
+                                             ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
+    "spec_av_budget": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_double,
+                                        _P, _P, _P, _P, _P]),
+    "spec_ngram_propose": (ctypes.c_int32, [_P, _P, ctypes.c_int32, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                            _P, _P, _P]),
     "spec_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 
@@ -287,3 +301,92 @@ def read_probe(logits: torch.Tensor, *, row_bytes: Optional[int] = None,
     _check(load().spec_read_probe(_ptr(x), rows, rb, stride_b, _ptr(sink), _stream(x.device)),
            "spec_read_probe")
     return sink
+
+
+def irls_state(K: int, device) -> torch.Tensor:
+    """A zeroed Newton-refit state for K draft positions (float64 device tensor)."""
+    n = load().spec_irls_state_bytes(int(K))
+    if n == 0:
+        raise SpecVerifyError("spec_irls_state_bytes: unsupported num_draft %d" % K)
+    st = torch.empty(n // 8, dtype=torch.float64, device=device)
+    _check(load().spec_irls_reset(_ptr(st), int(K), _stream(st.device)), "spec_irls_reset")
+    return st
+
+
+def irls_accumulate(state: torch.Tensor, draft_stats: torch.Tensor, accepted_len: torch.Tensor,
+                    kept_len: Optional[torch.Tensor], omega_beta: torch.Tensor, B: int,
+                    K: int) -> torch.Tensor:
+    """Add one step's labels to the round's gradient and Hessian."""
+    for t, n in ((state, "state"), (draft_stats, "draft_stats"), (accepted_len, "accepted_len"),
+                 (omega_beta, "omega_beta")):
+        _need_cuda(t, n)
+    _check(load().spec_irls_accumulate(_ptr(draft_stats), _ptr(accepted_len), _ptr(kept_len),
+                                       int(B), int(K), _ptr(omega_beta), _ptr(state),
+                                       _stream(state.device)), "spec_irls_accumulate")
+    return state
+
+
+def irls_solve(state: torch.Tensor, omega_beta: torch.Tensor, K: int, c_damp: float,
+               flags: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Solve the round's Newton system, update omega_beta in place, zero the state."""
+    _need_cuda(state, "state")
+    _need_cuda(omega_beta, "omega_beta")
+    _check(load().spec_irls_solve(_ptr(state), int(K), float(c_damp), _ptr(omega_beta),
+                                  _ptr(flags), _stream(state.device)), "spec_irls_solve")
+    return omega_beta
+
+
+def av_diagnostics(draft_stats: torch.Tensor, accepted_len: torch.Tensor,
+                   kept_len: Optional[torch.Tensor], omega_beta: torch.Tensor, B: int, K: int,
+                   nbins: int = 10, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """AUC, mean log-loss, ECE and label count of the estimator on one batch
+    (float64 device tensor of 4)."""
+    dev = draft_stats.device
+    if out is None:
+        out = torch.empty(4, dtype=torch.float64, device=dev)
+    n = load().spec_av_diagnostics_workspace_bytes(int(B), int(K), int(nbins))
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    _check(load().spec_av_diagnostics(_ptr(draft_stats), _ptr(accepted_len), _ptr(kept_len),
+                                      int(B), int(K), _ptr(omega_beta), int(nbins), _ptr(out),
+                                      _ptr(workspace), workspace.numel(), _stream(dev)),
+           "spec_av_diagnostics")
+    return out
+
+
+def av_budget(conf: torch.Tensor, cost: torch.Tensor, n_requests: Optional[float] = None,
+              mask: bool = True) -> dict:
+    """Budgeted trimming of a [B, K] confidence tensor against a float64 cost
+    table of B*K+1 entries: kept_len [B], keep mask, budget and best ratio."""
+    _need_cuda(conf, "conf")
+    _need_cuda(cost, "cost")
+    B, K = conf.shape
+    dev = conf.device
+    res = {"kept_len": torch.empty(B, dtype=torch.int32, device=dev),
+           "mask": torch.empty(B, K, dtype=torch.uint8, device=dev) if mask else None,
+           "budget": torch.empty(1, dtype=torch.int64, device=dev),
+           "best_ratio": torch.empty(1, dtype=torch.float64, device=dev)}
+    nr = float(B if n_requests is None else n_requests)
+    _check(load().spec_av_budget(_ptr(conf), int(B), int(K), _ptr(cost), nr,
+                                 _ptr(res["kept_len"]), _ptr(res["mask"]), _ptr(res["budget"]),
+                                 _ptr(res["best_ratio"]), _stream(dev)), "spec_av_budget")
+    return res
+
+
+def ngram_propose(context: torch.Tensor, lengths: torch.Tensor, n_min: int, n_max: int,
+                  K: int) -> dict:
+    """Prompt-lookup drafts for int32 contexts [B, S] of the given lengths."""
+    _need_cuda(context, "context")
+    _need_cuda(lengths, "lengths")
+    B, S = context.shape
+    dev = context.device
+    res = {"draft": torch.empty(B, K, dtype=torch.int32, device=dev),
+           "draft_len": torch.empty(B, dtype=torch.int32, device=dev),
+           "match_pos": torch.empty(B, dtype=torch.int32, device=dev),
+           "match_n": torch.empty(B, dtype=torch.int32, device=dev)}
+    _check(load().spec_ngram_propose(_ptr(context), _ptr(lengths), int(B), int(S), int(n_min),
+                                     int(n_max), int(K), _ptr(res["draft"]),
+                                     _ptr(res["draft_len"]), _ptr(res["match_pos"]),
+                                     _ptr(res["match_n"]), _stream(dev)), "spec_ngram_propose")
+    return res

@@ -11,6 +11,7 @@
 #include "sv_av.hpp"
 #include "sv_common.hpp"
 #include "sv_finish.hpp"
+#include "sv_next.hpp"
 #include "sv_rowstats.hpp"
 
 namespace {
@@ -37,6 +38,14 @@ constexpr int kMaxSegs = 64;
 constexpr int kSmallBlock = 64;
 // FLy resolver: one wave per sequence.
 constexpr int kFlyBlock = 256;
+// Label reductions (SGD step, Newton accumulation): a wave per position.
+constexpr int kLabelBlock = 512;
+// Diagnostics: labels per call, bins, label-kernel workgroup.
+constexpr int64_t kDiagMaxLabels = 1 << 16;
+constexpr int kDiagMaxBins = 64;
+constexpr int kDiagLabelBlock = 1024;
+// Prompt lookup: one workgroup per sequence.
+constexpr int kNgramBlock = 256;
 
 size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -342,8 +351,144 @@ spec_status spec_av_update(const void *draft_stats, const int32_t *accepted_len,
         return SPEC_ERR_ARG;
     const size_t n = static_cast<size_t>(batch) * num_draft;
     DraftStats ds = draft_stats_view(const_cast<void *>(draft_stats), n);
-    av_update_kernel<256><<<dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+    av_sgd_kernel<kLabelBlock><<<dim3(1), dim3(kLabelBlock), 0, static_cast<hipStream_t>(stream)>>>(
         ds.feat, accepted_len, kept_len, batch, num_draft, lr, omega_beta);
+    return launch_status();
+}
+
+size_t spec_irls_state_bytes(int32_t num_draft) {
+    if (num_draft < 1 || num_draft > 64) return 0;
+    return sizeof(double) * static_cast<size_t>(irls_state_doubles(num_draft));
+}
+
+spec_status spec_irls_reset(void *state, int32_t num_draft, void *stream) {
+    if (num_draft < 1) return SPEC_ERR_ARG;
+    if (num_draft > 64) return SPEC_ERR_UNSUPPORTED;
+    if (!state || (reinterpret_cast<uintptr_t>(state) & 7u)) return SPEC_ERR_ARG;
+    const int nd = irls_state_doubles(num_draft);
+    fill_f64_kernel<<<dim3((nd + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<double *>(state), nd, 0.0);
+    return launch_status();
+}
+
+spec_status spec_irls_accumulate(const void *draft_stats, const int32_t *accepted_len,
+                                 const int32_t *kept_len, int32_t batch, int32_t num_draft,
+                                 const float *omega_beta, void *state, void *stream) {
+    if (batch < 0 || num_draft < 1) return SPEC_ERR_ARG;
+    if (num_draft > 64) return SPEC_ERR_UNSUPPORTED;
+    if (batch == 0) return SPEC_OK;
+    if (!draft_stats || !aligned16(draft_stats) || !accepted_len || !omega_beta || !state ||
+        (reinterpret_cast<uintptr_t>(state) & 7u))
+        return SPEC_ERR_ARG;
+    const size_t n = static_cast<size_t>(batch) * num_draft;
+    DraftStats ds = draft_stats_view(const_cast<void *>(draft_stats), n);
+    irls_accumulate_kernel<kLabelBlock>
+        <<<dim3(1), dim3(kLabelBlock), 0, static_cast<hipStream_t>(stream)>>>(
+            ds.feat, accepted_len, kept_len, batch, num_draft, omega_beta,
+            static_cast<double *>(state));
+    return launch_status();
+}
+
+spec_status spec_irls_solve(void *state, int32_t num_draft, double c_damp, float *omega_beta,
+                            int32_t *flags, void *stream) {
+    if (num_draft < 1) return SPEC_ERR_ARG;
+    if (num_draft > 64) return SPEC_ERR_UNSUPPORTED;
+    if (!(c_damp >= 0.0) || !std::isfinite(c_damp)) return SPEC_ERR_ARG;
+    if (!state || (reinterpret_cast<uintptr_t>(state) & 7u) || !omega_beta) return SPEC_ERR_ARG;
+    irls_solve_kernel<<<dim3(1), dim3(kWave), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<double *>(state), num_draft, c_damp, omega_beta, flags);
+    return launch_status();
+}
+
+namespace {
+struct DiagLayout {
+    size_t z, y, ctr, pairs, total;
+    int tiles;
+};
+DiagLayout diag_layout(int32_t B, int32_t K, int32_t nbins) {
+    DiagLayout l{};
+    const size_t M = static_cast<size_t>(B) * K;
+    l.tiles = static_cast<int>((M + kDiagTile - 1) / kDiagTile);
+    l.z = 0;
+    l.y = align_up(l.z + 8 * M);
+    l.ctr = align_up(l.y + M);
+    l.pairs = align_up(l.ctr + 8 * static_cast<size_t>(3 + nbins));
+    l.total = align_up(l.pairs + 8 * static_cast<size_t>(l.tiles) * l.tiles);
+    return l;
+}
+}  // namespace
+
+size_t spec_av_diagnostics_workspace_bytes(int32_t batch, int32_t num_draft, int32_t nbins) {
+    if (batch < 1 || num_draft < 1 || num_draft > 64 || nbins < 1 || nbins > kDiagMaxBins ||
+        static_cast<int64_t>(batch) * num_draft > kDiagMaxLabels)
+        return 0;
+    return diag_layout(batch, num_draft, nbins).total;
+}
+
+spec_status spec_av_diagnostics(const void *draft_stats, const int32_t *accepted_len,
+                                const int32_t *kept_len, int32_t batch, int32_t num_draft,
+                                const float *omega_beta, int32_t nbins, double *out,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    if (batch < 1 || num_draft < 1 || nbins < 1) return SPEC_ERR_ARG;
+    if (num_draft > 64 || nbins > kDiagMaxBins ||
+        static_cast<int64_t>(batch) * num_draft > kDiagMaxLabels)
+        return SPEC_ERR_UNSUPPORTED;
+    if (!draft_stats || !aligned16(draft_stats) || !accepted_len || !omega_beta || !out ||
+        (reinterpret_cast<uintptr_t>(out) & 7u))
+        return SPEC_ERR_ARG;
+    const DiagLayout l = diag_layout(batch, num_draft, nbins);
+    if (!workspace || workspace_bytes < l.total) return SPEC_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SPEC_ERR_ARG;
+    char *w = static_cast<char *>(workspace);
+    DiagWs ws{reinterpret_cast<double *>(w + l.z), reinterpret_cast<int8_t *>(w + l.y),
+              reinterpret_cast<unsigned long long *>(w + l.ctr),
+              reinterpret_cast<unsigned long long *>(w + l.pairs)};
+    const size_t n = static_cast<size_t>(batch) * num_draft;
+    DraftStats ds = draft_stats_view(const_cast<void *>(draft_stats), n);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    diag_labels_kernel<kDiagLabelBlock><<<dim3(1), dim3(kDiagLabelBlock), 0, st>>>(
+        ds.feat, accepted_len, kept_len, batch, num_draft, omega_beta, nbins, ws);
+    diag_pairs_kernel<<<dim3(l.tiles * l.tiles), dim3(kDiagTile), 0, st>>>(
+        ws, static_cast<int>(n), l.tiles);
+    diag_finish_kernel<<<dim3(1), dim3(kWave), 0, st>>>(ws, nbins, l.tiles * l.tiles, out);
+    return launch_status();
+}
+
+spec_status spec_av_budget(const float *conf, int32_t batch, int32_t num_draft, const double *cost,
+                           double n_requests, int32_t *kept_len, uint8_t *keep_mask,
+                           int64_t *budget, double *best_ratio, void *stream) {
+    if (batch < 1 || num_draft < 1 || !std::isfinite(n_requests)) return SPEC_ERR_ARG;
+    const int64_t M = static_cast<int64_t>(batch) * num_draft;
+    if (M > kBudgetMax) return SPEC_ERR_UNSUPPORTED;
+    if (!conf || !cost || !kept_len || !budget || (reinterpret_cast<uintptr_t>(cost) & 7u) ||
+        (reinterpret_cast<uintptr_t>(budget) & 7u) ||
+        (best_ratio && (reinterpret_cast<uintptr_t>(best_ratio) & 7u)))
+        return SPEC_ERR_ARG;
+    int P = 1;
+    while (P < M) P <<= 1;
+    const size_t lds = 8 * static_cast<size_t>(P) + static_cast<size_t>(M);
+    int dev = 0, max_lds = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess)
+        return SPEC_ERR_HIP;
+    if (lds + 1024 > static_cast<size_t>(max_lds)) return SPEC_ERR_UNSUPPORTED;
+    budget_kernel<kBudgetThreads>
+        <<<dim3(1), dim3(kBudgetThreads), lds, static_cast<hipStream_t>(stream)>>>(
+            conf, batch, num_draft, cost, n_requests, kept_len, keep_mask, budget, best_ratio);
+    return launch_status();
+}
+
+spec_status spec_ngram_propose(const int32_t *context, const int32_t *lengths, int32_t batch,
+                               int64_t stride, int32_t n_min, int32_t n_max, int32_t num_draft,
+                               int32_t *draft, int32_t *draft_len, int32_t *match_pos,
+                               int32_t *match_n, void *stream) {
+    if (batch < 0 || stride < 1 || n_min < 1 || n_max < n_min || num_draft < 1) return SPEC_ERR_ARG;
+    if (n_max > kNgramMax || stride > INT32_MAX || num_draft > 64) return SPEC_ERR_UNSUPPORTED;
+    if (batch == 0) return SPEC_OK;
+    if (!context || !lengths || !draft || !draft_len) return SPEC_ERR_ARG;
+    ngram_kernel<kNgramBlock><<<dim3(batch), dim3(kNgramBlock), 0, static_cast<hipStream_t>(stream)>>>(
+        context, lengths, stride, n_min, n_max, num_draft, draft, draft_len, match_pos, match_n);
     return launch_status();
 }
 

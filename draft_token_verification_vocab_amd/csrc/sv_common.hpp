@@ -187,6 +187,13 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return lane63_u64(v);
 }
 
+// Maximum of a non-negative double over the wave (such doubles order like
+// their bit patterns).
+__device__ __forceinline__ double wave_max_f64_nonneg(double x) {
+    return __longlong_as_double(static_cast<long long>(
+        wave_max_u64(static_cast<uint64_t>(__double_as_longlong(x)))));
+}
+
 // Sum of a double over the wave, in a fixed order.
 __device__ __forceinline__ double wave_sum_f64(double x) {
     uint64_t v = static_cast<uint64_t>(__double_as_longlong(x));

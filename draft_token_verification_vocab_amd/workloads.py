@@ -164,3 +164,32 @@ def av_init(cfg: int, K: Optional[int] = None) -> list:
     a = CONFIGS[cfg]["av"]
     K = K or CONFIGS[cfg]["K"]
     return [a["omega"]] + [a["beta0"] + a["beta_step"] * i for i in range(K)]
+
+
+def budget_costs(B: int, K: int, per_request: float = 0.01, per_draft: float = 0.002,
+                 curve: float = 2.0):
+    """Synthetic cost table (ms) of verifying a budget of k = 0..B*K drafts
+    in one step, standing in for the measured draft + verify cost tables of
+    budgeted trimming: a per-request base, a per-draft slope and a quadratic
+    term that reaches `curve` ms at k = B*K.  float64 numpy array."""
+    import numpy as np
+    M = B * K
+    k = np.arange(M + 1, dtype=np.float64)
+    return per_request * B + per_draft * k + curve * (k / max(M, 1)) ** 2
+
+
+def ngram_contexts(B: int, S: int, vocab: int, seed: int = 0, repeat_every: int = 3,
+                   device="cpu"):
+    """Synthetic token contexts for prompt-lookup drafting: uniform token ids
+    over `vocab`, lengths uniform in [S/2, S], and in every `repeat_every`-th
+    sequence a span of 2..11 tokens from the first half copied to the end (the
+    repetition prompt lookup exploits).  Returns (int32 [B, S], int32 [B])."""
+    g = generator(seed, "cpu")
+    ctx = torch.randint(0, vocab, (B, S), generator=g, dtype=torch.int32)
+    lens = torch.randint(S // 2, S + 1, (B,), generator=g, dtype=torch.int32)
+    for b in range(0, B, repeat_every):
+        n = int(lens[b])
+        src = int(torch.randint(0, n // 2, (1,), generator=g))
+        span = int(torch.randint(2, 12, (1,), generator=g))
+        ctx[b, n - span:n] = ctx[b, src:src + span].clone()
+    return ctx.to(device), lens.to(device)

@@ -174,11 +174,103 @@ spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,
  * N = 0 leaves the parameters unchanged.  draft_stats: filled by
  * spec_av_score; accepted_len: from spec_verify; kept_len: device int32 [B]
  * or NULL (= K); omega_beta: device float[K+1], updated in place.  Single
- * workgroup, fixed-order double-precision reduction.
+ * workgroup (a wave per position), fixed-order double-precision sums.
  */
 spec_status spec_av_update(const void *draft_stats, const int32_t *accepted_len,
                            const int32_t *kept_len, int32_t batch, int32_t num_draft, float lr,
                            float *omega_beta, void *stream);
+
+/*
+ * Newton (IRLS) refit of the estimator ([AV] section "Ajuste de los
+ * Coeficientes").  The pages refit omega and the beta_i after every round of
+ * N decoding steps: each step adds its labelled drafts (the same labels as
+ * spec_av_update) to the gradient g and Hessian H of the summed log-loss at
+ * the current coefficients; the last step of the round solves H dtheta = -g
+ * and moves each coefficient by dtheta scaled by n / (n + c_damp), n being
+ * the labels behind it (all labels for omega, the labels at position i for
+ * beta_i).
+ *
+ * With one shared slope, H has nonzeros only at H[0][0], H[0][1+i] and the
+ * diagonal, so the state is 4K+3 doubles (spec_irls_state_bytes): device
+ * memory, 8-byte aligned, owned by the caller, zero at the start of a round
+ * (spec_irls_reset zeroes it; spec_irls_solve leaves it zeroed).
+ *
+ * spec_irls_accumulate: draft_stats from spec_av_score, accepted_len from
+ *   spec_verify, kept_len device int32 [B] or NULL (= K), omega_beta device
+ *   float [K+1] (read only).  One workgroup; fixed-order sums (deterministic).
+ * spec_irls_solve: solves over the coefficients that have labels; when the
+ *   slope has no curvature of its own left (Schur complement
+ *   <= 1e-12 x the largest diagonal entry, e.g. every feature equal) the
+ *   slope is held and each intercept takes its own Newton step.  omega_beta
+ *   (device float [K+1]) is updated in place; flags (device int32, nullable)
+ *   receives bit 0 = updated, bit 1 = slope held.  c_damp >= 0.
+ */
+size_t spec_irls_state_bytes(int32_t num_draft);
+spec_status spec_irls_reset(void *state, int32_t num_draft, void *stream);
+spec_status spec_irls_accumulate(const void *draft_stats, const int32_t *accepted_len,
+                                 const int32_t *kept_len, int32_t batch, int32_t num_draft,
+                                 const float *omega_beta, void *state, void *stream);
+spec_status spec_irls_solve(void *state, int32_t num_draft, double c_damp, float *omega_beta,
+                            int32_t *flags, void *stream);
+
+/*
+ * spec_av_diagnostics -- the estimator's quality over one batch's labels
+ * ([AV] section "Otras Caracteristicas Consideradas": AUC, log-loss, ECE).
+ * With z = omega*feat + beta_i (double; feat from draft_stats) and
+ * s = sigmoid(z) over the labelled drafts:
+ *   out[0] AUC: over every (accepted, rejected) pair, the share where the
+ *          accepted draft's z is larger, ties counting one half (NaN without
+ *          both classes);
+ *   out[1] mean log-loss; out[2] ECE over nbins equal-width bins of s;
+ *   out[3] the number of labels.
+ * out: device double[4].  workspace: device, spec_av_diagnostics_workspace_bytes,
+ * 16-byte aligned.  Log-loss and bin sums are accumulated in fixed point
+ * (2^-32 and 2^-40 per label), so the result does not depend on the order of
+ * the additions.  B*K <= 65536, nbins <= 64, else SPEC_ERR_UNSUPPORTED.
+ */
+size_t spec_av_diagnostics_workspace_bytes(int32_t batch, int32_t num_draft, int32_t nbins);
+spec_status spec_av_diagnostics(const void *draft_stats, const int32_t *accepted_len,
+                                const int32_t *kept_len, int32_t batch, int32_t num_draft,
+                                const float *omega_beta, int32_t nbins, double *out,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * spec_av_budget -- budgeted trimming ([AV] section "Otras Caracteristicas
+ * Consideradas", the survival / top-k and draft-budget snippets).
+ *   survival(b, i) = conf(b,0) * ... * conf(b,i), formed in float;
+ *   the B*K survivals in decreasing order (ties: lower flat index b*K+i
+ *   first) are s_(1) >= s_(2) >= ...;
+ *   est(k) = n_requests + s_(1) + ... + s_(k),  k = 0..B*K;
+ *   budget = the first k maximising est(k) / cost[k];
+ *   the first `budget` drafts of that order are kept (a prefix of each
+ *   sequence, as survival never grows along a sequence).
+ * conf: device float [B][K] (spec_av_score's conf); cost: device double
+ * [B*K+1], 8-byte aligned (the measured cost of verifying k drafts).
+ * Outputs: kept_len device int32 [B]; keep_mask device uint8 [B][K] or NULL;
+ * budget device int64 (8-byte aligned); best_ratio device double or NULL.
+ * One workgroup sorts the survivals in LDS: B*K <= 16384 and within the
+ * device's per-workgroup LDS, else SPEC_ERR_UNSUPPORTED.
+ */
+spec_status spec_av_budget(const float *conf, int32_t batch, int32_t num_draft, const double *cost,
+                           double n_requests, int32_t *kept_len, uint8_t *keep_mask,
+                           int64_t *budget, double *best_ratio, void *stream);
+
+/*
+ * spec_ngram_propose -- prompt-lookup drafting ([SD] section "N-gram (prompt
+ * lookup)"; [FLy] section "B. Aceleracao Multinivel"): for each sequence,
+ * the longest suffix n-gram of its context (n from n_max down to n_min) that
+ * also occurs earlier; of its earlier occurrences the latest; the draft is
+ * the up to num_draft tokens that followed it.
+ * context: device int32 [B][stride]; lengths: device int32 [B] (clamped to
+ * [0, stride]).  Outputs (device int32): draft [B][num_draft] (-1 after
+ * draft_len), draft_len [B], match_pos [B] (start of the matched occurrence,
+ * -1 when none; nullable), match_n [B] (its length, 0 when none; nullable).
+ * 1 <= n_min <= n_max <= 32, num_draft <= 64.
+ */
+spec_status spec_ngram_propose(const int32_t *context, const int32_t *lengths, int32_t batch,
+                               int64_t stride, int32_t n_min, int32_t n_max, int32_t num_draft,
+                               int32_t *draft, int32_t *draft_len, int32_t *match_pos,
+                               int32_t *match_n, void *stream);
 
 /*
  * spec_row_stats -- the streaming row pass on its own: per row of V logits,

@@ -41,7 +41,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_av_score", "spec_av_update", "spec_row_stats",
               "spec_workspace_bytes", "spec_draft_stats_bytes", "spec_status_string",
-              "spec_read_probe"):
+              "spec_read_probe", "spec_irls_state_bytes", "spec_irls_reset",
+              "spec_irls_accumulate", "spec_irls_solve", "spec_av_diagnostics",
+              "spec_av_diagnostics_workspace_bytes", "spec_av_budget", "spec_ngram_propose"):
         assert n in names
 
 
@@ -142,3 +144,40 @@ def test_other_entry_points_validate(L):
     assert L.spec_read_probe(None, 0, 32, 32, None, None) == 0
     for s in (0, -1, -2, -3, -4, 99):
         assert isinstance(L.spec_status_string(s), bytes)
+
+
+def test_next_rows_sizes(L):
+    assert L.spec_irls_state_bytes(8) == 8 * (4 * 8 + 3)
+    assert L.spec_irls_state_bytes(0) == 0 and L.spec_irls_state_bytes(65) == 0
+    assert L.spec_av_diagnostics_workspace_bytes(1024, 8, 10) > 8 * 8192
+    assert L.spec_av_diagnostics_workspace_bytes(1024, 8, 65) == 0
+    assert L.spec_av_diagnostics_workspace_bytes(8192, 16, 10) == 0  # > 65536 labels
+
+
+@host_only
+def test_next_rows_validate_on_host(L):
+    P = ctypes.c_void_p
+    a = P(16)
+    assert L.spec_irls_reset(a, 0, None) == -1
+    assert L.spec_irls_reset(a, 65, None) == -2
+    assert L.spec_irls_reset(P(12), 4, None) == -1              # not 8-byte aligned
+    assert L.spec_irls_accumulate(a, a, None, 4, 65, a, a, None) == -2
+    assert L.spec_irls_accumulate(a, None, None, 4, 4, a, a, None) == -1
+    assert L.spec_irls_accumulate(None, None, None, 0, 4, None, None, None) == 0
+    assert L.spec_irls_solve(a, 4, -1.0, a, None, None) == -1
+    assert L.spec_irls_solve(a, 4, float("inf"), a, None, None) == -1
+    assert L.spec_irls_solve(a, 4, 1.0, None, None, None) == -1
+    assert L.spec_av_diagnostics(a, a, None, 4, 4, a, 0, a, a, 1 << 20, None) == -1
+    assert L.spec_av_diagnostics(a, a, None, 4, 4, a, 65, a, a, 1 << 20, None) == -2
+    assert L.spec_av_diagnostics(a, a, None, 4, 4, a, 10, a, a, 16, None) == -3
+    assert L.spec_av_diagnostics(a, a, None, 4, 4, a, 10, a, None, 1 << 20, None) == -3
+    assert L.spec_av_budget(a, 2049, 8, a, 1.0, a, None, a, None, None) == -2
+    assert L.spec_av_budget(a, 4, 4, P(12), 1.0, a, None, a, None, None) == -1
+    assert L.spec_av_budget(a, 4, 4, a, float("nan"), a, None, a, None, None) == -1
+    assert L.spec_av_budget(a, 0, 4, a, 1.0, a, None, a, None, None) == -1
+    assert L.spec_ngram_propose(a, a, 4, 100, 0, 3, 4, a, a, None, None, None) == -1
+    assert L.spec_ngram_propose(a, a, 4, 100, 3, 2, 4, a, a, None, None, None) == -1
+    assert L.spec_ngram_propose(a, a, 4, 100, 1, 33, 4, a, a, None, None, None) == -2
+    assert L.spec_ngram_propose(a, a, 4, 100, 1, 3, 65, a, a, None, None, None) == -2
+    assert L.spec_ngram_propose(a, None, 4, 100, 1, 3, 4, a, a, None, None, None) == -1
+    assert L.spec_ngram_propose(None, None, 0, 100, 1, 3, 4, None, None, None, None, None) == 0

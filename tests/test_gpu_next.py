@@ -1,0 +1,245 @@
+"""GPU parity of the Newton refit, the estimator diagnostics, budgeted
+trimming and prompt-lookup drafting: the HIP library through its C ABI
+against the CPU oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_vocab_amd as sv
+from draft_token_verification_vocab_amd import workloads as W
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the GPU tests need an MI355X"
+    sv.load()
+    ref.lib()
+
+
+def np_(t):
+    return t.detach().cpu().numpy()
+
+
+def _label_batch(rng, B, K, feat_const=None):
+    """Draft features (float32, as the row pass stores them), accepted and
+    kept lengths; accepted never exceeds kept."""
+    feat = rng.normal(-1.2, 1.3, (B, K)).astype(np.float32)
+    if feat_const is not None:
+        feat[:] = feat_const
+    kept = rng.integers(0, K + 1, B).astype(np.int32)
+    acc = np.minimum(rng.geometric(0.45, B) - 1, K).astype(np.int32)
+    acc = np.minimum(acc, kept)
+    return feat, acc, kept
+
+
+def _device_stats(feat):
+    B, K = feat.shape
+    ds = torch.zeros(24 * B * K, dtype=torch.uint8, device=DEV)
+    sv.draft_stats_view(ds, B, K)["feat"].copy_(torch.from_numpy(feat.ravel()))
+    return ds
+
+
+def _to_dev(*arrs):
+    return [torch.from_numpy(np.ascontiguousarray(a)).to(DEV) for a in arrs]
+
+
+# ---------------------------------------------------------------------------
+# Newton refit
+# ---------------------------------------------------------------------------
+def _arrow(H):
+    K = H.shape[0] - 1
+    return np.r_[H[0, 0], H[0, 1:], np.diag(H)[1:]]
+
+
+@pytest.mark.parametrize("B,K", [(1024, 8), (37, 5), (200, 64), (3, 1)])
+def test_irls_round_parity(B, K):
+    rng = np.random.default_rng(B + K)
+    ob_host = np.r_[1.0, 0.5 - 0.3 * np.arange(K)].astype(np.float32)
+    ob = torch.from_numpy(ob_host.copy()).to(DEV)
+    st = sv.irls_state(K, DEV)
+    ost = ref.IrlsState(K)
+    for step in range(3):  # one round of three decoding steps
+        feat, acc, kept = _label_batch(rng, B, K)
+        ds = _device_stats(feat)
+        a_d, k_d = _to_dev(acc, kept)
+        sv.irls_accumulate(st, ds, a_d, k_d, ob, B, K)
+        ref.irls_accumulate(ost, feat.astype(np.float64), acc, kept, ob_host.astype(np.float64))
+    torch.cuda.synchronize()
+    s = np_(st)
+    assert np.allclose(s[:K + 1], ost.g, rtol=1e-12, atol=1e-9)
+    assert np.allclose(s[K + 1:3 * K + 2], _arrow(ost.H), rtol=1e-12, atol=1e-9)
+    assert np.array_equal(s[3 * K + 2:], ost.cnt.astype(np.float64))
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sv.irls_solve(st, ob, K, 20.0, flags)
+    torch.cuda.synchronize()
+    want, oflags = ref.irls_solve(ost, ob_host.astype(np.float64), 20.0)
+    assert int(np_(flags)[0]) == oflags
+    assert np.allclose(np_(ob), want, rtol=2 ** -22, atol=1e-7), (np_(ob), want)
+    assert not np_(st).any()  # the solve leaves the next round a zero state
+
+
+def test_irls_slope_held_and_unlabelled_positions():
+    rng = np.random.default_rng(7)
+    B, K = 300, 4
+    feat, acc, kept = _label_batch(rng, B, K, feat_const=0.7)
+    kept = np.minimum(kept, 2)  # positions 2 and 3 never carry a label
+    acc = np.minimum(acc, kept)
+    ob_host = np.array([1.0, 0.2, -0.1, -0.5, -0.8], dtype=np.float32)
+    ob = torch.from_numpy(ob_host.copy()).to(DEV)
+    st = sv.irls_state(K, DEV)
+    a_d, k_d = _to_dev(acc, kept)
+    sv.irls_accumulate(st, _device_stats(feat), a_d, k_d, ob, B, K)
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sv.irls_solve(st, ob, K, 0.0, flags)
+    torch.cuda.synchronize()
+    ost = ref.IrlsState(K)
+    ref.irls_accumulate(ost, feat.astype(np.float64), acc, kept, ob_host.astype(np.float64))
+    want, oflags = ref.irls_solve(ost, ob_host.astype(np.float64), 0.0)
+    assert oflags == 3 and int(np_(flags)[0]) == 3
+    got = np_(ob)
+    assert got[0] == ob_host[0] and got[3] == ob_host[3] and got[4] == ob_host[4]
+    assert np.allclose(got, want, rtol=2 ** -22, atol=1e-7)
+
+
+def test_irls_no_labels_is_a_noop():
+    K = 3
+    ob_host = np.array([0.5, 0.1, 0.2, 0.3], dtype=np.float32)
+    ob = torch.from_numpy(ob_host.copy()).to(DEV)
+    st = sv.irls_state(K, DEV)
+    feat = np.zeros((10, K), dtype=np.float32)
+    a_d, k_d = _to_dev(np.zeros(10, dtype=np.int32), np.zeros(10, dtype=np.int32))
+    sv.irls_accumulate(st, _device_stats(feat), a_d, k_d, ob, 10, K)
+    flags = torch.full((1,), 9, dtype=torch.int32, device=DEV)
+    sv.irls_solve(st, ob, K, 1.0, flags)
+    torch.cuda.synchronize()
+    assert int(np_(flags)[0]) == 0 and np.array_equal(np_(ob), ob_host)
+
+
+def test_irls_on_the_pipeline_features():
+    # features from real draft rows (the AV pipeline recipe at a small batch)
+    batch = W.make(4, B=48, V=5000, stride=5000)
+    K = batch.tokens.shape[1]
+    ob = torch.tensor(W.av_init(4), dtype=torch.float32, device=DEV)
+    d, t, tok = batch.draft.to(DEV), batch.target.to(DEV), batch.tokens.to(DEV)
+    conf, mask, kept, ds = sv.av_score(d, tok, ob, 0.2, vocab=batch.V)
+    r = sv.verify(t, d, tok, seed=3, vocab=batch.V, kept_len=kept, draft_stats=ds)
+    st = sv.irls_state(K, DEV)
+    sv.irls_accumulate(st, ds, r.accepted_len, kept, ob, 48, K)
+    torch.cuda.synchronize()
+    feat = np_(sv.draft_stats_view(ds, 48, K)["feat"]).reshape(48, K).astype(np.float64)
+    ost = ref.IrlsState(K)
+    ref.irls_accumulate(ost, feat, np_(r.accepted_len), np_(kept), np_(ob).astype(np.float64))
+    s = np_(st)
+    assert np.allclose(s[:K + 1], ost.g, rtol=1e-12, atol=1e-9)
+    assert np.allclose(s[K + 1:3 * K + 2], _arrow(ost.H), rtol=1e-12, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# Diagnostics
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,K,nbins", [(1024, 8, 10), (129, 3, 7), (5, 2, 1), (4096, 16, 64)])
+def test_diagnostics_parity(B, K, nbins):
+    rng = np.random.default_rng(B * K + nbins)
+    feat, acc, kept = _label_batch(rng, B, K)
+    feat = np.round(feat * 4) / 4  # ties between scores
+    ob_host = np.r_[0.9, 0.6 - 0.2 * np.arange(K)].astype(np.float32)
+    a_d, k_d, ob = _to_dev(acc, kept, ob_host)
+    out = np_(sv.av_diagnostics(_device_stats(feat.astype(np.float32)), a_d, k_d, ob, B, K,
+                                nbins))
+    o = ref.av_diagnostics(feat.astype(np.float64), acc, kept, ob_host.astype(np.float64), nbins)
+    assert out[3] == o["n"]
+    assert out[0] == o["auc"] or (np.isnan(out[0]) and np.isnan(o["auc"]))  # exact counts
+    assert abs(out[1] - o["logloss"]) <= 1e-9
+    if not o["near_bin_edge"]:
+        assert abs(out[2] - o["ece"]) <= 1e-9
+
+
+def test_diagnostics_one_class_and_no_labels():
+    K = 4
+    feat = np.linspace(-2, 2, 40 * K).reshape(40, K).astype(np.float32)
+    kept = np.full(40, K, dtype=np.int32)
+    ob_host = np.r_[1.0, np.zeros(K)].astype(np.float32)
+    a_d, k_d, ob = _to_dev(np.full(40, K, dtype=np.int32), kept, ob_host)  # all accepted
+    out = np_(sv.av_diagnostics(_device_stats(feat), a_d, k_d, ob, 40, K))
+    assert np.isnan(out[0]) and out[3] == 40 * K
+    a_d, k_d = _to_dev(np.zeros(40, dtype=np.int32), np.zeros(40, dtype=np.int32))
+    out = np_(sv.av_diagnostics(_device_stats(feat), a_d, k_d, ob, 40, K))
+    assert out[3] == 0 and np.isnan(out[0]) and np.isnan(out[1]) and np.isnan(out[2])
+
+
+# ---------------------------------------------------------------------------
+# Budgeted trimming
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("B,K", [(1024, 8), (40, 6), (1, 1), (2048, 8), (3, 7)])
+def test_budget_parity(B, K):
+    rng = np.random.default_rng(B + 3 * K)
+    conf = rng.uniform(0.02, 1.0, (B, K)).astype(np.float32)
+    assert B * K < 16 or 0 < ref.av_budget(conf, W.budget_costs(B, K))["budget"] < B * K
+    conf[rng.random((B, K)) < 0.05] = 1.0   # ties at survival 1
+    cost = W.budget_costs(B, K)
+    c_d, cost_d = _to_dev(conf, cost)
+    r = sv.av_budget(c_d, cost_d)
+    o = ref.av_budget(conf, cost)
+    if o["near"]:
+        pytest.skip("budget ratios tie within rounding")
+    assert int(np_(r["budget"])[0]) == o["budget"]
+    assert np.array_equal(np_(r["kept_len"]), o["kept_len"])
+    assert np.array_equal(np_(r["mask"]), o["mask"])
+    assert np_(r["best_ratio"])[0] == pytest.approx(o["best_ratio"], rel=1e-12)
+
+
+def test_budget_on_scorer_confidences():
+    # the AV pipeline's own confidences feed the budget
+    batch = W.make(4, B=64, V=5000, stride=5000)
+    ob = torch.tensor(W.av_init(4), dtype=torch.float32, device=DEV)
+    conf, _, _, _ = sv.av_score(batch.draft.to(DEV), batch.tokens.to(DEV), ob, 0.0, vocab=5000)
+    cost = W.budget_costs(*conf.shape)
+    r = sv.av_budget(conf, torch.from_numpy(cost).to(DEV))
+    o = ref.av_budget(np_(conf), cost)
+    assert 0 < o["budget"] < conf.numel()
+    assert int(np_(r["budget"])[0]) == o["budget"] or o["near"]
+    assert np.array_equal(np_(r["kept_len"]), o["kept_len"]) or o["near"]
+
+
+def test_budget_limits():
+    conf = torch.full((2049, 8), 0.5, device=DEV)
+    cost = torch.ones(2049 * 8 + 1, dtype=torch.float64, device=DEV)
+    with pytest.raises(sv.SpecVerifyError):
+        sv.av_budget(conf, cost)
+
+
+# ---------------------------------------------------------------------------
+# Prompt lookup
+# ---------------------------------------------------------------------------
+def _contexts(rng, B, S, alphabet, plant=True):
+    ctx = rng.integers(0, alphabet, (B, S)).astype(np.int32)
+    lens = rng.integers(0, S + 1, B).astype(np.int32)
+    if plant:  # copy a span from early in the context to its end
+        for b in range(0, B, 3):
+            n = lens[b]
+            if n > 40:
+                src = rng.integers(0, n // 2)
+                span = rng.integers(2, 12)
+                ctx[b, n - span:n] = ctx[b, src:src + span]
+    return ctx, lens
+
+
+@pytest.mark.parametrize("B,S,alphabet,n_min,n_max,K", [
+    (64, 300, 4, 1, 4, 5), (256, 8192, 32000, 2, 4, 8), (33, 1000, 50, 3, 3, 16),
+    (8, 70, 2, 1, 32, 64)])
+def test_ngram_parity(B, S, alphabet, n_min, n_max, K):
+    rng = np.random.default_rng(S + alphabet)
+    ctx, lens = _contexts(rng, B, S, alphabet)
+    gl = lens.copy()
+    gl[::7] += 5  # beyond the stride: the kernel clamps
+    c_d, l_d = _to_dev(ctx, gl)
+    r = sv.ngram_propose(c_d, l_d, n_min, n_max, K)
+    o = ref.ngram_propose(ctx, np.minimum(gl, S), n_min, n_max, K)
+    for k in ("draft", "draft_len", "match_pos", "match_n"):
+        assert np.array_equal(np_(r[k]), o[k]), k
