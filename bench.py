@@ -22,7 +22,8 @@ Besides the headline it reports:
   secondary     the other verification workloads (lossless with adaptive
                 verification, lossless at T=0.7 on V=152064, the full
                 adaptive-verification step loop, lossless at the headline
-                shape), each timed the same way.
+                shape), each timed the same way, and the estimator's Newton
+                refit, diagnostics, budgeted trimming and prompt lookup.
 """
 from __future__ import annotations
 
@@ -347,6 +348,71 @@ def run_secondary(sv, W, dev, stream, args):
     line["omega_beta_after"] = [round(v, 5) for v in ob.tolist()]
     out[c["name"]] = line
     del sets
+    torch.cuda.synchronize()
+    out["next_rows"] = run_next_rows(sv, W, dev, stream, args)
+    return out
+
+
+def run_next_rows(sv, W, dev, stream, args):
+    """The estimator refit, diagnostics, budgeted trimming and prompt lookup
+    at the adaptive-verification workload's shape (B=1024, K=8), each call
+    timed back to back."""
+    import numpy as np
+    import torch
+    out = {}
+    n = max(10, min(args.steps, 50))
+    B, K = 1024, 8
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    feat = (torch.randn(B, K, generator=g) * 1.3 - 1.2).to(dev)
+    ds = torch.zeros(24 * B * K, dtype=torch.uint8, device=dev)
+    sv.draft_stats_view(ds, B, K)["feat"].copy_(feat.view(-1))
+    kept = torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev)
+    acc = torch.minimum(torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev),
+                        kept)
+    ob = torch.tensor(W.av_init(4), dtype=torch.float32, device=dev)
+    st = sv.irls_state(K, dev)
+
+    ms = _timeit(lambda i: sv.irls_accumulate(st, ds, acc, kept, ob, B, K), n, 3, stream, torch)
+    out["irls_accumulate_b1024_k8"] = {"us_per_call": round(ms * 1e3, 2)}
+    ob2 = ob.clone()
+    ms = _timeit(lambda i: sv.irls_solve(st, ob2, K, 10.0), n, 3, stream, torch)
+    out["irls_solve_k8"] = {"us_per_call": round(ms * 1e3, 2)}
+    ms = _timeit(lambda i: sv.av_update(ds, acc, kept, ob2, 0.05, B, K), n, 3, stream, torch)
+    out["sgd_update_b1024_k8"] = {"us_per_call": round(ms * 1e3, 2)}
+
+    dout = torch.empty(4, dtype=torch.float64, device=dev)
+    dws = torch.empty(sv.load().spec_av_diagnostics_workspace_bytes(B, K, 10), dtype=torch.uint8,
+                      device=dev)
+    ms = _timeit(lambda i: sv.av_diagnostics(ds, acc, kept, ob, B, K, 10, out=dout,
+                                             workspace=dws), n, 3, stream, torch)
+    out["diagnostics_b1024_k8"] = {"us_per_call": round(ms * 1e3, 2),
+                                   "labels": int(dout[3].item())}
+
+    for Bb in (1024, 2048):
+        conf = torch.rand(Bb, K, generator=g).to(dev) * 0.98 + 0.02
+        cost = torch.from_numpy(W.budget_costs(Bb, K)).to(dev)
+        bws = torch.empty(sv.load().spec_av_budget_workspace_bytes(Bb, K), dtype=torch.uint8,
+                          device=dev)
+        res = {}
+
+        def fb(i):
+            res["r"] = sv.av_budget(conf, cost, workspace=bws)
+        ms = _timeit(fb, n, 3, stream, torch)
+        out["budget_b%d_k8" % Bb] = {"us_per_call": round(ms * 1e3, 2),
+                                     "budget": int(res["r"]["budget"].item()),
+                                     "drafts": Bb * K}
+
+    ctx, lens = W.ngram_contexts(256, 8192, 128256, seed=7, device=dev)
+    res = {}
+
+    def fn(i):
+        res["r"] = sv.ngram_propose(ctx, lens, 2, 4, 8)
+    ms = _timeit(fn, n, 3, stream, torch)
+    ctx_bytes = int(lens.sum().item()) * 4
+    out["ngram_b256_s8192_n2to4_k8"] = {
+        "us_per_call": round(ms * 1e3, 2), "context_bytes": ctx_bytes,
+        "gbps_context": round(ctx_bytes / (ms * 1e-3) / 1e9, 1),
+        "with_draft": int((res["r"]["draft_len"] > 0).sum().item())}
     torch.cuda.synchronize()
     return out
 

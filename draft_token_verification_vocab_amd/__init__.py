@@ -72,8 +72,9 @@ _SIGNATURES = {
                                                               ctypes.c_int32]),
     "spec_av_diagnostics": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P,
                                              ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
+    "spec_av_budget_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
     "spec_av_budget": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_double,
-                                        _P, _P, _P, _P, _P]),
+                                        _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "spec_ngram_propose": (ctypes.c_int32, [_P, _P, ctypes.c_int32, ctypes.c_int64,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                             _P, _P, _P]),
@@ -356,7 +357,7 @@ def av_diagnostics(draft_stats: torch.Tensor, accepted_len: torch.Tensor,
 
 
 def av_budget(conf: torch.Tensor, cost: torch.Tensor, n_requests: Optional[float] = None,
-              mask: bool = True) -> dict:
+              mask: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
     """Budgeted trimming of a [B, K] confidence tensor against a float64 cost
     table of B*K+1 entries: kept_len [B], keep mask, budget and best ratio."""
     _need_cuda(conf, "conf")
@@ -368,9 +369,13 @@ def av_budget(conf: torch.Tensor, cost: torch.Tensor, n_requests: Optional[float
            "budget": torch.empty(1, dtype=torch.int64, device=dev),
            "best_ratio": torch.empty(1, dtype=torch.float64, device=dev)}
     nr = float(B if n_requests is None else n_requests)
+    if workspace is None:
+        n = load().spec_av_budget_workspace_bytes(int(B), int(K))
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
     _check(load().spec_av_budget(_ptr(conf), int(B), int(K), _ptr(cost), nr,
                                  _ptr(res["kept_len"]), _ptr(res["mask"]), _ptr(res["budget"]),
-                                 _ptr(res["best_ratio"]), _stream(dev)), "spec_av_budget")
+                                 _ptr(res["best_ratio"]), _ptr(workspace), workspace.numel(),
+                                 _stream(dev)), "spec_av_budget")
     return res
 
 

@@ -43,9 +43,9 @@ constexpr int kLabelBlock = 512;
 // Diagnostics: labels per call, bins, label-kernel workgroup.
 constexpr int64_t kDiagMaxLabels = 1 << 16;
 constexpr int kDiagMaxBins = 64;
-constexpr int kDiagLabelBlock = 1024;
 // Prompt lookup: one workgroup per sequence.
 constexpr int kNgramBlock = 256;
+constexpr int kNgramUnroll = 8;
 
 size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -402,18 +402,21 @@ spec_status spec_irls_solve(void *state, int32_t num_draft, double c_damp, float
 
 namespace {
 struct DiagLayout {
-    size_t z, y, ctr, pairs, total;
-    int tiles;
+    size_t zpos, zneg, cnt, loss, bins, pairs, total;
+    int regions;
 };
 DiagLayout diag_layout(int32_t B, int32_t K, int32_t nbins) {
     DiagLayout l{};
     const size_t M = static_cast<size_t>(B) * K;
-    l.tiles = static_cast<int>((M + kDiagTile - 1) / kDiagTile);
-    l.z = 0;
-    l.y = align_up(l.z + 8 * M);
-    l.ctr = align_up(l.y + M);
-    l.pairs = align_up(l.ctr + 8 * static_cast<size_t>(3 + nbins));
-    l.total = align_up(l.pairs + 8 * static_cast<size_t>(l.tiles) * l.tiles);
+    l.regions = static_cast<int>((M + kDiagTile - 1) / kDiagTile);
+    const size_t R = static_cast<size_t>(l.regions);
+    l.zpos = 0;
+    l.zneg = align_up(8 * R * kDiagTile);
+    l.cnt = align_up(l.zneg + 8 * R * kDiagTile);
+    l.loss = align_up(l.cnt + 8 * R);
+    l.bins = align_up(l.loss + 8 * R);
+    l.pairs = align_up(l.bins + 8 * R * static_cast<size_t>(nbins));
+    l.total = align_up(l.pairs + 8 * R * R);
     return l;
 }
 }  // namespace
@@ -440,23 +443,48 @@ spec_status spec_av_diagnostics(const void *draft_stats, const int32_t *accepted
     if (!workspace || workspace_bytes < l.total) return SPEC_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SPEC_ERR_ARG;
     char *w = static_cast<char *>(workspace);
-    DiagWs ws{reinterpret_cast<double *>(w + l.z), reinterpret_cast<int8_t *>(w + l.y),
-              reinterpret_cast<unsigned long long *>(w + l.ctr),
+    DiagWs ws{reinterpret_cast<double *>(w + l.zpos), reinterpret_cast<double *>(w + l.zneg),
+              reinterpret_cast<int32_t *>(w + l.cnt),
+              reinterpret_cast<unsigned long long *>(w + l.loss),
+              reinterpret_cast<unsigned long long *>(w + l.bins),
               reinterpret_cast<unsigned long long *>(w + l.pairs)};
     const size_t n = static_cast<size_t>(batch) * num_draft;
     DraftStats ds = draft_stats_view(const_cast<void *>(draft_stats), n);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    diag_labels_kernel<kDiagLabelBlock><<<dim3(1), dim3(kDiagLabelBlock), 0, st>>>(
+    diag_labels_kernel<<<dim3(l.regions), dim3(kDiagTile), 0, st>>>(
         ds.feat, accepted_len, kept_len, batch, num_draft, omega_beta, nbins, ws);
-    diag_pairs_kernel<<<dim3(l.tiles * l.tiles), dim3(kDiagTile), 0, st>>>(
-        ws, static_cast<int>(n), l.tiles);
-    diag_finish_kernel<<<dim3(1), dim3(kWave), 0, st>>>(ws, nbins, l.tiles * l.tiles, out);
+    diag_pairs_kernel<<<dim3(l.regions * l.regions), dim3(kDiagTile), 0, st>>>(ws, l.regions);
+    diag_finish_kernel<<<dim3(1), dim3(kWave), 0, st>>>(ws, l.regions, nbins, out);
     return launch_status();
+}
+
+namespace {
+struct BudgetLayout {
+    size_t counts, sorted_s, sorted_e, total;
+    int tiles;
+};
+BudgetLayout budget_layout(int32_t B, int32_t K) {
+    BudgetLayout l{};
+    const size_t M = static_cast<size_t>(B) * K;
+    l.tiles = static_cast<int>((M + kBudgetTile - 1) / kBudgetTile);
+    l.counts = 0;
+    l.sorted_s = align_up(l.counts + 2 * M * static_cast<size_t>(l.tiles));
+    l.sorted_e = align_up(l.sorted_s + 4 * M);
+    l.total = align_up(l.sorted_e + 4 * M);
+    return l;
+}
+}  // namespace
+
+size_t spec_av_budget_workspace_bytes(int32_t batch, int32_t num_draft) {
+    if (batch < 1 || num_draft < 1 || static_cast<int64_t>(batch) * num_draft > kBudgetMax)
+        return 0;
+    return budget_layout(batch, num_draft).total;
 }
 
 spec_status spec_av_budget(const float *conf, int32_t batch, int32_t num_draft, const double *cost,
                            double n_requests, int32_t *kept_len, uint8_t *keep_mask,
-                           int64_t *budget, double *best_ratio, void *stream) {
+                           int64_t *budget, double *best_ratio, void *workspace,
+                           size_t workspace_bytes, void *stream) {
     if (batch < 1 || num_draft < 1 || !std::isfinite(n_requests)) return SPEC_ERR_ARG;
     const int64_t M = static_cast<int64_t>(batch) * num_draft;
     if (M > kBudgetMax) return SPEC_ERR_UNSUPPORTED;
@@ -464,18 +492,20 @@ spec_status spec_av_budget(const float *conf, int32_t batch, int32_t num_draft, 
         (reinterpret_cast<uintptr_t>(budget) & 7u) ||
         (best_ratio && (reinterpret_cast<uintptr_t>(best_ratio) & 7u)))
         return SPEC_ERR_ARG;
-    int P = 1;
-    while (P < M) P <<= 1;
-    const size_t lds = 8 * static_cast<size_t>(P) + static_cast<size_t>(M);
-    int dev = 0, max_lds = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-            hipSuccess)
-        return SPEC_ERR_HIP;
-    if (lds + 1024 > static_cast<size_t>(max_lds)) return SPEC_ERR_UNSUPPORTED;
-    budget_kernel<kBudgetThreads>
-        <<<dim3(1), dim3(kBudgetThreads), lds, static_cast<hipStream_t>(stream)>>>(
-            conf, batch, num_draft, cost, n_requests, kept_len, keep_mask, budget, best_ratio);
+    const BudgetLayout l = budget_layout(batch, num_draft);
+    if (!workspace || workspace_bytes < l.total) return SPEC_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SPEC_ERR_ARG;
+    char *w = static_cast<char *>(workspace);
+    BudgetWs ws{reinterpret_cast<uint16_t *>(w + l.counts), reinterpret_cast<float *>(w + l.sorted_s),
+                reinterpret_cast<int32_t *>(w + l.sorted_e)};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int m = static_cast<int>(M);
+    budget_rank_kernel<<<dim3(l.tiles * l.tiles), dim3(kBudgetTile), 0, st>>>(conf, num_draft, ws,
+                                                                            m, l.tiles);
+    budget_scatter_kernel<<<dim3((m + 255) / 256), dim3(256), 0, st>>>(conf, num_draft, ws, m,
+                                                                     l.tiles);
+    budget_finish_kernel<kBudgetThreads><<<dim3(1), dim3(kBudgetThreads), 0, st>>>(
+        ws, batch, num_draft, cost, n_requests, kept_len, keep_mask, budget, best_ratio);
     return launch_status();
 }
 
@@ -487,7 +517,7 @@ spec_status spec_ngram_propose(const int32_t *context, const int32_t *lengths, i
     if (n_max > kNgramMax || stride > INT32_MAX || num_draft > 64) return SPEC_ERR_UNSUPPORTED;
     if (batch == 0) return SPEC_OK;
     if (!context || !lengths || !draft || !draft_len) return SPEC_ERR_ARG;
-    ngram_kernel<kNgramBlock><<<dim3(batch), dim3(kNgramBlock), 0, static_cast<hipStream_t>(stream)>>>(
+    ngram_kernel<kNgramBlock, kNgramUnroll><<<dim3(batch), dim3(kNgramBlock), 0, static_cast<hipStream_t>(stream)>>>(
         context, lengths, stride, n_min, n_max, num_draft, draft, draft_len, match_pos, match_n);
     return launch_status();
 }

@@ -187,6 +187,35 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return lane63_u64(v);
 }
 
+// Sum of an unsigned 64-bit integer over the wave (exact in any order).
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+    v += dpp_pull64<0x111, 0xF>(v);
+    v += dpp_pull64<0x112, 0xF>(v);
+    v += dpp_pull64<0x114, 0xF>(v);
+    v += dpp_pull64<0x118, 0xF>(v);
+    v += dpp_pull64<0x142, 0xA>(v);
+    v += dpp_pull64<0x143, 0xC>(v);
+    return lane63_u64(v);
+}
+
+// Adds v into sh[key] for every active lane, one LDS atomic per distinct key
+// in the wave: lanes sharing a key are summed first (exact integer sums).
+// Call from wave-uniform control flow.
+__device__ __forceinline__ void wave_keyed_add(unsigned long long *sh, int key, uint64_t v,
+                                               bool active) {
+    uint64_t todo = __ballot(active);
+    const int lane = threadIdx.x & (kWave - 1);
+    while (todo) {
+        const int leader = __ffsll(static_cast<long long>(todo)) - 1;
+        const int q = __shfl(key, leader, kWave);
+        const bool mine = active && key == q;
+        const uint64_t grp = __ballot(mine);
+        const uint64_t sum = wave_sum_u64(mine ? v : 0ull);
+        if (lane == leader) atomicAdd(&sh[q], static_cast<unsigned long long>(sum));
+        todo &= ~grp;
+    }
+}
+
 // Maximum of a non-negative double over the wave (such doubles order like
 // their bit patterns).
 __device__ __forceinline__ double wave_max_f64_nonneg(double x) {

@@ -57,22 +57,36 @@ __device__ void label_sums(const float *feat, const int32_t *accepted_len,
     for (int i = wv; i < K; i += NT / kWave) {
         const double beta = static_cast<double>(omega_beta[1 + i]);
         double n = 0.0, r = 0.0, rf = 0.0, w = 0.0, wf = 0.0, wff = 0.0;
-        for (int b = lane; b < B; b += kWave) {
-            const int L = kept_len ? clamp_len(kept_len[b], K) : K;
-            const int a = clamp_len(accepted_len[b], K);
-            const int nl = a + 1 < L ? a + 1 : L;
-            if (i < nl) {
-                const double f = static_cast<double>(feat[static_cast<int64_t>(b) * K + i]);
-                const double s = 1.0 / (1.0 + exp(-(omega * f + beta)));
-                const double d = s - (i < a ? 1.0 : 0.0);
-                n += 1.0;
-                r += d;
-                rf += d * f;
-                if (CURV) {
-                    const double ww = s * (1.0 - s);
-                    w += ww;
-                    wf += ww * f;
-                    wff += ww * f * f;
+        constexpr int U = 4;  // sequences per lane per pass: their loads go out together
+        for (int b0 = lane; b0 < B; b0 += U * kWave) {
+            int La[U], aa[U];
+            float fa[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int b = b0 + u * kWave;
+                const int bc = b < B ? b : B - 1;  // in range; masked out below
+                La[u] = kept_len ? kept_len[bc] : K;
+                aa[u] = accepted_len[bc];
+                fa[u] = feat[static_cast<int64_t>(bc) * K + i];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int L = clamp_len(La[u], K);
+                const int a = clamp_len(aa[u], K);
+                const int nl = a + 1 < L ? a + 1 : L;
+                if (b0 + u * kWave < B && i < nl) {
+                    const double f = static_cast<double>(fa[u]);
+                    const double s = 1.0 / (1.0 + exp(-(omega * f + beta)));
+                    const double d = s - (i < a ? 1.0 : 0.0);
+                    n += 1.0;
+                    r += d;
+                    rf += d * f;
+                    if (CURV) {
+                        const double ww = s * (1.0 - s);
+                        w += ww;
+                        wf += ww * f;
+                        wff += ww * f * f;
+                    }
                 }
             }
         }
@@ -215,173 +229,231 @@ __global__ __launch_bounds__(kWave) void irls_solve_kernel(double *state, int K,
 }
 
 // --------------------------------------------------------------------------
-// Diagnostics.  Workspace: z[M] doubles (NaN where no label) | y[M] int8 |
-// counters: loss (fixed point 2^-32), npos, nneg, bins[nbins] (fixed point
-// 2^-40) | pair partials [tiles^2] uint64 (2 x wins + ties).
-// Fixed-point sums make the order of additions irrelevant, so the figures are
-// deterministic; the rounding is below 2^-32 per label.
+// Diagnostics, spread over the GPU without atomics to global memory:
+//   labels  a workgroup per 256 drafts: z and y of each label; within the
+//           workgroup the accepted labels' z are packed at the front of its
+//           256-slot region of zpos, the rejected ones' in zneg; its label
+//           counts, loss sum and bin sums (fixed point: order-free) go to
+//           per-workgroup slots;
+//   pairs   a workgroup per (region i, region j): accepted of i against
+//           rejected of j, 2 x wins + ties;
+//   finish  one wave sums the slots and forms the ratios.
+// Fixed point: loss in units of 2^-32, bin sums in 2^-40 per label.
 // --------------------------------------------------------------------------
 constexpr int kDiagTile = 256;
 constexpr double kLossScale = 4294967296.0;        // 2^32
 constexpr double kBinScale = 1099511627776.0;      // 2^40
 
 struct DiagWs {
-    double *z;
-    int8_t *y;
-    unsigned long long *ctr;  // [0] loss, [1] npos, [2] nneg, [3..3+nbins) bins
-    unsigned long long *pairs;
+    double *zpos, *zneg;        // [regions * 256]
+    int32_t *cnt;               // [regions][2]: accepted, rejected
+    unsigned long long *loss;   // [regions]
+    unsigned long long *bins;   // [regions][nbins]
+    unsigned long long *pairs;  // [regions^2]
 };
 
-template <int NT>
-__global__ __launch_bounds__(NT) void diag_labels_kernel(const float *feat,
-                                                        const int32_t *accepted_len,
-                                                        const int32_t *kept_len, int B, int K,
-                                                        const float *omega_beta, int nbins,
-                                                        DiagWs ws) {
-    __shared__ unsigned long long sh[3 + 64];
-    for (int q = threadIdx.x; q < 3 + nbins; q += NT) sh[q] = 0ull;
+__global__ __launch_bounds__(kDiagTile) void diag_labels_kernel(
+    const float *feat, const int32_t *accepted_len, const int32_t *kept_len, int B, int K,
+    const float *omega_beta, int nbins, DiagWs ws) {
+    constexpr int NW = kDiagTile / kWave;
+    __shared__ unsigned long long sh_bins[64];
+    __shared__ unsigned long long sh_loss[NW];
+    __shared__ int sh_np[NW], sh_nn[NW];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int reg = blockIdx.x;
+    for (int q = tid; q < nbins; q += kDiagTile) sh_bins[q] = 0ull;
     __syncthreads();
-    const double omega = static_cast<double>(omega_beta[0]);
     const int M = B * K;
-    for (int t = threadIdx.x; t < M; t += NT) {
-        const int b = t / K, i = t - b * K;
-        const int L = kept_len ? clamp_len(kept_len[b], K) : K;
-        const int a = clamp_len(accepted_len[b], K);
-        const int nl = a + 1 < L ? a + 1 : L;
-        if (i < nl) {
-            // z rounded after the product and after the sum, as plain double
-            // arithmetic forms it
-            const double z = __dadd_rn(__dmul_rn(omega, static_cast<double>(feat[t])),
-                                       static_cast<double>(omega_beta[1 + i]));
-            const int yv = i < a ? 1 : 0;
-            ws.z[t] = z;
-            ws.y[t] = static_cast<int8_t>(yv);
-            // -log s = softplus(-z), -log(1 - s) = softplus(z)
-            const double u = yv ? -z : z;
-            const double loss = u > 0.0 ? u + log1p(exp(-u)) : log1p(exp(u));
-            const double s = 1.0 / (1.0 + exp(-z));
-            int bin = static_cast<int>(floor(s * nbins));
-            bin = bin < 0 ? 0 : (bin > nbins - 1 ? nbins - 1 : bin);
-            atomicAdd(&sh[0], static_cast<unsigned long long>(llrint(loss * kLossScale)));
-            atomicAdd(&sh[yv ? 1 : 2], 1ull);
-            atomicAdd(&sh[3 + bin],
-                      static_cast<unsigned long long>(llrint((s - yv) * kBinScale)));
-        } else {
-            ws.z[t] = __builtin_nan("");
-            ws.y[t] = -1;
-        }
+    const int t = reg * kDiagTile + tid;
+    const int b = t < M ? t / K : 0, i = t < M ? t - b * K : 0;
+    const int L = t < M ? (kept_len ? clamp_len(kept_len[b], K) : K) : 0;
+    const int a = t < M ? clamp_len(accepted_len[b], K) : 0;
+    const int nl = a + 1 < L ? a + 1 : L;
+    const bool lab = t < M && i < nl;
+    const int yv = i < a ? 1 : 0;
+    double z = 0.0;
+    int bin = 0;
+    uint64_t bv = 0ull, lv = 0ull;
+    if (lab) {
+        // z rounded after the product and after the sum, as plain double
+        // arithmetic forms it
+        z = __dadd_rn(__dmul_rn(static_cast<double>(omega_beta[0]), static_cast<double>(feat[t])),
+                      static_cast<double>(omega_beta[1 + i]));
+        // -log s = softplus(-z), -log(1 - s) = softplus(z)
+        const double u = yv ? -z : z;
+        const double loss = u > 0.0 ? u + log1p(exp(-u)) : log1p(exp(u));
+        const double s = 1.0 / (1.0 + exp(-z));
+        bin = static_cast<int>(floor(s * nbins));
+        bin = bin < 0 ? 0 : (bin > nbins - 1 ? nbins - 1 : bin);
+        bv = static_cast<uint64_t>(llrint((s - yv) * kBinScale));
+        lv = static_cast<uint64_t>(llrint(loss * kLossScale));
+    }
+    wave_keyed_add(sh_bins, bin, bv, lab);
+    const bool pos = lab && yv, neg = lab && !yv;
+    const uint64_t bp = __ballot(pos), bn = __ballot(neg);
+    const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;  // lanes under this one
+    const uint64_t wl = wave_sum_u64(lv);
+    if (lane == 0) {
+        sh_np[wv] = __popcll(bp);
+        sh_nn[wv] = __popcll(bn);
+        sh_loss[wv] = wl;
     }
     __syncthreads();
-    for (int q = threadIdx.x; q < 3 + nbins; q += NT) ws.ctr[q] = sh[q];
+    int op = 0, on = 0;
+    for (int w = 0; w < wv; ++w) {
+        op += sh_np[w];
+        on += sh_nn[w];
+    }
+    if (pos) ws.zpos[reg * kDiagTile + op + __popcll(bp & below)] = z;
+    if (neg) ws.zneg[reg * kDiagTile + on + __popcll(bn & below)] = z;
+    if (tid == 0) {
+        int np = 0, nn = 0;
+        unsigned long long ls = 0ull;
+        for (int w = 0; w < NW; ++w) {
+            np += sh_np[w];
+            nn += sh_nn[w];
+            ls += sh_loss[w];
+        }
+        ws.cnt[2 * reg] = np;
+        ws.cnt[2 * reg + 1] = nn;
+        ws.loss[reg] = ls;
+    }
+    for (int q = tid; q < nbins; q += kDiagTile) ws.bins[static_cast<int64_t>(reg) * nbins + q] = sh_bins[q];
 }
 
-// Tile (row tile, column tile): rows that are accepted against columns that
-// are rejected.  One partial per workgroup.
-__global__ __launch_bounds__(kDiagTile) void diag_pairs_kernel(DiagWs ws, int M, int tiles) {
-    __shared__ double cz[kDiagTile];
-    __shared__ int8_t cy[kDiagTile];
+__global__ __launch_bounds__(kDiagTile) void diag_pairs_kernel(DiagWs ws, int regions) {
+    __shared__ double zn[kDiagTile];
     __shared__ unsigned long long acc;
-    const int rt = blockIdx.x / tiles, ct = blockIdx.x - rt * tiles;
-    const int r = rt * kDiagTile + threadIdx.x, c = ct * kDiagTile + threadIdx.x;
-    if (threadIdx.x == 0) acc = 0ull;
-    cz[threadIdx.x] = c < M ? ws.z[c] : 0.0;
-    cy[threadIdx.x] = c < M ? ws.y[c] : static_cast<int8_t>(-1);
-    const bool pos = r < M && ws.y[r] == 1;
-    const double zr = r < M ? ws.z[r] : 0.0;
-    __syncthreads();
-    unsigned int cnt = 0;
-    if (pos) {
-        for (int k = 0; k < kDiagTile; ++k) {
-            if (cy[k] == 0) cnt += zr > cz[k] ? 2u : (zr == cz[k] ? 1u : 0u);
-        }
+    const int ri = blockIdx.x / regions, rj = blockIdx.x - ri * regions;
+    const int np = ws.cnt[2 * ri], nn = ws.cnt[2 * rj + 1];
+    if (np == 0 || nn == 0) {
+        if (threadIdx.x == 0) ws.pairs[blockIdx.x] = 0ull;
+        return;
     }
-    atomicAdd(&acc, static_cast<unsigned long long>(cnt));
+    if (threadIdx.x == 0) acc = 0ull;
+    if (threadIdx.x < nn) zn[threadIdx.x] = ws.zneg[rj * kDiagTile + threadIdx.x];
+    const double zp = threadIdx.x < np ? ws.zpos[ri * kDiagTile + threadIdx.x] : 0.0;
+    __syncthreads();
+    unsigned int c = 0;
+    if (threadIdx.x < np)
+        for (int k = 0; k < nn; ++k) c += zp > zn[k] ? 2u : (zp == zn[k] ? 1u : 0u);
+    const uint64_t wc = wave_sum_u64(c);
+    if ((threadIdx.x & (kWave - 1)) == 0) atomicAdd(&acc, static_cast<unsigned long long>(wc));
     __syncthreads();
     if (threadIdx.x == 0) ws.pairs[blockIdx.x] = acc;
 }
 
-__global__ __launch_bounds__(kWave) void diag_finish_kernel(DiagWs ws, int nbins, int npart,
+__global__ __launch_bounds__(kWave) void diag_finish_kernel(DiagWs ws, int regions, int nbins,
                                                             double *out) {
-    unsigned long long part = 0ull;
-    for (int q = threadIdx.x; q < npart; q += kWave) part += ws.pairs[q];
-    // integer sums: any order gives the same total
-    for (int o = kWave / 2; o > 0; o /= 2)
-        part += static_cast<unsigned long long>(__shfl_xor(static_cast<long long>(part), o));
-    if (threadIdx.x == 0) {
-        const double npos = static_cast<double>(ws.ctr[1]);
-        const double nneg = static_cast<double>(ws.ctr[2]);
+    const int lane = threadIdx.x;
+    uint64_t part = 0ull, np = 0ull, nn = 0ull, ls = 0ull;
+    for (int q = lane; q < regions * regions; q += kWave) part += ws.pairs[q];
+    for (int r = lane; r < regions; r += kWave) {
+        np += static_cast<uint64_t>(ws.cnt[2 * r]);
+        nn += static_cast<uint64_t>(ws.cnt[2 * r + 1]);
+        ls += ws.loss[r];
+    }
+    part = wave_sum_u64(part);
+    np = wave_sum_u64(np);
+    nn = wave_sum_u64(nn);
+    ls = wave_sum_u64(ls);
+    // ECE: |sum over regions| per bin, a lane per bin
+    long long ece_fp = 0;
+    for (int q = lane; q < nbins; q += kWave) {
+        uint64_t v = 0ull;
+        for (int r = 0; r < regions; ++r) v += ws.bins[static_cast<int64_t>(r) * nbins + q];
+        const long long sv = static_cast<long long>(v);
+        ece_fp += sv < 0 ? -sv : sv;
+    }
+    ece_fp = static_cast<long long>(wave_sum_u64(static_cast<uint64_t>(ece_fp)));
+    if (lane == 0) {
+        const double npos = static_cast<double>(np), nneg = static_cast<double>(nn);
         const double N = npos + nneg;
-        long long ece_fp = 0;
-        for (int q = 0; q < nbins; ++q) {
-            const long long v = static_cast<long long>(ws.ctr[3 + q]);
-            ece_fp += v < 0 ? -v : v;
-        }
         const double nan = __builtin_nan("");
         out[0] = (npos > 0.0 && nneg > 0.0) ? static_cast<double>(part) / (2.0 * npos * nneg) : nan;
-        out[1] = N > 0.0 ? static_cast<double>(ws.ctr[0]) / kLossScale / N : nan;
+        out[1] = N > 0.0 ? static_cast<double>(ls) / kLossScale / N : nan;
         out[2] = N > 0.0 ? static_cast<double>(ece_fp) / kBinScale / N : nan;
         out[3] = N;
     }
 }
 
 // --------------------------------------------------------------------------
-// Budgeted trimming: one workgroup, the B*K <= kBudgetMax survivals sorted in
-// LDS by a bitonic network on 64-bit keys (~ordered(survival), flat index).
+// Budgeted trimming, spread over the GPU:
+//   key      survival of a draft (its float running product) and its index
+//            as one 64-bit key (~ordered(survival), flat index): ascending
+//            keys = decreasing survival, ties by flat index; all distinct;
+//   rank     a 2D grid of 256 x 256 tiles counts, for every draft, the keys
+//            of one tile below its own (exact integer counts);
+//   scatter  rank = sum of its counts; the draft's survival and index go to
+//            that slot of the sorted arrays;
+//   finish   one workgroup scans the sorted survivals (double), takes the
+//            first best ratio, and marks the first `budget` drafts.
+// Workspace: counts[tiles][M] u16 | sorted_s[M] f32 | sorted_e[M] i32.
 // --------------------------------------------------------------------------
-constexpr int kBudgetMax = 16384;
+constexpr int kBudgetMax = 1 << 16;
+constexpr int kBudgetTile = 256;
 constexpr int kBudgetThreads = 1024;
 
-template <int NT>
-__global__ __launch_bounds__(NT) void budget_kernel(const float *conf, int B, int K,
-                                                   const double *cost, double n_requests,
-                                                   int32_t *kept_len, uint8_t *mask,
-                                                   int64_t *budget_out, double *best_ratio) {
-    extern __shared__ unsigned long long keys[];  // [P] then M mask bytes
-    const int M = B * K;
-    int P = 1;
-    while (P < M) P <<= 1;
-    uint8_t *kmask = reinterpret_cast<uint8_t *>(keys + P);
-    const int tid = threadIdx.x;
-    // survival, formed in float along each sequence
-    for (int b = tid; b < B; b += NT) {
-        float S = 1.0f;
-        for (int i = 0; i < K; ++i) {
-            const int f = b * K + i;
-            S = S * conf[f];
-            keys[f] = (static_cast<unsigned long long>(~ordered_bits(S)) << 32) |
-                      static_cast<unsigned int>(f);
-        }
-    }
-    for (int f = M + tid; f < P; f += NT) keys[f] = ~0ull;
-    for (int f = tid; f < M; f += NT) kmask[f] = 0;
+struct BudgetWs {
+    uint16_t *counts;
+    float *sorted_s;
+    int32_t *sorted_e;
+};
+
+// Key of draft f: its survival (the running float product along its
+// sequence) and its index.
+__device__ __forceinline__ unsigned long long budget_key(const float *conf, int K, int f) {
+    const int b = f / K, i = f - b * K;
+    float S = 1.0f;
+    for (int q = 0; q <= i; ++q) S = S * conf[b * K + q];
+    return (static_cast<unsigned long long>(~ordered_bits(S)) << 32) |
+           static_cast<unsigned int>(f);
+}
+
+__global__ __launch_bounds__(kBudgetTile) void budget_rank_kernel(const float *conf, int K,
+                                                                 BudgetWs ws, int M, int tiles) {
+    __shared__ unsigned long long tk[kBudgetTile];
+    const int te = blockIdx.x / tiles, tt = blockIdx.x - te * tiles;
+    const int e = te * kBudgetTile + threadIdx.x;
+    const int k = tt * kBudgetTile + threadIdx.x;
+    tk[threadIdx.x] = k < M ? budget_key(conf, K, k) : ~0ull;  // padding sorts last
+    const unsigned long long me = e < M ? budget_key(conf, K, e) : 0ull;
     __syncthreads();
-    // ascending bitonic sort: survival decreasing, ties by flat index
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int e = tid; e < P / 2; e += NT) {
-                const int lo = (e / j) * 2 * j + (e % j);
-                const int hi = lo + j;
-                const bool up = (lo & k) == 0;
-                const unsigned long long x = keys[lo], y = keys[hi];
-                if ((x > y) == up) {
-                    keys[lo] = y;
-                    keys[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
+    if (e >= M) return;
+    unsigned int c = 0;
+#pragma unroll 8
+    for (int q = 0; q < kBudgetTile; ++q) c += tk[q] < me ? 1u : 0u;
+    ws.counts[static_cast<int64_t>(tt) * M + e] = static_cast<uint16_t>(c);
+}
+
+__global__ __launch_bounds__(256) void budget_scatter_kernel(const float *conf, int K, BudgetWs ws,
+                                                           int M, int tiles) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= M) return;
+    int r = 0;
+#pragma unroll 8
+    for (int t = 0; t < tiles; ++t) r += ws.counts[static_cast<int64_t>(t) * M + e];
+    const unsigned long long key = budget_key(conf, K, e);
+    ws.sorted_s[r] = from_ordered_bits(~static_cast<unsigned int>(key >> 32));
+    ws.sorted_e[r] = static_cast<int32_t>(key & 0xFFFFFFFFull);
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void budget_finish_kernel(BudgetWs ws, int B, int K,
+                                                          const double *cost, double n_requests,
+                                                          int32_t *kept_len, uint8_t *mask,
+                                                          int64_t *budget_out, double *best_ratio) {
+    const int M = B * K;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wv = tid / kWave;
     // prefix sums of the sorted survivals: each thread a contiguous segment
     const int seg = (M + NT - 1) / NT;
-    const int s0 = tid * seg, s1 = min(M, s0 + seg);
-    auto surv_at = [&](int t) -> double {
-        return static_cast<double>(from_ordered_bits(~static_cast<unsigned int>(keys[t] >> 32)));
-    };
+    const int s0 = tid * seg < M ? tid * seg : M;
+    const int s1 = s0 + seg < M ? s0 + seg : M;
     double tot = 0.0;
-    for (int t = s0; t < s1; ++t) tot += surv_at(t);
-    // exclusive scan of the segment totals (fixed order)
+#pragma unroll 8
+    for (int t = s0; t < s1; ++t) tot += static_cast<double>(ws.sorted_s[t]);
     __shared__ double wsum[NT / kWave];
-    const int lane = tid & (kWave - 1), wv = tid / kWave;
     double incl = tot;
     for (int o = 1; o < kWave; o <<= 1) {
         const double v = __shfl_up(incl, o, kWave);
@@ -394,7 +466,6 @@ __global__ __launch_bounds__(NT) void budget_kernel(const float *conf, int B, in
     double before = 0.0;
     for (int w = 0; w < wv; ++w) before += wsum[w];
     double est = n_requests + (before + excl);
-    // best ratio over this segment's budgets k = t+1 (and k = 0 for thread 0)
     double best = -__builtin_inf();
     int bk = INT_MAX;
     if (tid == 0) {
@@ -402,15 +473,14 @@ __global__ __launch_bounds__(NT) void budget_kernel(const float *conf, int B, in
         bk = 0;
     }
     for (int t = s0; t < s1; ++t) {
-        est += surv_at(t);
+        est += static_cast<double>(ws.sorted_s[t]);
         const double r = est / cost[t + 1];
         if (r > best) {
             best = r;
             bk = t + 1;
         }
     }
-    // first maximum over the workgroup
-    for (int o = kWave / 2; o > 0; o /= 2) {
+    for (int o = kWave / 2; o > 0; o /= 2) {  // first maximum
         const double ob = __shfl_xor(best, o, kWave);
         const int ok = __shfl_xor(bk, o, kWave);
         if (ob > best || (ob == best && ok < bk)) {
@@ -425,6 +495,8 @@ __global__ __launch_bounds__(NT) void budget_kernel(const float *conf, int B, in
         wb[wv] = best;
         wk[wv] = bk;
     }
+    for (int b = tid; b < B; b += NT) kept_len[b] = 0;
+    for (int f = tid; f < M && mask; f += NT) mask[f] = 0;
     __syncthreads();
     if (tid == 0) {
         double b0 = wb[0];
@@ -439,25 +511,27 @@ __global__ __launch_bounds__(NT) void budget_kernel(const float *conf, int B, in
         if (best_ratio) *best_ratio = b0;
     }
     __syncthreads();
-    for (int t = tid; t < s_budget; t += NT) kmask[keys[t] & 0xFFFFFFFFull] = 1;
-    __syncthreads();
-    for (int f = tid; f < M && mask; f += NT) mask[f] = kmask[f];
-    for (int b = tid; b < B; b += NT) {
-        int n = 0;
-        for (int i = 0; i < K; ++i) n += kmask[b * K + i];
-        kept_len[b] = n;
+    // kept drafts are a prefix of each sequence: kept_len = 1 + last kept position
+    for (int t = tid; t < s_budget; t += NT) {
+        const int e = ws.sorted_e[t];
+        if (mask) mask[e] = 1;
+        atomicMax(&kept_len[e / K], e % K + 1);
     }
 }
 
 // --------------------------------------------------------------------------
-// Prompt lookup: one workgroup per sequence.  For n-gram length g from n_max
-// down, the workgroup scans start positions p = n-g-1, n-g-2, ... NT at a
-// time and stops at the first block of positions holding a match; the
-// largest matching p there is the latest earlier occurrence.
+// Prompt lookup: one workgroup per sequence, one backward pass.  For an end
+// position e <= n-2 let l(e) be the length of the match between the tokens
+// ending at e and the context's last tokens (capped at n_max).  A g-gram
+// occurrence ends at e iff l(e) >= g; the answer is the largest g with such
+// an e, and the largest e for it.  The workgroup scans e = n-2, n-3, ...,
+// NT*U positions per pass, keeps best_e[g] = max e with l(e) >= g in LDS, and
+// stops once the longest possible length has an occurrence (the first pass
+// that finds one holds its latest).
 // --------------------------------------------------------------------------
 constexpr int kNgramMax = 32;
 
-template <int NT>
+template <int NT, int U>
 __global__ __launch_bounds__(NT) void ngram_kernel(const int32_t *ctx, const int32_t *lengths,
                                                   int64_t stride, int n_min, int n_max, int K,
                                                   int32_t *draft, int32_t *draft_len,
@@ -467,39 +541,45 @@ __global__ __launch_bounds__(NT) void ngram_kernel(const int32_t *ctx, const int
     const int32_t *c = ctx + static_cast<int64_t>(b) * stride;
     const int nb = lengths[b];
     const int n = nb < 0 ? 0 : (nb > stride ? static_cast<int>(stride) : nb);
-    __shared__ int32_t suf[kNgramMax];
-    __shared__ int s_hit;
-    __shared__ int wmin[NT / kWave];
-    int pos = -1, gf = 0;
-    for (int g = n_max; g >= n_min && pos < 0; --g) {
-        if (g >= n) continue;
-        __syncthreads();
-        if (tid < g) suf[tid] = c[n - g + tid];
-        __syncthreads();
-        for (int base = n - g - 1; base >= 0; base -= NT) {
-            const int p = base - tid;
-            bool ok = p >= 0;
-            // last token first: most start positions fail there
-            for (int q = g - 1; q >= 0 && ok; --q) ok = c[p + q] == suf[q];
-            // smallest thread index with a match = largest p
-            const unsigned long long m = __ballot(ok);
-            if ((tid & (kWave - 1)) == 0)
-                wmin[tid / kWave] = m ? (tid + __ffsll(static_cast<long long>(m)) - 1) : INT_MAX;
-            __syncthreads();
-            if (tid == 0) {
-                int mn = INT_MAX;
-                for (int w = 0; w < NT / kWave; ++w) mn = wmin[w] < mn ? wmin[w] : mn;
-                s_hit = mn;
+    __shared__ int32_t suf[kNgramMax];     // suf[q] = c[n-1-q]
+    __shared__ int best_e[kNgramMax + 1];  // by length g
+    __shared__ int s_stop;
+    // the longest length that can occur: an occurrence ends at e <= n-2
+    const int gmax = n_max < n - 1 ? n_max : n - 1;
+    for (int q = tid; q <= kNgramMax; q += NT) best_e[q] = -1;
+    if (tid < gmax) suf[tid] = c[n - 1 - tid];
+    __syncthreads();
+    if (gmax >= n_min) {
+        for (int top = n - 2; top >= 0; top -= NT * U) {
+            int32_t last[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {  // the tokens at e, loaded together
+                const int e = top - tid - NT * u;
+                last[u] = e >= 0 ? c[e] : -1;
+            }
+            const int32_t s0 = suf[0];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = top - tid - NT * u;
+                if (e >= 0 && last[u] == s0) {
+                    int l = 1;
+                    while (l < gmax && l <= e && c[e - l] == suf[l]) ++l;
+                    for (int g = n_min; g <= l; ++g) atomicMax(&best_e[g], e);
+                }
             }
             __syncthreads();
-            const int hit = s_hit;
-            if (hit != INT_MAX) {
-                pos = base - hit;
-                gf = g;
-                break;
-            }
+            if (tid == 0) s_stop = best_e[gmax] >= 0;
+            __syncthreads();
+            if (s_stop) break;
         }
     }
+    int pos = -1, gf = 0;
+    for (int g = gmax; g >= n_min; --g)
+        if (best_e[g] >= 0) {
+            pos = best_e[g] - g + 1;
+            gf = g;
+            break;
+        }
     int dl = 0;
     if (pos >= 0) {
         dl = n - (pos + gf);

@@ -248,12 +248,16 @@ spec_status spec_av_diagnostics(const void *draft_stats, const int32_t *accepted
  * [B*K+1], 8-byte aligned (the measured cost of verifying k drafts).
  * Outputs: kept_len device int32 [B]; keep_mask device uint8 [B][K] or NULL;
  * budget device int64 (8-byte aligned); best_ratio device double or NULL.
- * One workgroup sorts the survivals in LDS: B*K <= 16384 and within the
- * device's per-workgroup LDS, else SPEC_ERR_UNSUPPORTED.
+ * workspace: device, spec_av_budget_workspace_bytes, 16-byte aligned.  The
+ * order is found by counting, for every draft, the keys below its own over
+ * the whole GPU (O((B*K)^2) comparisons): B*K <= 65536, else
+ * SPEC_ERR_UNSUPPORTED.
  */
+size_t spec_av_budget_workspace_bytes(int32_t batch, int32_t num_draft);
 spec_status spec_av_budget(const float *conf, int32_t batch, int32_t num_draft, const double *cost,
                            double n_requests, int32_t *kept_len, uint8_t *keep_mask,
-                           int64_t *budget, double *best_ratio, void *stream);
+                           int64_t *budget, double *best_ratio, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * spec_ngram_propose -- prompt-lookup drafting ([SD] section "N-gram (prompt

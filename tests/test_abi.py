@@ -43,7 +43,8 @@ def test_header_declares_the_entry_points():
               "spec_workspace_bytes", "spec_draft_stats_bytes", "spec_status_string",
               "spec_read_probe", "spec_irls_state_bytes", "spec_irls_reset",
               "spec_irls_accumulate", "spec_irls_solve", "spec_av_diagnostics",
-              "spec_av_diagnostics_workspace_bytes", "spec_av_budget", "spec_ngram_propose"):
+              "spec_av_diagnostics_workspace_bytes", "spec_av_budget",
+              "spec_av_budget_workspace_bytes", "spec_ngram_propose"):
         assert n in names
 
 
@@ -152,6 +153,8 @@ def test_next_rows_sizes(L):
     assert L.spec_av_diagnostics_workspace_bytes(1024, 8, 10) > 8 * 8192
     assert L.spec_av_diagnostics_workspace_bytes(1024, 8, 65) == 0
     assert L.spec_av_diagnostics_workspace_bytes(8192, 16, 10) == 0  # > 65536 labels
+    assert L.spec_av_budget_workspace_bytes(1024, 8) >= 8192 * (2 * 32 + 8)
+    assert L.spec_av_budget_workspace_bytes(8193, 8) == 0
 
 
 @host_only
@@ -171,10 +174,13 @@ def test_next_rows_validate_on_host(L):
     assert L.spec_av_diagnostics(a, a, None, 4, 4, a, 65, a, a, 1 << 20, None) == -2
     assert L.spec_av_diagnostics(a, a, None, 4, 4, a, 10, a, a, 16, None) == -3
     assert L.spec_av_diagnostics(a, a, None, 4, 4, a, 10, a, None, 1 << 20, None) == -3
-    assert L.spec_av_budget(a, 2049, 8, a, 1.0, a, None, a, None, None) == -2
-    assert L.spec_av_budget(a, 4, 4, P(12), 1.0, a, None, a, None, None) == -1
-    assert L.spec_av_budget(a, 4, 4, a, float("nan"), a, None, a, None, None) == -1
-    assert L.spec_av_budget(a, 0, 4, a, 1.0, a, None, a, None, None) == -1
+    big = 1 << 30
+    assert L.spec_av_budget(a, 8193, 8, a, 1.0, a, None, a, None, a, big, None) == -2
+    assert L.spec_av_budget(a, 4, 4, P(12), 1.0, a, None, a, None, a, big, None) == -1
+    assert L.spec_av_budget(a, 4, 4, a, float("nan"), a, None, a, None, a, big, None) == -1
+    assert L.spec_av_budget(a, 0, 4, a, 1.0, a, None, a, None, a, big, None) == -1
+    assert L.spec_av_budget(a, 4, 4, a, 1.0, a, None, a, None, a, 16, None) == -3
+    assert L.spec_av_budget(a, 4, 4, a, 1.0, a, None, a, None, None, big, None) == -3
     assert L.spec_ngram_propose(a, a, 4, 100, 0, 3, 4, a, a, None, None, None) == -1
     assert L.spec_ngram_propose(a, a, 4, 100, 3, 2, 4, a, a, None, None, None) == -1
     assert L.spec_ngram_propose(a, a, 4, 100, 1, 33, 4, a, a, None, None, None) == -2

@@ -207,9 +207,21 @@ def test_budget_on_scorer_confidences():
     assert np.array_equal(np_(r["kept_len"]), o["kept_len"]) or o["near"]
 
 
-def test_budget_limits():
-    conf = torch.full((2049, 8), 0.5, device=DEV)
-    cost = torch.ones(2049 * 8 + 1, dtype=torch.float64, device=DEV)
+def test_budget_largest_batch_and_limit():
+    # 8192 sequences x 8 drafts = 65536, the largest batch the call takes
+    rng = np.random.default_rng(21)
+    B, K = 8192, 8
+    conf = rng.uniform(0.02, 1.0, (B, K)).astype(np.float32)
+    cost = W.budget_costs(B, K)
+    c_d, cost_d = _to_dev(conf, cost)
+    r = sv.av_budget(c_d, cost_d)
+    o = ref.av_budget(conf, cost)
+    assert 0 < o["budget"] < B * K
+    if not o["near"]:
+        assert int(np_(r["budget"])[0]) == o["budget"]
+        assert np.array_equal(np_(r["kept_len"]), o["kept_len"])
+    conf = torch.full((8193, 8), 0.5, device=DEV)
+    cost = torch.ones(8193 * 8 + 1, dtype=torch.float64, device=DEV)
     with pytest.raises(sv.SpecVerifyError):
         sv.av_budget(conf, cost)
 
