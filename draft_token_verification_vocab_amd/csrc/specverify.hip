@@ -279,6 +279,7 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     rg.t_logp2 = t_logp2;
     rg.d_lse2 = ds.lse2;
     rg.d_logq2 = ds.logq2;
+    rg.t_am = t_am;
     rg.c = c;
     rg.inv_t = 1.0 / static_cast<double>(p.temperature);
     rg.seed = seed;

@@ -14,7 +14,11 @@
 // split into segments so that small batches still fill the GPU.  Each
 // segment screens keys in float (log2 domain), re-evaluates every candidate
 // within a margin of the segment's best in double, and reports its best
-// double key; a combine kernel takes the best segment.
+// double key; a combine kernel takes the best segment.  The key of the
+// target's top token bounds the row's best from below; since no id's key
+// exceeds its log2 weight by more than 23.5 on the 2^-24 lattice, blocks of
+// ids whose weights cannot reach that bound skip their draws (on peaked rows
+// nearly all of them).
 //
 // FLy (page "Training-Free Loosely Speculative Decoding...", section
 // "2. Metodologia", part A): one thread per sequence scans the flags.
@@ -40,6 +44,7 @@ struct RaceArgs {
     const double *t_logp2;    // [B*K]
     const double *d_lse2;     // [B*K]
     const double *d_logq2;    // [B*K]
+    const int32_t *t_am;      // [B*(K+1)] target top token per row
     float c;                  // log2(e)/T (float, as in the row pass)
     double inv_t;             // 1/T in double
     uint64_t seed;
@@ -72,14 +77,22 @@ __device__ __forceinline__ int decide_lossless(const RaceArgs &a, int b, int L, 
     return s_jstar;
 }
 
+// Largest value -log2(E/ln2) can take on the 2^-24 lattice (u <= 1 - 2^-24
+// gives E/ln2 >= 8.6e-8, i.e. 23.47), rounded up: no id's key exceeds its
+// log2 weight by more.
+constexpr float kMaxNegLogE = 23.5f;
+
 // Race over vectors [v_lo, v_hi) of one row (pair) with NT threads.
 // residual: w = max(0, p - q) from the target and draft rows; otherwise
-// w = p of the target row.  Returns (in thread 0) the best double key and id.
+// w = p of the target row.  floor: a key some id of the row is known to reach
+// (less the margin); ids whose weight cannot bring them within the margin of
+// it skip their Philox draws.  Returns (in thread 0) the best double key and
+// id, or id -1 when no id of the range can win.
 template <typename T, int NT>
 __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo, int v_hi, int V,
                            float c, double cd, double inv_t, double lse2_t, double lse2_d,
-                           PhiloxKey key, uint32_t pos, uint32_t seq, double *out_key,
-                           int *out_x) {
+                           PhiloxKey key, uint32_t pos, uint32_t seq, float floor,
+                           double *out_key, int *out_x) {
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
     constexpr int NW = NT / kWave;
@@ -90,37 +103,49 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     const float lt2 = static_cast<float>(lse2_t);
     const float ld2 = static_cast<float>(lse2_d);
 
-    float best = -__builtin_inff();
+    float best = floor;
     int bx = INT_MAX;
-    for (int vi = v_lo + tid; vi < v_hi; vi += NT) {
-        const uint4 tq = vi < nfull ? tv[vi] : E::partial(trow, vi, V);
-        float xt[EPV], xd[EPV];
+    const int nv = v_hi - v_lo;
+    const int trips = (nv + NT - 1) / NT;  // wave-uniform: the skip test below is a ballot
+    for (int it = 0; it < trips; ++it) {
+        const int vi = v_lo + it * NT + tid;
+        const bool live = vi < v_hi;
+        const int vl = live ? vi : v_lo;
+        const uint4 tq = vl < nfull ? tv[vl] : E::partial(trow, vl, V);
+        float xt[EPV], lw[EPV];
         E::unpack(tq, xt);
         if (residual) {
-            const uint4 dq = vi < nfull ? dv[vi] : E::partial(drow, vi, V);
+            float xd[EPV];
+            const uint4 dq = vl < nfull ? dv[vl] : E::partial(drow, vl, V);
             E::unpack(dq, xd);
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) {
+                const float p = hw_exp2(fmaf(xt[k], c, -lt2));
+                const float qq = hw_exp2(fmaf(xd[k], c, -ld2));
+                const float w = p - qq;
+                lw[k] = w > 0.f ? hw_log2(w) : -__builtin_inff();
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPV; ++k) lw[k] = xt[k] * c;  // log2 p + the row's normaliser
         }
 #pragma unroll
         for (int blk = 0; blk < EPV / 4; ++blk) {
-            const uint32_t base = static_cast<uint32_t>(vi) * EPV + blk * 4;
+            const uint32_t base = static_cast<uint32_t>(vl) * EPV + blk * 4;
+            const float ub = fmaxf(fmaxf(lw[blk * 4], lw[blk * 4 + 1]),
+                                   fmaxf(lw[blk * 4 + 2], lw[blk * 4 + 3])) +
+                             kMaxNegLogE;
+            const bool need = live && ub >= best - kScreenMargin;
+            if (__ballot(need) == 0ull) continue;  // no lane's block can win: no draws
             const uint4 r = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
             const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int k = blk * 4 + q;
                 const float e2 = -hw_log2(lattice_u32f(w4[q]));  // E / ln 2 > 0
-                const float lg = hw_log2(e2);
-                float g;
-                if (residual) {
-                    const float p = hw_exp2(fmaf(xt[k], c, -lt2));
-                    const float qq = hw_exp2(fmaf(xd[k], c, -ld2));
-                    const float w = p - qq;
-                    g = w > 0.f ? hw_log2(w) - lg : -__builtin_inff();
-                } else {
-                    g = xt[k] * c - lg;  // log2 p + log2-normaliser, which all ids share
-                }
+                const float g = lw[k] - hw_log2(e2);
                 const int x = static_cast<int>(base) + q;
-                if (g > best && x < V) {
+                if (live && g > best && x < V) {
                     best = g;
                     bx = x;
                 }
@@ -145,7 +170,7 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     // Double-precision keys of the candidates within the margin.
     double k64 = -__builtin_inf();
     int kx = INT_MAX;
-    if (best > -__builtin_inff() && best >= g1 - kScreenMargin) {
+    if (bx != INT_MAX && best >= g1 - kScreenMargin) {
         const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(bx), pos, seq, kTagRace));
         const double lnE = log(-log(u));
         const double lt = static_cast<double>(E::at(trow, bx));
@@ -191,6 +216,31 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     __syncthreads();
 }
 
+// The key the race gives the target's top token am, less the screening
+// margin: a floor that the row's best key is known to reach.  -inf when am
+// has no weight (then nothing is screened out).
+template <typename T>
+__device__ float race_floor(const T *trow, const T *drow, bool residual, int am, int V, float c,
+                           double lse2_t, double lse2_d, PhiloxKey key, uint32_t pos,
+                           uint32_t seq) {
+    using E = Elem<T>;
+    if (am < 0 || am >= V) return -__builtin_inff();
+    const float xt = E::at(trow, am);
+    float lw;
+    if (residual) {
+        const float p = hw_exp2(fmaf(xt, c, -static_cast<float>(lse2_t)));
+        const float qq = hw_exp2(fmaf(E::at(drow, am), c, -static_cast<float>(lse2_d)));
+        const float w = p - qq;
+        lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
+    } else {
+        lw = xt * c;
+    }
+    if (!(lw > -__builtin_inff())) return -__builtin_inff();
+    const float e2 = -hw_log2(lattice_u32f(draw_u32(key, static_cast<uint32_t>(am), pos, seq,
+                                                    kTagRace)));
+    return lw - hw_log2(e2) - kScreenMargin;
+}
+
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     const int seg = blockIdx.x;
@@ -209,10 +259,12 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
     const int v_lo = seg * a.seg_vecs;
     const int v_hi = min(nvec, v_lo + a.seg_vecs);
+    const float fl = race_floor<T>(trow, drow, residual, a.t_am[b * (a.K + 1) + jstar], a.V, a.c,
+                                   lt, ld, key, jstar, b);
     double k;
     int x;
     race_range<T, NT>(trow, drow, residual, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
-                      a.inv_t, lt, ld, key, jstar, b, &k, &x);
+                      a.inv_t, lt, ld, key, jstar, b, fl, &k, &x);
     if (threadIdx.x == 0) a.cand[b * a.segs + seg] = RaceCand{k, x, jstar};
 }
 
@@ -246,11 +298,14 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
         const T *trow = static_cast<const T *>(a.target) +
                         (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
         const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
+        const double lt = a.t_lse2[b * (a.K + 1) + jstar];
+        const PhiloxKey key = philox_key(a.seed);
+        const float fl = race_floor<T>(trow, nullptr, false, a.t_am[b * (a.K + 1) + jstar], a.V,
+                                       a.c, lt, 0.0, key, jstar, b);
         double k;
         int x;
         race_range<T, NT>(trow, nullptr, false, 0, nvec, a.V, a.c, static_cast<double>(a.c),
-                          a.inv_t, a.t_lse2[b * (a.K + 1) + jstar], 0.0, philox_key(a.seed),
-                          jstar, b, &k, &x);
+                          a.inv_t, lt, 0.0, key, jstar, b, fl, &k, &x);
         if (tid == 0) s_y = x;
         __syncthreads();
     }
