@@ -103,8 +103,10 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
 
     // Thread state.  s, t: sums outside the chunk that holds the maximum;
     // cs, ct: that chunk's sums; saved / itb: that chunk's data and index.
+    // A thread adds a few tens of chunk sums of one sign, so float carries
+    // them to ~1e-6; the sums over threads are formed in double.
     float m = kNoMax, mc = kNoMax * c, cs = 0.f, ct = 0.f;
-    double s = 0.0, t = 0.0;
+    float s = 0.f, t = 0.f;
     int itb = -1;
     uint4 saved[UNROLL];
 #pragma unroll
@@ -156,9 +158,9 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
             // chunk joins the rest, which is rescaled to the new maximum by
             // 2^dl, and this chunk becomes the max chunk.
             const float dl = mc - mcn;
-            const double al = static_cast<double>(hw_exp2(dl));
-            const double stot = s + static_cast<double>(cs);
-            if (ENT) t = al * (t + static_cast<double>(ct) + static_cast<double>(dl) * stot);
+            const float al = hw_exp2(dl);
+            const float stot = s + cs;
+            if (ENT) t = al * (t + ct + dl * stot);
             s = al * stot;
             cs = csum;
             ct = ctsum;
@@ -168,8 +170,8 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) saved[u] = buf[u];
         } else {
-            s += static_cast<double>(csum);
-            if (ENT) t += static_cast<double>(ctsum);
+            s += csum;
+            if (ENT) t += ctsum;
         }
     };
 
@@ -261,8 +263,8 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
                 if (ENT) ot = fmaf(e, d, ot);
             }
         }
-        X = s + static_cast<double>(os);
-        if (ENT) Y = t + static_cast<double>(ot);
+        X = static_cast<double>(s) + static_cast<double>(os);
+        if (ENT) Y = static_cast<double>(t) + static_cast<double>(ot);
     } else {
         const float dl = mc - Mc;
         const double al = static_cast<double>(hw_exp2(dl));
