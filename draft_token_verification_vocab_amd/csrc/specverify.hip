@@ -254,6 +254,7 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     ra.tokens = draft_tokens;
     ra.kept_len = kept_len;
     ra.c = c;
+    ra.inv_ln_v = 1.0 / std::log(static_cast<double>(V));
     const int nrows = ra.nrows0 + (own_draft ? B * K : 0);
     const bool ent0 = !lossless || out->target_entropy != nullptr;
     launch_rows(p.dtype, ra, nrows, ent0, st);
@@ -334,6 +335,7 @@ spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,
     ra.tokens = draft_tokens;
     ra.kept_len = nullptr;
     ra.c = log2e_over(p.temperature);
+    ra.inv_ln_v = 1.0 / std::log(static_cast<double>(p.vocab));
     launch_rows(p.dtype, ra, B * K, false, st);
     if ((s = launch_status()) != SPEC_OK) return s;
     av_score_kernel<<<dim3((B + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock), 0, st>>>(
@@ -549,6 +551,7 @@ spec_status spec_row_stats(const void *logits, int64_t rows, int32_t vocab, int6
     ra.V = vocab;
     ra.K = 1;
     ra.c = log2e_over(temperature);
+    ra.inv_ln_v = 1.0 / std::log(static_cast<double>(vocab));
     launch_rows(dtype, ra, static_cast<int>(rows), entropy != nullptr,
                 static_cast<hipStream_t>(stream));
     return launch_status();

@@ -48,7 +48,10 @@ struct Elem;
 template <>
 struct Elem<uint16_t> {  // bfloat16 bit patterns
     static constexpr int kPerVec = 8;
-    static constexpr uint32_t kNegInfPair = 0xFF80FF80u;
+    // Padding past the row's end: -1.996e30 (bfloat16 0xF1C9), below every
+    // logit the passes take as finite (they treat logits <= -1e30 as -inf)
+    // yet finite, so 2^(pad*c - m*c) is 0 and its entropy term 0 * d is 0.
+    static constexpr uint32_t kPadPair = 0xF1C9F1C9u;
     __device__ static __forceinline__ void unpack(const uint4 &v, float *x) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -66,13 +69,13 @@ struct Elem<uint16_t> {  // bfloat16 bit patterns
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             int e0 = vi * 8 + 2 * i, e1 = e0 + 1;
-            uint32_t lo = e0 < V ? row[e0] : 0xFF80u;
-            uint32_t hi = e1 < V ? row[e1] : 0xFF80u;
+            uint32_t lo = e0 < V ? row[e0] : 0xF1C9u;
+            uint32_t hi = e1 < V ? row[e1] : 0xF1C9u;
             w[i] = lo | (hi << 16);
         }
         return make_uint4(w[0], w[1], w[2], w[3]);
     }
-    static constexpr uint32_t neg_inf_word() { return kNegInfPair; }
+    static constexpr uint32_t pad_word() { return kPadPair; }
 };
 
 template <>
@@ -90,11 +93,11 @@ struct Elem<float> {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             int e = vi * 4 + i;
-            w[i] = e < V ? __float_as_uint(row[e]) : 0xFF800000u;
+            w[i] = e < V ? __float_as_uint(row[e]) : 0xF1C9F2CAu;  // -2e30, as above
         }
         return make_uint4(w[0], w[1], w[2], w[3]);
     }
-    static constexpr uint32_t neg_inf_word() { return 0xFF800000u; }
+    static constexpr uint32_t pad_word() { return 0xF1C9F2CAu; }
 };
 
 // --------------------------------------------------------------------------
@@ -173,6 +176,19 @@ __device__ __forceinline__ uint64_t lane63_u64(uint64_t v) {
     const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), 63);
     const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), 63);
     return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Maximum of an unsigned 32-bit value over the wave (lanes without a DPP
+// source read 0, the identity).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    uint32_t o;
+    o = dpp_pull<0x111, 0xF>(v); v = o > v ? o : v;  // row_shr:1
+    o = dpp_pull<0x112, 0xF>(v); v = o > v ? o : v;  // row_shr:2
+    o = dpp_pull<0x114, 0xF>(v); v = o > v ? o : v;  // row_shr:4
+    o = dpp_pull<0x118, 0xF>(v); v = o > v ? o : v;  // row_shr:8
+    o = dpp_pull<0x142, 0xA>(v); v = o > v ? o : v;  // row_bcast15
+    o = dpp_pull<0x143, 0xC>(v); v = o > v ? o : v;  // row_bcast31
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Maximum of an unsigned 64-bit key over the wave.

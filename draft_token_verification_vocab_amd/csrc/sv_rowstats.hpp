@@ -60,6 +60,8 @@ struct RowArgs {
     const int32_t *tokens;    // [B][K] or null
     const int32_t *kept_len;  // [B] or null
     float c;                  // log2(e) / T
+    float pad2_;
+    double inv_ln_v;          // 1 / ln V
 };
 
 template <typename T, int BLOCK, int UNROLL, bool ENT>
@@ -102,15 +104,14 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     const uint4 *vrow = reinterpret_cast<const uint4 *>(rp);
 
     // Thread state.  s, t: sums outside the chunk that holds the maximum;
-    // cs, ct: that chunk's sums; saved / itb: that chunk's data and index.
+    // cs, ct: that chunk's sums; itb: its index.  Its raw data is kept in
+    // LDS (sh_saved), out of the registers.
     // A thread adds a few tens of chunk sums of one sign, so float carries
     // them to ~1e-6; the sums over threads are formed in double.
     float m = kNoMax, mc = kNoMax * c, cs = 0.f, ct = 0.f;
     float s = 0.f, t = 0.f;
     int itb = -1;
-    uint4 saved[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) saved[u] = make_uint4(0u, 0u, 0u, 0u);
+    __shared__ uint4 sh_saved[UNROLL][BLOCK];
 
     // it: the chunk's index; thread tid's chunk `it` starts at vector
     // it*UNROLL*BLOCK + tid.
@@ -168,7 +169,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
             mc = mcn;
             itb = it;
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) saved[u] = buf[u];
+            for (int u = 0; u < UNROLL; ++u) sh_saved[u][tid] = buf[u];
         } else {
             s += csum;
             if (ENT) t += ctsum;
@@ -180,29 +181,28 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     constexpr int kChunkVecs = UNROLL * BLOCK;
     const int nit = nfull / kChunkVecs;
     // The next chunk's loads are issued before this chunk's arithmetic, so
-    // every wave keeps a chunk in flight while it computes.
-    uint4 nxt[UNROLL];
-    if (nit > 0) {
+    // every wave keeps a chunk in flight while it computes; two register
+    // buffers take turns (no copies).
+    auto load_chunk = [&](uint4 (&buf)[UNROLL], int it) {
+        const uint4 *cp = vrow + static_cast<int64_t>(it) * kChunkVecs;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            nxt[u] = load_stream_at(vrow, static_cast<uint32_t>(tid + u * BLOCK) * 16u);
+            buf[u] = load_stream_at(cp, static_cast<uint32_t>(tid + u * BLOCK) * 16u);
+    };
+    uint4 bufA[UNROLL], bufB[UNROLL];
+    if (nit > 0) load_chunk(bufA, 0);
+    int it = 0;
+    for (; it + 1 < nit; it += 2) {
+        load_chunk(bufB, it + 1);
+        consume(bufA, it);
+        if (it + 2 < nit) load_chunk(bufA, it + 2);
+        consume(bufB, it + 1);
     }
-    for (int it = 0; it < nit; ++it) {
-        uint4 buf[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) buf[u] = nxt[u];
-        if (it + 1 < nit) {
-            const uint4 *cp = vrow + static_cast<int64_t>(it + 1) * kChunkVecs;
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-                nxt[u] = load_stream_at(cp, static_cast<uint32_t>(tid + u * BLOCK) * 16u);
-        }
-        consume(buf, it);
-    }
+    if (it < nit) consume(bufA, it);
     const int v = nit * kChunkVecs + tid;
     if (v < nvec) {  // the last, partly filled chunk of this thread
         uint4 buf[UNROLL];
-        const uint32_t ni = E::neg_inf_word();
+        const uint32_t ni = E::pad_word();
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int vi = v + u * BLOCK;
@@ -216,33 +216,38 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
         consume(buf, nit);
     }
 
-    // First id attaining the thread maximum (element order inside the saved
-    // chunk: vector u-major, lane k-minor).
+    // (1) Row maximum M (a 32-bit max of the ordered bits), then its first
+    // id: only threads whose maximum is M search their max chunk (element
+    // order inside it: vector u-major, lane k-minor), and the lowest id wins.
+    __shared__ uint32_t sh_m[NW], sh_p[NW];
+    __shared__ double sh_s[NW], sh_t[NW];
+    const int lane = tid & (kWave - 1), wv = tid / kWave;
+    const uint32_t om = ordered_bits(m);
+    const uint32_t wm = wave_max_u32(om);
+    if (lane == 0) sh_m[wv] = wm;
+    __syncthreads();
+    uint32_t bm = sh_m[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) bm = sh_m[w] > bm ? sh_m[w] : bm;
+    const float M = from_ordered_bits(bm);
     const int v0b = itb < 0 ? -1 : itb * kChunkVecs + tid;  // first vector of the max chunk
     float xs[N];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) E::unpack(saved[u], xs + u * EPV);
     int pos = INT_MAX;
-    if (v0b >= 0) {
+    if (om == bm && v0b >= 0) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) E::unpack(sh_saved[u][tid], xs + u * EPV);
 #pragma unroll
         for (int k = N - 1; k >= 0; --k)
             if (xs[k] == m) pos = (v0b + (k / EPV) * BLOCK) * EPV + (k % EPV);
     }
-
-    // (1) Row maximum and its first id in one key: (ordered max, -id).
-    __shared__ uint64_t sh_key[NW];
-    __shared__ double sh_s[NW], sh_t[NW];
-    const int lane = tid & (kWave - 1), wv = tid / kWave;
-    const uint64_t key =
-        (static_cast<uint64_t>(ordered_bits(m)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(pos));
-    const uint64_t wkey = wave_max_u64(key);
-    if (lane == 0) sh_key[wv] = wkey;
+    // lowest id = largest complement; no candidate leaves ~INT_MAX
+    const uint32_t wp = wave_max_u32(~static_cast<uint32_t>(pos));
+    if (lane == 0) sh_p[wv] = wp;
     __syncthreads();
-    uint64_t bkey = sh_key[0];
+    uint32_t bp = sh_p[0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) bkey = sh_key[w] > bkey ? sh_key[w] : bkey;
-    const float M = from_ordered_bits(static_cast<uint32_t>(bkey >> 32));
-    const int P = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(bkey));
+    for (int w = 1; w < NW; ++w) bp = sh_p[w] > bp ? sh_p[w] : bp;
+    const int P = static_cast<int>(~bp);
     const float Mc = M * c;
 
     // (2) Every thread rescales its sums to M.  The thread holding the
@@ -303,16 +308,20 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
             // H = ln(sum) - ln2 * (sum of term*exponent) / sum, rewritten
             // around the argmax term: H = ln(1 + rho) + ln2 (r0 r - t_o) / (2^r0 + r).
             const double H = l1p + kLn2 * (r0 * r - to) / (e0 + r);
-            const float h = static_cast<float>(H / log(static_cast<double>(V)));
+            const float h = static_cast<float>(H * a.inv_ln_v);
             if (g.entropy) g.entropy[row] = h;
             if (g.h_int) g.h_int[row] = h;
         }
-        const float qm = static_cast<float>(1.0 / (1.0 + rho));
-        const float ft = static_cast<float>(-log(fmax(rho, 0x1.0p-126)));  // logit(q_max)
-        if (g.qmax) g.qmax[row] = qm;
-        if (g.qmax_int) g.qmax_int[row] = qm;
-        if (g.feat) g.feat[row] = ft;
-        if (g.feat_int) g.feat_int[row] = ft;
+        if (g.qmax || g.qmax_int) {
+            const float qm = static_cast<float>(1.0 / (1.0 + rho));
+            if (g.qmax) g.qmax[row] = qm;
+            if (g.qmax_int) g.qmax_int[row] = qm;
+        }
+        if (g.feat || g.feat_int) {
+            const float ft = static_cast<float>(-log(fmax(rho, 0x1.0p-126)));  // logit(q_max)
+            if (g.feat) g.feat[row] = ft;
+            if (g.feat_int) g.feat_int[row] = ft;
+        }
         if (gather && g.logtok2)
             g.logtok2[gidx] = static_cast<double>(ltok) * static_cast<double>(c) - lse2;
     }
