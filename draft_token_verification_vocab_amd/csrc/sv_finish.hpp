@@ -107,16 +107,25 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     int bx = INT_MAX;
     const int nv = v_hi - v_lo;
     const int trips = (nv + NT - 1) / NT;  // wave-uniform: the skip test below is a ballot
+    // The next trip's vectors are loaded before this trip's arithmetic.
+    auto fetch = [&](int it, uint4 &tq, uint4 &dq) {
+        const int vi = v_lo + it * NT + tid;
+        const int vl = vi < v_hi ? vi : v_lo;
+        tq = vl < nfull ? load_stream(tv + vl) : E::partial(trow, vl, V);
+        if (residual) dq = vl < nfull ? load_stream(dv + vl) : E::partial(drow, vl, V);
+    };
+    uint4 tn = make_uint4(0u, 0u, 0u, 0u), dn = tn;
+    if (trips > 0) fetch(0, tn, dn);
     for (int it = 0; it < trips; ++it) {
         const int vi = v_lo + it * NT + tid;
         const bool live = vi < v_hi;
         const int vl = live ? vi : v_lo;
-        const uint4 tq = vl < nfull ? tv[vl] : E::partial(trow, vl, V);
+        const uint4 tq = tn, dq = dn;
+        if (it + 1 < trips) fetch(it + 1, tn, dn);
         float xt[EPV], lw[EPV];
         E::unpack(tq, xt);
         if (residual) {
             float xd[EPV];
-            const uint4 dq = vl < nfull ? dv[vl] : E::partial(drow, vl, V);
             E::unpack(dq, xd);
 #pragma unroll
             for (int k = 0; k < EPV; ++k) {
