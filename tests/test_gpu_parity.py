@@ -192,6 +192,15 @@ def test_lossless_c0_full_size():
         _lossless_check(batch, seed=s)
 
 
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_lossless_workloads_full_size(cfg):
+    # the benchmarked lossless workloads at their full sizes, every output
+    # checked: B=64 K=5 V=128256, and B=512 K=4 V=152064 at T=0.7
+    batch = W.make(cfg, device=DEV)
+    _, o, nm, nb = _lossless_check(batch, seed=0)
+    assert batch.tokens.shape[0] == W.CONFIGS[cfg]["B"]
+
+
 @pytest.mark.parametrize("cfg,B,K,V,stride", [(1, 12, 5, 128256, 128256), (3, 12, 4, 152064, 152064),
                                               (1, 16, 3, 7001, 7008), (0, 32, 4, 32000, 32000),
                                               (3, 8, 2, 1003, 1008)])
@@ -278,6 +287,18 @@ def test_av_score_update_parity_c1_recipe():
     got, want, _, okept = _av_step(batch, ob0, tau=0.0, lr=0.05, seed=0)
     assert np.all(okept == 5)
     assert np.allclose(got, want, rtol=0, atol=1e-5), (got, want)
+
+
+def test_av_pipeline_full_size_steps():
+    # the B=1024 K=8 adaptive-verification pipeline at full size, three steps
+    # with fresh inputs, parameters carried over as the pipeline does
+    ob = W.av_init(4)
+    for step in range(3):
+        batch = W.make(4, device=DEV, step=step)
+        got, want, o, okept = _av_step(batch, ob, tau=0.2, lr=0.05, seed=step)
+        assert batch.tokens.shape[0] == 1024
+        assert np.allclose(got, want, rtol=0, atol=1e-5), (step, got, want)
+        ob = got.tolist()
 
 
 def test_av_pipeline_c4_recipe_steps():
