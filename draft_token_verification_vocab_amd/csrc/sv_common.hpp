@@ -120,8 +120,11 @@ __device__ __forceinline__ uint4 philox10(uint4 c, PhiloxKey k) {
     for (int r = 0; r < 10; ++r) {
         const uint64_t a = static_cast<uint64_t>(0xD2511F53u) * c.x;
         const uint64_t b = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
-        c = make_uint4(static_cast<uint32_t>(b >> 32) ^ c.y ^ k0, static_cast<uint32_t>(b),
-                       static_cast<uint32_t>(a >> 32) ^ c.w ^ k1, static_cast<uint32_t>(a));
+        // three-input XORs in one instruction each (truth table 0x96: odd parity)
+        c = make_uint4(__builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(b >> 32), c.y, k0, 0x96),
+                       static_cast<uint32_t>(b),
+                       __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(a >> 32), c.w, k1, 0x96),
+                       static_cast<uint32_t>(a));
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
