@@ -21,7 +21,8 @@
 // nearly all of them).
 //
 // FLy (page "Training-Free Loosely Speculative Decoding...", section
-// "2. Metodologia", part A): one thread per sequence scans the flags.
+// "2. Metodologia", part A): one wave per sequence; deviations and gate
+// passes are two ballots and the scan walks those bit masks.
 #pragma once
 
 #include "sv_common.hpp"

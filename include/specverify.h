@@ -25,8 +25,10 @@
  *    base + r*row_stride elements.  dtype SPEC_DTYPE_F32 (float) or
  *    SPEC_DTYPE_BF16 (bfloat16 bit patterns).  The base pointer must be
  *    16-byte aligned and row_stride*sizeof(element) a multiple of 16.
- *    Logits must be finite or -inf (a masked vocabulary entry); +inf and NaN
- *    are not supported.  At least one entry per row must be finite.
+ *    Logits must be -inf (a masked vocabulary entry) or finite and greater
+ *    than -1e30 (the passes treat values at or below -1e30 as "no maximum
+ *    yet"); +inf and NaN are not supported.  At least one entry per row must
+ *    be finite.
  *  - Every statistic is of the temperature-scaled distribution softmax(l/T).
  *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *    the null stream).  Arguments are validated on the host before anything
