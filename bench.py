@@ -43,6 +43,7 @@ ROW_PASS_SOURCES = ["draft_token_verification_vocab_amd/csrc/sv_rowstats.hpp",
                     "draft_token_verification_vocab_amd/csrc/sv_common.hpp",
                     "draft_token_verification_vocab_amd/csrc/specverify.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_pass_fly_b256_k8_v128256_bf16.traffic.json")
+VALU_FILE = os.path.join(ROOT, "profiles", "row_pass_valu_fly_b256_k8_v128256_bf16.json")
 
 
 def row_pass_source_hash() -> str:
@@ -199,11 +200,18 @@ def main():
             tr = json.load(f)
         if tr.get("source_hash") == row_pass_source_hash():
             traffic = tr.get("bytes_per_launch")
+    valu = None  # VALU counters recorded for the same kernel source
+    if os.path.exists(VALU_FILE):
+        with open(VALU_FILE) as f:
+            va = json.load(f)
+        if va.get("source_hash") == row_pass_source_hash():
+            valu = {k: va[k] for k in ("valu_insts_per_logit", "valu_busy_frac")}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": "row_stats_kernel<bf16,512,2,entropy>", "kernel_us": round(kms * 1e3, 2),
                 "algorithmic_bytes_per_launch": bytes_per_step,
                 "evented_launch_us_p10_p50_p90": _pcts(launch_us),
+                "valu": valu,
                 "source_hash": row_pass_source_hash()}
     log("row pass: %.1f us/launch, %.0f GB/s (%.1f%% of peak)" % (kms * 1e3, achieved,
                                                                   100 * achieved / HBM_PEAK_GBPS))
@@ -455,10 +463,17 @@ def cpu_baseline(batch, cfg, budget_s):
         total += time.perf_counter() - t
         reps += 1
     rows = n * (cfg["K"] + 1)
+    # one thread on a smaller sample, for scale
+    n1 = max(1, min(Btot, n // max(threads, 1)))
+    t = time.perf_counter()
+    ref.verify(tgt[:n1], None, tok[:n1], 0, ref.MODE_FLY, theta=cfg["theta"],
+               window=cfg["window"], nthreads=1)
+    dt1 = time.perf_counter() - t
     return {"value": round(rows * reps / total, 1), "unit": "rows/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d of %d sequences (%d target rows) of %s, FLy mode, %d pass(es), %.1f s"
-                      % (n, Btot, rows, cfg["name"], reps, total)}
+                      % (n, Btot, rows, cfg["name"], reps, total),
+            "single_thread_rows_per_s": round(n1 * (cfg["K"] + 1) / dt1, 1)}
 
 
 if __name__ == "__main__":
