@@ -286,16 +286,31 @@ def run_secondary(sv, W, dev, stream, args):
     b1 = W.gaussian(256, 8, 128256, "bf16", 1.0, seed=78, token_seed=1, device=dev)
     bs = [b0, b1]
     ws = torch.empty(sv.workspace_bytes(256, 8, 128256), dtype=torch.uint8, device=dev)
-    res = [None, None]
+    calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws) for b in bs]
+    res = [c.out for c in calls]
 
     def f(i):
-        b = bs[i % 2]
-        res[i % 2] = sv.verify(b.target, b.draft, b.tokens, seed=i, workspace=ws)
+        calls[i % 2](i)
     ms = _timeit(f, n, 2, stream, torch)
     rows = 256 * 17
     byt = rows * 128256 * 2
     out["lossless_b256_k8_v128256_bf16"] = _line(ms, rows, byt, res)
     del bs, b0, b1
+
+    # c0: lossless, B=1 K=4 V=32000 float32 (latency: a handful of rows)
+    c = W.CONFIGS[0]
+    sets = [W.make(0, device=dev, step=s) for s in range(4)]
+    ws0 = torch.empty(sv.workspace_bytes(1, c["K"], c["V"], dtype=sv.DTYPE_F32), dtype=torch.uint8,
+                      device=dev)
+    calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws0) for b in sets]
+    res = [c.out for c in calls]
+
+    def f0(i):
+        calls[i % 4](i)
+    ms = _timeit(f0, n, 2, stream, torch)
+    rows = 2 * c["K"] + 1
+    out[c["name"]] = _line(ms, rows, rows * c["V"] * 4, res)
+    del sets
 
     # c1: lossless + AV score + one SGD step, B=64 K=5
     c = W.CONFIGS[1]
@@ -303,15 +318,12 @@ def run_secondary(sv, W, dev, stream, args):
     K = c["K"]
     ob = torch.tensor(W.av_init(1), dtype=torch.float32, device=dev)
     ws1 = torch.empty(sv.workspace_bytes(64, K, c["V"]), dtype=torch.uint8, device=dev)
-    res = [None] * 4
+    calls = [sv.AvStepCall(b.target, b.draft, b.tokens, ob, c["av"]["tau"], c["av"]["lr"],
+                           workspace=ws1) for b in sets]
+    res = [cl.verify.out for cl in calls]
 
     def f1(i):
-        b = sets[i % 4]
-        conf, mask, kept, ds = sv.av_score(b.draft, b.tokens, ob, c["av"]["tau"])
-        r = sv.verify(b.target, b.draft, b.tokens, seed=0, kept_len=kept, draft_stats=ds,
-                      workspace=ws1)
-        sv.av_update(ds, r.accepted_len, kept, ob, c["av"]["lr"], 64, K)
-        res[i % 4] = r
+        calls[i % 4](0)
     ms = _timeit(f1, n, 2, stream, torch)
     rows = 64 * (2 * K + 1)
     out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
@@ -322,12 +334,12 @@ def run_secondary(sv, W, dev, stream, args):
     sets = [W.make(3, device=dev, step=s) for s in range(2)]
     ws3 = torch.empty(sv.workspace_bytes(512, 4, c["V"], temperature=0.7), dtype=torch.uint8,
                       device=dev)
-    res = [None] * 2
+    calls = [sv.VerifyCall(b.target, b.draft, b.tokens, temperature=0.7, workspace=ws3)
+             for b in sets]
+    res = [c.out for c in calls]
 
     def f3(i):
-        b = sets[i % 2]
-        res[i % 2] = sv.verify(b.target, b.draft, b.tokens, seed=0, temperature=0.7,
-                               workspace=ws3)
+        calls[i % 2](0)
     ms = _timeit(f3, n, 2, stream, torch)
     rows = 512 * 9
     out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
@@ -339,20 +351,16 @@ def run_secondary(sv, W, dev, stream, args):
     K = c["K"]
     ob = torch.tensor(W.av_init(4), dtype=torch.float32, device=dev)
     ws4 = torch.empty(sv.workspace_bytes(1024, K, c["V"]), dtype=torch.uint8, device=dev)
-    res = [None] * 2
-    kept_hist = []
+    calls = [sv.AvStepCall(b.target, b.draft, b.tokens, ob, c["av"]["tau"], c["av"]["lr"],
+                           workspace=ws4) for b in sets]
+    res = [cl.verify.out for cl in calls]
 
     def f4(i):
-        b = sets[i % 2]
-        conf, mask, kept, ds = sv.av_score(b.draft, b.tokens, ob, c["av"]["tau"])
-        r = sv.verify(b.target, b.draft, b.tokens, seed=i, kept_len=kept, draft_stats=ds,
-                      workspace=ws4)
-        sv.av_update(ds, r.accepted_len, kept, ob, c["av"]["lr"], 1024, K)
-        res[i % 2] = r
-        kept_hist.append(kept)
+        calls[i % 2](i)
     ms = _timeit(f4, c["steps"], 2, stream, torch)
-    kept_all = torch.stack(kept_hist[-c["steps"]:]).float()
-    rows = 1024 * K + int((kept_all + 1).sum().item() / c["steps"])
+    # kept lengths of the last step on each input set
+    kept_all = torch.stack([cl.kept for cl in calls]).float()
+    rows = 1024 * K + int((kept_all + 1).sum().item() / len(calls))
     line = _line(ms, rows, rows * c["V"] * 2, res)
     line["mean_kept_len"] = round(float(kept_all.mean().item()), 4)
     line["omega_beta_after"] = [round(v, 5) for v in ob.tolist()]

@@ -213,6 +213,47 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
     return out
 
 
+class VerifyCall:
+    """A verification call with its arguments marshalled once, for loops that
+    verify the same buffers again and again (a serving step, a benchmark):
+    calling it only sets the seed and enqueues spec_verify on the stream that
+    was current at construction.  The tensors must stay alive and in place."""
+
+    def __init__(self, target: torch.Tensor, draft: Optional[torch.Tensor],
+                 draft_tokens: torch.Tensor, mode: int = MODE_LOSSLESS, *,
+                 temperature: float = 1.0, fly_theta: float = 0.3, fly_window: int = 4,
+                 kept_len: Optional[torch.Tensor] = None,
+                 draft_stats: Optional[torch.Tensor] = None, vocab: Optional[int] = None,
+                 out: Optional[VerifyResult] = None, workspace: Optional[torch.Tensor] = None):
+        _need_cuda(target, "target")
+        B, K1, S = target.shape
+        K = K1 - 1
+        V = S if vocab is None else int(vocab)
+        dev = target.device
+        self.L = load()
+        self.params = _params(B, K, V, S, _dtype_code(target), temperature, fly_theta,
+                              fly_window)
+        if out is None:
+            out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                               torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+        self.out = out
+        self.vout = _VerifyOut(*[None if t is None else t.data_ptr() for t in (
+            out.accepted_len, out.tokens, out.target_lse, out.target_entropy, out.target_argmax,
+            out.draft_lse, out.draft_qmax, out.draft_feat)])
+        need = int(self.L.spec_workspace_bytes(ctypes.byref(self.params)))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self._keep = (target, draft, draft_tokens, kept_len, draft_stats, workspace)
+        self.args = [_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(kept_len),
+                     _ptr(draft_stats), ctypes.c_uint64(0), int(mode), ctypes.byref(self.params),
+                     ctypes.byref(self.vout), _ptr(workspace), workspace.numel(), _stream(dev)]
+
+    def __call__(self, seed: int = 0) -> VerifyResult:
+        self.args[5] = ctypes.c_uint64(int(seed) & (2**64 - 1))
+        _check(self.L.spec_verify(*self.args), "spec_verify")
+        return self.out
+
+
 def av_score(draft: torch.Tensor, draft_tokens: torch.Tensor, omega_beta: torch.Tensor,
              tau: float, *, temperature: float = 1.0, vocab: Optional[int] = None,
              draft_stats: Optional[torch.Tensor] = None):
@@ -240,6 +281,47 @@ def av_score(draft: torch.Tensor, draft_tokens: torch.Tensor, omega_beta: torch.
                            float(tau), _ptr(conf), _ptr(mask), _ptr(kept), _ptr(draft_stats),
                            _stream(dev)), "spec_av_score")
     return conf, mask, kept, draft_stats
+
+
+class AvStepCall:
+    """One adaptive-verification step (score and trim, verify, SGD update)
+    with its arguments marshalled once and its buffers allocated once: the
+    buffers of one batch of draft and target logits, verified again and again
+    (a serving loop that refills them in place, a benchmark).  Calling it
+    enqueues spec_av_score, spec_verify and spec_av_update on the stream that
+    was current at construction; omega_beta is updated in place."""
+
+    def __init__(self, target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                 omega_beta: torch.Tensor, tau: float, lr: float, *, temperature: float = 1.0,
+                 vocab: Optional[int] = None, workspace: Optional[torch.Tensor] = None):
+        _need_cuda(draft, "draft")
+        B, K, S = draft.shape
+        V = S if vocab is None else int(vocab)
+        dev = draft.device
+        L = load()
+        self.L = L
+        self.conf = torch.empty(B, K, dtype=torch.float32, device=dev)
+        self.mask = torch.empty(B, K, dtype=torch.uint8, device=dev)
+        self.kept = torch.empty(B, dtype=torch.int32, device=dev)
+        self.stats = torch.empty(max(int(L.spec_draft_stats_bytes(B, K)), 16), dtype=torch.uint8,
+                                 device=dev)
+        self.params = _params(B, K, V, S, _dtype_code(draft), temperature)
+        st = _stream(dev)
+        self.score_args = (_ptr(draft), _ptr(draft_tokens), ctypes.byref(self.params),
+                           _ptr(omega_beta), float(tau), _ptr(self.conf), _ptr(self.mask),
+                           _ptr(self.kept), _ptr(self.stats), st)
+        self.verify = VerifyCall(target, draft, draft_tokens, temperature=temperature,
+                                 kept_len=self.kept, draft_stats=self.stats, vocab=vocab,
+                                 workspace=workspace)
+        self.update_args = (_ptr(self.stats), _ptr(self.verify.out.accepted_len),
+                            _ptr(self.kept), int(B), int(K), float(lr), _ptr(omega_beta), st)
+        self._keep = (target, draft, draft_tokens, omega_beta)
+
+    def __call__(self, seed: int = 0) -> VerifyResult:
+        _check(self.L.spec_av_score(*self.score_args), "spec_av_score")
+        r = self.verify(seed)
+        _check(self.L.spec_av_update(*self.update_args), "spec_av_update")
+        return r
 
 
 def draft_stats_view(draft_stats: torch.Tensor, B: int, K: int):
