@@ -382,7 +382,7 @@ def run_next_rows(sv, W, dev, stream, args):
     B, K = 1024, 8
     g = torch.Generator(device="cpu").manual_seed(4242)
     feat = (torch.randn(B, K, generator=g) * 1.3 - 1.2).to(dev)
-    ds = torch.zeros(24 * B * K, dtype=torch.uint8, device=dev)
+    ds = torch.zeros(sv.draft_stats_bytes(B, K), dtype=torch.uint8, device=dev)
     sv.draft_stats_view(ds, B, K)["feat"].copy_(feat.view(-1))
     kept = torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev)
     acc = torch.minimum(torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(dev),

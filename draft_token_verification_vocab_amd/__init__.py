@@ -274,9 +274,11 @@ def av_score(draft: torch.Tensor, draft_tokens: torch.Tensor, omega_beta: torch.
     conf = torch.empty(B, K, dtype=torch.float32, device=dev)
     mask = torch.empty(B, K, dtype=torch.uint8, device=dev)
     kept = torch.empty(B, dtype=torch.int32, device=dev)
+    need = int(L.spec_draft_stats_bytes(B, K))
     if draft_stats is None:
-        draft_stats = torch.empty(max(int(L.spec_draft_stats_bytes(B, K)), 16),
-                                  dtype=torch.uint8, device=dev)
+        draft_stats = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif draft_stats.numel() * draft_stats.element_size() < need:
+        raise ValueError("draft_stats must hold spec_draft_stats_bytes(B, K) = %d bytes" % need)
     _check(L.spec_av_score(_ptr(draft), _ptr(draft_tokens), ctypes.byref(p), _ptr(omega_beta),
                            float(tau), _ptr(conf), _ptr(mask), _ptr(kept), _ptr(draft_stats),
                            _stream(dev)), "spec_av_score")

@@ -64,6 +64,64 @@ struct RowArgs {
     double inv_ln_v;          // 1 / ln V
 };
 
+// Row j of sequence b is not read when adaptive verification trimmed it.
+__device__ __forceinline__ bool row_trimmed(const RowArgs &a, const RowGroup &g, int b, int j) {
+    return a.kept_len && j >= clamp_len(a.kept_len[b], a.K) + g.active_extra;
+}
+
+// What a row that was not read reports.
+__device__ __forceinline__ void write_unread(const RowGroup &g, int64_t row) {
+    const float nan = __builtin_nanf("");
+    if (g.lse) g.lse[row] = nan;
+    if (g.entropy) g.entropy[row] = nan;
+    if (g.argmax) g.argmax[row] = -1;
+    if (g.qmax) g.qmax[row] = nan;
+    if (g.feat) g.feat[row] = nan;
+}
+
+// The row's results from its maximum M, the first id P attaining it (INT_MAX
+// when none), the sum r of 2^(l*c - Mc) over the other ids (Mc = M*c rounded
+// to float) and the matching sum `to` of term * exponent.
+template <bool ENT>
+__device__ __forceinline__ void row_emit(const RowArgs &a, const RowGroup &g, int64_t row, float M,
+                                         int P, double r, double to, bool gather, int gidx,
+                                         float ltok) {
+    const float c = a.c;
+    const float Mc = M * c;
+    // The argmax term is 2^r0 with r0 = M*c - Mc, the rounding residue of Mc
+    // (exact in float); the row's sum of terms is 2^r0 + r.
+    const double r0 = static_cast<double>(fmaf(M, c, -Mc));
+    const double e0 = exp2(r0);
+    const double rho = r / e0;      // (1 - q_max) / q_max
+    const double l1p = log1p(rho);  // ln(sum / 2^r0)
+    const double lse2 = static_cast<double>(Mc) + r0 + l1p * kLog2eD;
+    if (g.lse2) g.lse2[row] = lse2;
+    if (g.lse) g.lse[row] = static_cast<float>(lse2 * kLn2);
+    const int am = P == INT_MAX ? -1 : P;
+    if (g.argmax) g.argmax[row] = am;
+    if (g.am_int) g.am_int[row] = am;
+    if (ENT) {
+        // H = ln(sum) - ln2 * (sum of term*exponent) / sum, rewritten around
+        // the argmax term: H = ln(1 + rho) + ln2 (r0 r - t_o) / (2^r0 + r).
+        const double H = l1p + kLn2 * (r0 * r - to) / (e0 + r);
+        const float h = static_cast<float>(H * a.inv_ln_v);
+        if (g.entropy) g.entropy[row] = h;
+        if (g.h_int) g.h_int[row] = h;
+    }
+    if (g.qmax || g.qmax_int) {
+        const float qm = static_cast<float>(1.0 / (1.0 + rho));
+        if (g.qmax) g.qmax[row] = qm;
+        if (g.qmax_int) g.qmax_int[row] = qm;
+    }
+    if (g.feat || g.feat_int) {
+        const float ft = static_cast<float>(-log(fmax(rho, 0x1.0p-126)));  // logit(q_max)
+        if (g.feat) g.feat[row] = ft;
+        if (g.feat_int) g.feat_int[row] = ft;
+    }
+    if (gather && g.logtok2)
+        g.logtok2[gidx] = static_cast<double>(ltok) * static_cast<double>(c) - lse2;
+}
+
 template <typename T, int BLOCK, int UNROLL, bool ENT>
 __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int64_t row) {
     using E = Elem<T>;
@@ -76,19 +134,9 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
 
     const int b = static_cast<int>(row / g.rows_per_seq);
     const int j = static_cast<int>(row - static_cast<int64_t>(b) * g.rows_per_seq);
-    if (a.kept_len) {
-        const int L = clamp_len(a.kept_len[b], a.K);
-        if (j >= L + g.active_extra) {  // trimmed away: report "not read"
-            if (tid == 0) {
-                const float nan = __builtin_nanf("");
-                if (g.lse) g.lse[row] = nan;
-                if (g.entropy) g.entropy[row] = nan;
-                if (g.argmax) g.argmax[row] = -1;
-                if (g.qmax) g.qmax[row] = nan;
-                if (g.feat) g.feat[row] = nan;
-            }
-            return;
-        }
+    if (row_trimmed(a, g, b, j)) {  // report "not read"
+        if (tid == 0) write_unread(g, row);
+        return;
     }
     const T *rp = static_cast<const T *>(g.base) + row * g.stride;
     const bool gather = a.tokens != nullptr && j < g.gather_rows;
@@ -222,7 +270,9 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     __shared__ uint32_t sh_m[NW], sh_p[NW];
     __shared__ double sh_s[NW], sh_t[NW];
     const int lane = tid & (kWave - 1), wv = tid / kWave;
-    const uint32_t om = ordered_bits(m);
+    // m + 0 turns -0 into +0, so that a row maximum of zero is one key and
+    // its first id is the lowest of every zero, whatever its sign.
+    const uint32_t om = ordered_bits(m + 0.0f);
     const uint32_t wm = wave_max_u32(om);
     if (lane == 0) sh_m[wv] = wm;
     __syncthreads();
@@ -292,38 +342,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
             r += sh_s[w];
             to += sh_t[w];
         }
-        // The argmax term is 2^r0 with r0 = M*c - Mc, the rounding residue of
-        // Mc (exact in float); the row's sum of terms is 2^r0 + r.
-        const double r0 = static_cast<double>(fmaf(M, c, -Mc));
-        const double e0 = exp2(r0);
-        const double rho = r / e0;      // (1 - q_max) / q_max
-        const double l1p = log1p(rho);  // ln(sum / 2^r0)
-        const double lse2 = static_cast<double>(Mc) + r0 + l1p * kLog2eD;
-        if (g.lse2) g.lse2[row] = lse2;
-        if (g.lse) g.lse[row] = static_cast<float>(lse2 * kLn2);
-        const int am = P == INT_MAX ? -1 : P;
-        if (g.argmax) g.argmax[row] = am;
-        if (g.am_int) g.am_int[row] = am;
-        if (ENT) {
-            // H = ln(sum) - ln2 * (sum of term*exponent) / sum, rewritten
-            // around the argmax term: H = ln(1 + rho) + ln2 (r0 r - t_o) / (2^r0 + r).
-            const double H = l1p + kLn2 * (r0 * r - to) / (e0 + r);
-            const float h = static_cast<float>(H * a.inv_ln_v);
-            if (g.entropy) g.entropy[row] = h;
-            if (g.h_int) g.h_int[row] = h;
-        }
-        if (g.qmax || g.qmax_int) {
-            const float qm = static_cast<float>(1.0 / (1.0 + rho));
-            if (g.qmax) g.qmax[row] = qm;
-            if (g.qmax_int) g.qmax_int[row] = qm;
-        }
-        if (g.feat || g.feat_int) {
-            const float ft = static_cast<float>(-log(fmax(rho, 0x1.0p-126)));  // logit(q_max)
-            if (g.feat) g.feat[row] = ft;
-            if (g.feat_int) g.feat_int[row] = ft;
-        }
-        if (gather && g.logtok2)
-            g.logtok2[gidx] = static_cast<double>(ltok) * static_cast<double>(c) - lse2;
+        row_emit<ENT>(a, g, row, M, P, r, to, gather, gidx, ltok);
     }
 }
 

@@ -38,7 +38,7 @@ def _label_batch(rng, B, K, feat_const=None):
 
 def _device_stats(feat):
     B, K = feat.shape
-    ds = torch.zeros(24 * B * K, dtype=torch.uint8, device=DEV)
+    ds = torch.zeros(sv.draft_stats_bytes(B, K), dtype=torch.uint8, device=DEV)
     sv.draft_stats_view(ds, B, K)["feat"].copy_(torch.from_numpy(feat.ravel()))
     return ds
 

@@ -68,13 +68,21 @@ def test_row_stats_parity(dtype, V, stride, T):
 
 
 def test_row_stats_reproducible_and_ordered_ties():
-    x = torch.zeros(3, 40000, device=DEV, dtype=torch.bfloat16)
+    x = torch.zeros(5, 40000, device=DEV, dtype=torch.bfloat16)
     x[0, [39999, 12345, 20000]] = 1.0
     x[1, 1] = -1.0
+    # a maximum of zero held by -0 and +0: one value, so the lowest id wins
+    # whatever its sign (ids held by different threads and chunks)
+    x[3] = -1.0
+    x[3, [7, 30001]] = torch.tensor([-0.0, 0.0], dtype=torch.bfloat16, device=DEV)
+    x[4] = -1.0
+    x[4, [5, 17, 39000]] = torch.tensor([0.0, -0.0, -0.0], dtype=torch.bfloat16, device=DEV)
     a = sv.row_stats(x)
     b = sv.row_stats(x)
     assert torch.equal(a["lse"], b["lse"]) and torch.equal(a["entropy"], b["entropy"])
-    assert np_(a["argmax"]).tolist() == [12345, 0, 0]
+    assert np_(a["argmax"]).tolist() == [12345, 0, 0, 7, 5]
+    o = ref.rows_stats(host_logits(x.cpu()), temperature=1.0, V=40000, nthreads=NT)
+    assert np.array_equal(np_(a["argmax"]), o["argmax"])
 
 
 def test_read_probe_folds_every_word():
