@@ -18,19 +18,6 @@ namespace {
 
 using namespace sv;
 
-// Row pass shape: threads per workgroup and 16-byte vectors per thread per
-// chunk.  A chunk holds 16 bfloat16 or 16 float logits.
-constexpr int kRowBlock = 512;
-template <typename T>
-struct RowUnroll;
-template <>
-struct RowUnroll<uint16_t> {
-    static constexpr int value = 2;
-};
-template <>
-struct RowUnroll<float> {
-    static constexpr int value = 4;
-};
 // Race shape and the number of race workgroups to aim for per launch.
 constexpr int kRaceBlock = 256;
 constexpr int kRaceTargetBlocks = 2048;

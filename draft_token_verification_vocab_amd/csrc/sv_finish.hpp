@@ -14,11 +14,13 @@
 // split into segments so that small batches still fill the GPU.  Each
 // segment screens keys in float (log2 domain), re-evaluates every candidate
 // within a margin of the segment's best in double, and reports its best
-// double key; a combine kernel takes the best segment.  The key of the
-// target's top token bounds the row's best from below; since no id's key
-// exceeds its log2 weight by more than 23.5 on the 2^-24 lattice, blocks of
-// ids whose weights cannot reach that bound skip their draws (on peaked rows
-// nearly all of them).
+// double key; a combine kernel takes the best segment.  Work is pruned by
+// bounds: the key of the target's top token (then the wave's best) bounds
+// the row's best from below; an id's key is at most log2 p plus 23.5 on the
+// 2^-24 lattice, and at most log2 p + 0.5 + (leading one bits of its Philox
+// word) once drawn.  Blocks of ids below the first bound skip their draws
+// (on peaked rows nearly all of them); drawn ids below the second skip their
+// exact weight and logarithms (nearly all ids of any row).
 //
 // FLy (page "Training-Free Loosely Speculative Decoding...", section
 // "2. Metodologia", part A): one wave per sequence; deviations and gate
@@ -26,6 +28,7 @@
 #pragma once
 
 #include "sv_common.hpp"
+#include "sv_philox.hpp"
 
 namespace sv {
 
@@ -104,10 +107,18 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     const float lt2 = static_cast<float>(lse2_t);
     const float ld2 = static_cast<float>(lse2_d);
 
+    // best: this lane's best screening key; thr: the wave's best less the
+    // margin.  An id whose key cannot reach thr is never a candidate, so it
+    // needs neither its exact weight nor its logarithms.
     float best = floor;
     int bx = INT_MAX;
+    float thr = floor - kScreenMargin;
+    // lb = l*c - lsub bounds the log2 weight: log2 p for a residual row
+    // (w = max(0, p - q) <= p), the weight itself (up to the row's constant
+    // normaliser) for a draw from p.
+    const float lsub = residual ? lt2 : 0.f;
     const int nv = v_hi - v_lo;
-    const int trips = (nv + NT - 1) / NT;  // wave-uniform: the skip test below is a ballot
+    const int trips = (nv + NT - 1) / NT;  // wave-uniform: the skip tests below are ballots
     // The next trip's vectors are loaded before this trip's arithmetic.
     auto fetch = [&](int it, uint4 &tq, uint4 &dq) {
         const int vi = v_lo + it * NT + tid;
@@ -123,44 +134,51 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
         const int vl = live ? vi : v_lo;
         const uint4 tq = tn, dq = dn;
         if (it + 1 < trips) fetch(it + 1, tn, dn);
-        float xt[EPV], lw[EPV];
+        float xt[EPV], lb[EPV];
         E::unpack(tq, xt);
-        if (residual) {
-            float xd[EPV];
-            E::unpack(dq, xd);
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) {
-                const float p = hw_exp2(fmaf(xt[k], c, -lt2));
-                const float qq = hw_exp2(fmaf(xd[k], c, -ld2));
-                const float w = p - qq;
-                lw[k] = w > 0.f ? hw_log2(w) : -__builtin_inff();
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < EPV; ++k) lw[k] = xt[k] * c;  // log2 p + the row's normaliser
-        }
+        for (int k = 0; k < EPV; ++k) lb[k] = fmaf(xt[k], c, -lsub);
+        bool evaluated = false;
 #pragma unroll
         for (int blk = 0; blk < EPV / 4; ++blk) {
             const uint32_t base = static_cast<uint32_t>(vl) * EPV + blk * 4;
-            const float ub = fmaxf(fmaxf(lw[blk * 4], lw[blk * 4 + 1]),
-                                   fmaxf(lw[blk * 4 + 2], lw[blk * 4 + 3])) +
+            const float ub = fmaxf(fmaxf(lb[blk * 4], lb[blk * 4 + 1]),
+                                   fmaxf(lb[blk * 4 + 2], lb[blk * 4 + 3])) +
                              kMaxNegLogE;
-            const bool need = live && ub >= best - kScreenMargin;
+            const bool need = live && ub >= thr;
             if (__ballot(need) == 0ull) continue;  // no lane's block can win: no draws
             const uint4 r = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
             const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
+            // key <= lb + 0.472 + min(leading ones, 23) < lb + 0.5 + leading ones
+            const float lim = thr - 0.5f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int k = blk * 4 + q;
-                const float e2 = -hw_log2(lattice_u32f(w4[q]));  // E / ln 2 > 0
-                const float g = lw[k] - hw_log2(e2);
                 const int x = static_cast<int>(base) + q;
-                if (live && g > best && x < V) {
-                    best = g;
-                    bx = x;
+                const bool cand = need && x < V &&
+                                  static_cast<float>(leading_ones(w4[q])) >= lim - lb[k];
+                if (cand) {
+                    float lw;
+                    if (residual) {
+                        const float p = hw_exp2(lb[k]);
+                        const float qq = hw_exp2(fmaf(E::elem(dq, k), c, -ld2));
+                        const float w = p - qq;
+                        lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
+                    } else {
+                        lw = lb[k];  // l*c: log2 p + the row's normaliser
+                    }
+                    const float e2 = -hw_log2(lattice_u32f(w4[q]));  // E / ln 2 > 0
+                    const float g = lw - hw_log2(e2);
+                    if (g > best) {
+                        best = g;
+                        bx = x;
+                    }
+                    evaluated = true;
                 }
             }
         }
+        if (__ballot(evaluated) != 0ull)
+            thr = fmaxf(thr, from_ordered_bits(wave_max_u32(ordered_bits(best))) - kScreenMargin);
     }
 
     // Workgroup maximum of the screening keys.

@@ -1,0 +1,73 @@
+// sv_philox.hpp -- the counter-based generator behind every random draw of
+// lossless verification: Philox4x32-10, the stream layout (which counter a
+// draw uses) and the maps from a 32-bit word to a uniform on the 2^-24
+// lattice.
+#pragma once
+
+#include "sv_common.hpp"
+
+namespace sv {
+
+// --------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies by fixed odd multipliers on counter words 0 and 2,
+// with the products' high halves mixed into the other two words and the
+// round key; the key advances by two Weyl constants after every round.
+// --------------------------------------------------------------------------
+struct PhiloxKey {
+    uint32_t lo, hi;
+};
+
+__device__ __forceinline__ PhiloxKey philox_key(uint64_t seed) {
+    return PhiloxKey{static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32)};
+}
+
+__device__ __forceinline__ uint4 philox10(uint4 c, PhiloxKey k) {
+    uint32_t k0 = k.lo, k1 = k.hi;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t a = static_cast<uint64_t>(0xD2511F53u) * c.x;
+        const uint64_t b = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
+        // three-input XORs in one instruction each (truth table 0x96: odd parity)
+        c = make_uint4(__builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(b >> 32), c.y, k0, 0x96),
+                       static_cast<uint32_t>(b),
+                       __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(a >> 32), c.w, k1, 0x96),
+                       static_cast<uint32_t>(a));
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// Stream tags (fourth counter word).
+constexpr uint32_t kTagAccept = 1u;
+constexpr uint32_t kTagRace = 2u;
+
+__device__ __forceinline__ uint32_t pick_word(const uint4 &r, uint32_t w) {
+    return w == 0 ? r.x : (w == 1 ? r.y : (w == 2 ? r.z : r.w));
+}
+
+// One draw for vocabulary id x at (position, sequence, tag).
+__device__ __forceinline__ uint32_t draw_u32(PhiloxKey k, uint32_t x, uint32_t pos, uint32_t seq,
+                                             uint32_t tag) {
+    return pick_word(philox10(make_uint4(x >> 2, pos, seq, tag), k), x & 3u);
+}
+
+// The 23 leading bits on the odd points of the 2^-24 grid: (2k+1) 2^-24,
+// exact in float and double, never 0 or 1.
+__device__ __forceinline__ float lattice_u32f(uint32_t r) {
+    return fmaf(static_cast<float>(r >> 9), 0x1.0p-23f, 0x1.0p-24f);
+}
+__device__ __forceinline__ double lattice_u64(uint32_t r) {
+    return (2.0 * static_cast<double>(r >> 9) + 1.0) * 0x1.0p-24;
+}
+
+// Leading one bits of a Philox word (0..32).  With u its lattice uniform
+// (2k+1) 2^-24 and n = min(leading ones, 23): 1 - u >= 2^(-1-n), and since
+// E = -ln u >= 1 - u, -log2(E / ln 2) <= 1 + n + log2(ln 2) < 0.472 + n.
+__device__ __forceinline__ int leading_ones(uint32_t r) {
+    const uint32_t nr = ~r;
+    return nr == 0u ? 32 : __builtin_clz(nr);
+}
+
+}  // namespace sv

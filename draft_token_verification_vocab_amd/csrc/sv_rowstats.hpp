@@ -27,6 +27,20 @@
 
 namespace sv {
 
+// Launch shape: threads per workgroup and 16-byte vectors per thread per
+// chunk.  A chunk holds 16 bfloat16 or 16 float logits.
+constexpr int kRowBlock = 512;
+template <typename T>
+struct RowUnroll;
+template <>
+struct RowUnroll<uint16_t> {
+    static constexpr int value = 2;
+};
+template <>
+struct RowUnroll<float> {
+    static constexpr int value = 4;
+};
+
 // One group of rows processed by the same launch (target rows and draft rows
 // share a launch).  Row j of sequence b is row b*rows_per_seq + j.
 struct RowGroup {
