@@ -67,11 +67,18 @@ __device__ __forceinline__ int decide_lossless(const RaceArgs &a, int b, int L, 
     __shared__ int s_jstar;
     const int tid = threadIdx.x;
     if (tid < kWave) {
+        // the loads do not wait for L (kept_len), and the draw overlaps them
+        double lp = 0.0, lq = 0.0;
+        if (tid < a.K) {
+            const int i = b * a.K + tid;
+            lp = a.t_logp2[i];
+            lq = a.d_logq2[i];
+        }
+        const uint32_t uw = draw_u32(key, 0u, tid, b, kTagAccept);
         bool rej = false;
         if (tid < L) {
-            const double u = lattice_u64(draw_u32(key, 0u, tid, b, kTagAccept));
-            const int i = b * a.K + tid;
-            const double ratio = exp2(a.t_logp2[i] - a.d_logq2[i]);  // p(x_j)/q(x_j)
+            const double u = lattice_u64(uw);
+            const double ratio = exp2(lp - lq);  // p(x_j)/q(x_j)
             rej = !(u < ratio);
         }
         const unsigned long long m = __ballot(rej);
@@ -86,17 +93,26 @@ __device__ __forceinline__ int decide_lossless(const RaceArgs &a, int b, int L, 
 // log2 weight by more.
 constexpr float kMaxNegLogE = 23.5f;
 
-// Race over vectors [v_lo, v_hi) of one row (pair) with NT threads.
-// residual: w = max(0, p - q) from the target and draft rows; otherwise
-// w = p of the target row.  floor: a key some id of the row is known to reach
-// (less the margin); ids whose weight cannot bring them within the margin of
-// it skip their Philox draws.  Returns (in thread 0) the best double key and
-// id, or id -1 when no id of the range can win.
-template <typename T, int NT>
+// Vectors per thread per trip of the race (more loads in flight per thread).
+constexpr int kRaceUnroll = 1;
+
+// Forward declaration: the floor is computed once the first loads are out.
+template <typename T>
+__device__ float race_floor(const T *trow, const T *drow, bool residual, int am, int V, float c,
+                           double lse2_t, double lse2_d, PhiloxKey key, uint32_t pos,
+                           uint32_t seq);
+
+// Race over vectors [v_lo, v_hi) of one row (pair) with NT threads, R
+// vectors per thread per trip.  residual: w = max(0, p - q) from the target
+// and draft rows; otherwise w = p of the target row.  am: the target's top
+// token, whose key (less the margin) is a floor the row's best is known to
+// reach.  Returns (in thread 0) the best double key and id, or id -1 when no
+// id of the range can win.
+template <typename T, int NT, int R>
 __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo, int v_hi, int V,
                            float c, double cd, double inv_t, double lse2_t, double lse2_d,
-                           PhiloxKey key, uint32_t pos, uint32_t seq, float floor,
-                           double *out_key, int *out_x) {
+                           PhiloxKey key, uint32_t pos, uint32_t seq, int am, double *out_key,
+                           int *out_x) {
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
     constexpr int NW = NT / kWave;
@@ -106,74 +122,91 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     const uint4 *dv = reinterpret_cast<const uint4 *>(drow);
     const float lt2 = static_cast<float>(lse2_t);
     const float ld2 = static_cast<float>(lse2_d);
+    const int nv = v_hi - v_lo;
+    const int trips = (nv + NT * R - 1) / (NT * R);  // wave-uniform: the skip tests are ballots
+    // Vector r of a thread's trip `it` is v_lo + (it*R + r)*NT + tid.  The
+    // next trip's vectors are loaded before this trip's arithmetic.
+    auto fetch = [&](int it, uint4 (&tq)[R], uint4 (&dq)[R]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int vi = v_lo + (it * R + r) * NT + tid;
+            const int vl = vi < v_hi ? vi : v_lo;
+            tq[r] = vl < nfull ? load_stream(tv + vl) : E::partial(trow, vl, V);
+            if (residual) dq[r] = vl < nfull ? load_stream(dv + vl) : E::partial(drow, vl, V);
+        }
+    };
+    uint4 tn[R], dn[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) tn[r] = dn[r] = make_uint4(0u, 0u, 0u, 0u);
+    if (trips > 0) fetch(0, tn, dn);
+    const float floor = race_floor<T>(trow, drow, residual, am, V, c, lse2_t, lse2_d, key, pos, seq);
 
     // best: this lane's best screening key; thr: the wave's best less the
     // margin.  An id whose key cannot reach thr is never a candidate, so it
     // needs neither its exact weight nor its logarithms.
     float best = floor;
     int bx = INT_MAX;
+    float bt = 0.f, bd = 0.f;  // the best id's target and draft logits
     float thr = floor - kScreenMargin;
     // lb = l*c - lsub bounds the log2 weight: log2 p for a residual row
     // (w = max(0, p - q) <= p), the weight itself (up to the row's constant
     // normaliser) for a draw from p.
     const float lsub = residual ? lt2 : 0.f;
-    const int nv = v_hi - v_lo;
-    const int trips = (nv + NT - 1) / NT;  // wave-uniform: the skip tests below are ballots
-    // The next trip's vectors are loaded before this trip's arithmetic.
-    auto fetch = [&](int it, uint4 &tq, uint4 &dq) {
-        const int vi = v_lo + it * NT + tid;
-        const int vl = vi < v_hi ? vi : v_lo;
-        tq = vl < nfull ? load_stream(tv + vl) : E::partial(trow, vl, V);
-        if (residual) dq = vl < nfull ? load_stream(dv + vl) : E::partial(drow, vl, V);
-    };
-    uint4 tn = make_uint4(0u, 0u, 0u, 0u), dn = tn;
-    if (trips > 0) fetch(0, tn, dn);
     for (int it = 0; it < trips; ++it) {
-        const int vi = v_lo + it * NT + tid;
-        const bool live = vi < v_hi;
-        const int vl = live ? vi : v_lo;
-        const uint4 tq = tn, dq = dn;
-        if (it + 1 < trips) fetch(it + 1, tn, dn);
-        float xt[EPV], lb[EPV];
-        E::unpack(tq, xt);
+        uint4 tq[R], dq[R];
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) lb[k] = fmaf(xt[k], c, -lsub);
+        for (int r = 0; r < R; ++r) {
+            tq[r] = tn[r];
+            dq[r] = dn[r];
+        }
+        if (it + 1 < trips) fetch(it + 1, tn, dn);
         bool evaluated = false;
 #pragma unroll
-        for (int blk = 0; blk < EPV / 4; ++blk) {
-            const uint32_t base = static_cast<uint32_t>(vl) * EPV + blk * 4;
-            const float ub = fmaxf(fmaxf(lb[blk * 4], lb[blk * 4 + 1]),
-                                   fmaxf(lb[blk * 4 + 2], lb[blk * 4 + 3])) +
-                             kMaxNegLogE;
-            const bool need = live && ub >= thr;
-            if (__ballot(need) == 0ull) continue;  // no lane's block can win: no draws
-            const uint4 r = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
-            const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
-            // key <= lb + 0.472 + min(leading ones, 23) < lb + 0.5 + leading ones
-            const float lim = thr - 0.5f;
+        for (int r = 0; r < R; ++r) {
+            const int vi = v_lo + (it * R + r) * NT + tid;
+            const bool live = vi < v_hi;
+            float xt[EPV], lb[EPV];
+            E::unpack(tq[r], xt);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int k = blk * 4 + q;
-                const int x = static_cast<int>(base) + q;
-                const bool cand = need && x < V &&
-                                  static_cast<float>(leading_ones(w4[q])) >= lim - lb[k];
-                if (cand) {
-                    float lw;
-                    if (residual) {
-                        const float p = hw_exp2(lb[k]);
-                        const float qq = hw_exp2(fmaf(E::elem(dq, k), c, -ld2));
-                        const float w = p - qq;
-                        lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
-                    } else {
-                        lw = lb[k];  // l*c: log2 p + the row's normaliser
+            for (int k = 0; k < EPV; ++k) lb[k] = fmaf(xt[k], c, -lsub);
+#pragma unroll
+            for (int blk = 0; blk < EPV / 4; ++blk) {
+                const uint32_t base = static_cast<uint32_t>(live ? vi : v_lo) * EPV + blk * 4;
+                const float ub = fmaxf(fmaxf(lb[blk * 4], lb[blk * 4 + 1]),
+                                       fmaxf(lb[blk * 4 + 2], lb[blk * 4 + 3])) +
+                                 kMaxNegLogE;
+                const bool need = live && ub >= thr;
+                if (__ballot(need) == 0ull) continue;  // no lane's block can win: no draws
+                const uint4 rw = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
+                const uint32_t w4[4] = {rw.x, rw.y, rw.z, rw.w};
+                // key <= lb + 0.472 + min(leading ones, 23) < lb + 0.5 + leading ones
+                const float lim = thr - 0.5f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int k = blk * 4 + q;
+                    const int x = static_cast<int>(base) + q;
+                    const bool cand = need && x < V &&
+                                      static_cast<float>(leading_ones(w4[q])) >= lim - lb[k];
+                    if (cand) {
+                        float lw;
+                        if (residual) {
+                            const float p = hw_exp2(lb[k]);
+                            const float qq = hw_exp2(fmaf(E::elem(dq[r], k), c, -ld2));
+                            const float w = p - qq;
+                            lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
+                        } else {
+                            lw = lb[k];  // l*c: log2 p + the row's normaliser
+                        }
+                        const float e2 = -hw_log2(lattice_u32f(w4[q]));  // E / ln 2 > 0
+                        const float g = lw - hw_log2(e2);
+                        if (g > best) {
+                            best = g;
+                            bx = x;
+                            bt = xt[k];
+                            if (residual) bd = E::elem(dq[r], k);
+                        }
+                        evaluated = true;
                     }
-                    const float e2 = -hw_log2(lattice_u32f(w4[q]));  // E / ln 2 > 0
-                    const float g = lw - hw_log2(e2);
-                    if (g > best) {
-                        best = g;
-                        bx = x;
-                    }
-                    evaluated = true;
                 }
             }
         }
@@ -201,9 +234,9 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     if (bx != INT_MAX && best >= g1 - kScreenMargin) {
         const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(bx), pos, seq, kTagRace));
         const double lnE = log(-log(u));
-        const double lt = static_cast<double>(E::at(trow, bx));
+        const double lt = static_cast<double>(bt);
         if (residual) {
-            const double ld = static_cast<double>(E::at(drow, bx));
+            const double ld = static_cast<double>(bd);
             const double w = exp2(lt * cd - lse2_t) - exp2(ld * cd - lse2_d);
             if (w > 0.0) {
                 k64 = log(w) - lnE;
@@ -287,12 +320,11 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
     const int v_lo = seg * a.seg_vecs;
     const int v_hi = min(nvec, v_lo + a.seg_vecs);
-    const float fl = race_floor<T>(trow, drow, residual, a.t_am[b * (a.K + 1) + jstar], a.V, a.c,
-                                   lt, ld, key, jstar, b);
     double k;
     int x;
-    race_range<T, NT>(trow, drow, residual, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
-                      a.inv_t, lt, ld, key, jstar, b, fl, &k, &x);
+    race_range<T, NT, kRaceUnroll>(trow, drow, residual, v_lo, v_hi, a.V, a.c,
+                                   static_cast<double>(a.c), a.inv_t, lt, ld, key, jstar, b,
+                                   a.t_am[b * (a.K + 1) + jstar], &k, &x);
     if (threadIdx.x == 0) a.cand[b * a.segs + seg] = RaceCand{k, x, jstar};
 }
 
@@ -328,12 +360,11 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
         const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
         const double lt = a.t_lse2[b * (a.K + 1) + jstar];
         const PhiloxKey key = philox_key(a.seed);
-        const float fl = race_floor<T>(trow, nullptr, false, a.t_am[b * (a.K + 1) + jstar], a.V,
-                                       a.c, lt, 0.0, key, jstar, b);
         double k;
         int x;
-        race_range<T, NT>(trow, nullptr, false, 0, nvec, a.V, a.c, static_cast<double>(a.c),
-                          a.inv_t, lt, 0.0, key, jstar, b, fl, &k, &x);
+        race_range<T, NT, 1>(trow, nullptr, false, 0, nvec, a.V, a.c, static_cast<double>(a.c),
+                             a.inv_t, lt, 0.0, key, jstar, b, a.t_am[b * (a.K + 1) + jstar], &k,
+                             &x);
         if (tid == 0) s_y = x;
         __syncthreads();
     }
