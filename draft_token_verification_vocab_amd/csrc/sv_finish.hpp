@@ -150,8 +150,12 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     float thr = floor - kScreenMargin;
     // lb = l*c - lsub bounds the log2 weight: log2 p for a residual row
     // (w = max(0, p - q) <= p), the weight itself (up to the row's constant
-    // normaliser) for a draw from p.
+    // normaliser) for a draw from p.  The tests use a = thr - 0.5 - lb, one
+    // FMA per id: the key is below lb + 0.5 + (leading ones), so an id is a
+    // candidate only if its leading ones reach a; a block of four needs its
+    // draw only if some a <= 23 (lb + 23.5 >= thr).
     const float lsub = residual ? lt2 : 0.f;
+    float abase = thr - 0.5f + lsub;
     for (int it = 0; it < trips; ++it) {
         uint4 tq[R], dq[R];
 #pragma unroll
@@ -165,37 +169,34 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
         for (int r = 0; r < R; ++r) {
             const int vi = v_lo + (it * R + r) * NT + tid;
             const bool live = vi < v_hi;
-            float xt[EPV], lb[EPV];
+            float xt[EPV], av[EPV];
             E::unpack(tq[r], xt);
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) lb[k] = fmaf(xt[k], c, -lsub);
+            for (int k = 0; k < EPV; ++k) av[k] = fmaf(xt[k], -c, abase);
 #pragma unroll
             for (int blk = 0; blk < EPV / 4; ++blk) {
                 const uint32_t base = static_cast<uint32_t>(live ? vi : v_lo) * EPV + blk * 4;
-                const float ub = fmaxf(fmaxf(lb[blk * 4], lb[blk * 4 + 1]),
-                                       fmaxf(lb[blk * 4 + 2], lb[blk * 4 + 3])) +
-                                 kMaxNegLogE;
-                const bool need = live && ub >= thr;
+                const float amin = fminf(fminf(av[blk * 4], av[blk * 4 + 1]),
+                                         fminf(av[blk * 4 + 2], av[blk * 4 + 3]));
+                const bool need = live && amin <= kMaxNegLogE - 0.5f;
                 if (__ballot(need) == 0ull) continue;  // no lane's block can win: no draws
                 const uint4 rw = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
                 const uint32_t w4[4] = {rw.x, rw.y, rw.z, rw.w};
-                // key <= lb + 0.472 + min(leading ones, 23) < lb + 0.5 + leading ones
-                const float lim = thr - 0.5f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int k = blk * 4 + q;
+                    const bool cand =
+                        need && static_cast<float>(leading_ones(w4[q])) >= av[k];
                     const int x = static_cast<int>(base) + q;
-                    const bool cand = need && x < V &&
-                                      static_cast<float>(leading_ones(w4[q])) >= lim - lb[k];
-                    if (cand) {
+                    if (cand && x < V) {
                         float lw;
                         if (residual) {
-                            const float p = hw_exp2(lb[k]);
+                            const float p = hw_exp2(fmaf(xt[k], c, -lt2));
                             const float qq = hw_exp2(fmaf(E::elem(dq[r], k), c, -ld2));
                             const float w = p - qq;
                             lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
                         } else {
-                            lw = lb[k];  // l*c: log2 p + the row's normaliser
+                            lw = xt[k] * c;  // log2 p + the row's normaliser
                         }
                         const float e2 = -hw_log2(lattice_u32f(w4[q]));  // E / ln 2 > 0
                         const float g = lw - hw_log2(e2);
@@ -210,8 +211,10 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
                 }
             }
         }
-        if (__ballot(evaluated) != 0ull)
+        if (__ballot(evaluated) != 0ull) {
             thr = fmaxf(thr, from_ordered_bits(wave_max_u32(ordered_bits(best))) - kScreenMargin);
+            abase = thr - 0.5f + lsub;
+        }
     }
 
     // Workgroup maximum of the screening keys.

@@ -62,12 +62,10 @@ __device__ __forceinline__ double lattice_u64(uint32_t r) {
     return (2.0 * static_cast<double>(r >> 9) + 1.0) * 0x1.0p-24;
 }
 
-// Leading one bits of a Philox word (0..32).  With u its lattice uniform
+// Leading one bits of a Philox word.  With u its lattice uniform
 // (2k+1) 2^-24 and n = min(leading ones, 23): 1 - u >= 2^(-1-n), and since
 // E = -ln u >= 1 - u, -log2(E / ln 2) <= 1 + n + log2(ln 2) < 0.472 + n.
-__device__ __forceinline__ int leading_ones(uint32_t r) {
-    const uint32_t nr = ~r;
-    return nr == 0u ? 32 : __builtin_clz(nr);
-}
+// Counts at most 31 (the bound only needs min(., 23)): ~r | 1 is never 0.
+__device__ __forceinline__ int leading_ones(uint32_t r) { return __builtin_clz(~r | 1u); }
 
 }  // namespace sv
