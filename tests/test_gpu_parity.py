@@ -238,6 +238,37 @@ def test_lossless_masked_vocab():
         assert tok[b, acc[b]] % 3 != 0
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_lossless_race_without_floor(dtype):
+    # The draft puts far more mass than the target on the target's top token,
+    # so max(0, p - q) is 0 there and the race starts with no floor; the
+    # target's last 40% of ids are masked (no residual mass in the last
+    # segments) and V leaves a ragged last vector.  The first draft token is
+    # that top token, so most sequences reject at position 0.
+    B, K, V = 24, 2, 5003
+    batch = W.make(1, B=B, K=K, V=V, stride=5008)
+    tgt = batch.target.float()
+    dft = batch.draft.float()
+    tgt[:, :, int(V * 0.6):V] = -float("inf")
+    am = tgt[:, :, :V].argmax(-1)
+    for b in range(B):
+        for j in range(K):
+            dft[b, j, am[b, j]] = tgt[b, j, am[b, j]] + 8.0
+    batch.target = tgt.to(dtype)
+    batch.draft = dft.to(dtype)
+    batch.tokens[:, 0] = am[:, 0].to(torch.int32)
+    for seed in range(4):
+        r, o, _, _ = _lossless_check(batch, seed=seed)
+        acc = np_(r.accepted_len)
+        tok = np_(r.tokens)
+        assert (acc == 0).mean() > 0.5
+        for b in range(B):  # a residual token has p > q: never masked, never the top token
+            y = tok[b, acc[b]]
+            assert 0 <= y < int(V * 0.6)
+            if acc[b] == 0:
+                assert y != am[b, 0]
+
+
 def test_lossless_deterministic_across_streams():
     batch = W.make(3, B=16, K=4, V=20000)
     t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
