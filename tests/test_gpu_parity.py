@@ -125,6 +125,33 @@ def test_fly_parity(B, K, V, stride):
     _fly_check(batch)
 
 
+def test_fly_workspace_contents_do_not_matter():
+    # The workspace's contents on entry do not matter: random bytes there, and
+    # what a previous call left, must not change the result.
+    batch = W.make(2, B=40, K=6, V=3001, stride=3008)
+    t, tok = batch.target.to(DEV), batch.tokens.to(DEV)
+    B, K = tok.shape
+    need = sv.workspace_bytes(B, K, batch.V, stride=3008)
+    assert need > 0
+    g = torch.Generator(device="cpu").manual_seed(5)
+    want = None
+    for trial in range(4):
+        ws = torch.randint(0, 256, (need,), generator=g, dtype=torch.uint8).to(DEV)
+        if trial == 3:
+            ws.zero_()
+        for rep in range(2):  # the second call finds the first call's words
+            r = sv.verify(t, None, tok, seed=0, mode=sv.MODE_FLY, fly_theta=0.3, fly_window=2,
+                          vocab=batch.V, workspace=ws)
+            torch.cuda.synchronize()
+            got = (np_(r.accepted_len).copy(), np_(r.tokens).copy())
+            if want is None:
+                want = got
+                o = ref.verify(host_logits(batch.target), None, np_(batch.tokens), 0, ref.MODE_FLY,
+                               theta=f32(0.3), window=2, V=batch.V, nthreads=NT)
+                compare_decisions(got[0], got[1], o, ref.NEAR_GATE, "fly")
+            assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
 def test_fly_gate_branches():
     # peaks of +16 make confident rows (h ~ 0.03): the reject-now branch
     batch = W.fly(32, 8, 20000, seed=5, peak=16.0)
