@@ -297,7 +297,7 @@ def run_secondary(sv, W, dev, stream, args):
     out["lossless_b256_k8_v128256_bf16"] = _line(ms, rows, byt, res)
     del bs, b0, b1
 
-    # c0: lossless, B=1 K=4 V=32000 float32 (latency: a handful of rows)
+    # lossless, B=1 K=4 V=32000 float32 (latency: a handful of rows)
     c = W.CONFIGS[0]
     sets = [W.make(0, device=dev, step=s) for s in range(4)]
     ws0 = torch.empty(sv.workspace_bytes(1, c["K"], c["V"], dtype=sv.DTYPE_F32), dtype=torch.uint8,
@@ -312,7 +312,7 @@ def run_secondary(sv, W, dev, stream, args):
     out[c["name"]] = _line(ms, rows, rows * c["V"] * 4, res)
     del sets
 
-    # c1: lossless + AV score + one SGD step, B=64 K=5
+    # lossless + AV score + one SGD step, B=64 K=5
     c = W.CONFIGS[1]
     sets = [W.make(1, device=dev, step=s) for s in range(4)]
     K = c["K"]
@@ -329,7 +329,7 @@ def run_secondary(sv, W, dev, stream, args):
     out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
     del sets
 
-    # c3: lossless at T = 0.7 on V = 152064, B = 512 K = 4
+    # lossless at T = 0.7 on V = 152064, B = 512 K = 4
     c = W.CONFIGS[3]
     sets = [W.make(3, device=dev, step=s) for s in range(2)]
     ws3 = torch.empty(sv.workspace_bytes(512, 4, c["V"], temperature=0.7), dtype=torch.uint8,
@@ -345,7 +345,7 @@ def run_secondary(sv, W, dev, stream, args):
     out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
     del sets
 
-    # c4: full AV pipeline step (score, trimmed verify, update), B=1024 K=8
+    # full AV pipeline step (score, trimmed verify, update), B=1024 K=8
     c = W.CONFIGS[4]
     sets = [W.make(4, device=dev, step=s) for s in range(2)]
     K = c["K"]
