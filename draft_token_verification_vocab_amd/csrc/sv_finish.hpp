@@ -61,20 +61,53 @@ struct RaceArgs {
 // few 1e-6; every thread best within the margin is re-evaluated in double.
 constexpr float kScreenMargin = 1e-3f;
 
-// First rejected position of sequence b (L when all verified drafts pass),
-// computed by the first wave; every workgroup of the sequence agrees.
-__device__ __forceinline__ int decide_lossless(const RaceArgs &a, int b, int L, PhiloxKey key) {
-    __shared__ int s_jstar;
+// What the race needs of the row it runs on, besides the row itself.
+struct RowPick {
+    int jstar;   // first rejected position (L when all verified drafts pass)
+    int am;      // the target's top token at row jstar
+    float xt;    // target logit at am (-inf when am is not a valid id)
+    float xd;    // draft logit at am (residual rows only)
+    double lt;   // target log2-normaliser of row jstar
+    double ld;   // draft log2-normaliser of row jstar (residual rows only)
+};
+
+// The accept tests of sequence b and the values the race needs at the first
+// rejected position, for every workgroup of the sequence (they all agree).
+// The first wave does it: lane j loads row j's inputs (accept ratio, top
+// token, normalisers, the logits at the top token) at once, so that the
+// chosen row's values cost no further round trip; row K = 64 has no lane and
+// is loaded after the decision.
+template <typename T>
+__device__ __forceinline__ RowPick decide_lossless(const RaceArgs &a, int b, int L,
+                                                   PhiloxKey key) {
+    using E = Elem<T>;
+    __shared__ RowPick s_pick;
     const int tid = threadIdx.x;
+    const int K = a.K;
     if (tid < kWave) {
-        // the loads do not wait for L (kept_len), and the draw overlaps them
-        double lp = 0.0, lq = 0.0;
-        if (tid < a.K) {
-            const int i = b * a.K + tid;
+        double lp = 0.0, lq = 0.0, lt = 0.0, ld = 0.0;
+        int am = -1;
+        if (tid < K) {
+            const int i = b * K + tid;
             lp = a.t_logp2[i];
             lq = a.d_logq2[i];
+            ld = a.d_lse2[i];
+        }
+        if (tid <= K) {
+            am = a.t_am[b * (K + 1) + tid];
+            lt = a.t_lse2[b * (K + 1) + tid];
         }
         const uint32_t uw = draw_u32(key, 0u, tid, b, kTagAccept);
+        float xt = -__builtin_inff(), xd = -__builtin_inff();
+        if (tid <= K && am >= 0 && am < a.V) {
+            xt = E::at(static_cast<const T *>(a.target) +
+                           (static_cast<int64_t>(b) * (K + 1) + tid) * a.stride,
+                       am);
+            if (tid < K)
+                xd = E::at(static_cast<const T *>(a.draft) +
+                               (static_cast<int64_t>(b) * K + tid) * a.stride,
+                           am);
+        }
         bool rej = false;
         if (tid < L) {
             const double u = lattice_u64(uw);
@@ -82,10 +115,21 @@ __device__ __forceinline__ int decide_lossless(const RaceArgs &a, int b, int L, 
             rej = !(u < ratio);
         }
         const unsigned long long m = __ballot(rej);
-        if (tid == 0) s_jstar = m ? __ffsll(m) - 1 : L;
+        const int jstar = m ? __ffsll(m) - 1 : L;
+        if (tid == jstar) s_pick = RowPick{jstar, am, xt, xd, lt, ld};
+        if (jstar == kWave && tid == 0) {  // K = 64 and every draft accepted: row 64
+            const int r = b * (K + 1) + kWave;
+            const int am64 = a.t_am[r];
+            const float xt64 =
+                am64 >= 0 && am64 < a.V
+                    ? E::at(static_cast<const T *>(a.target) + static_cast<int64_t>(r) * a.stride,
+                            am64)
+                    : -__builtin_inff();
+            s_pick = RowPick{jstar, am64, xt64, -__builtin_inff(), a.t_lse2[r], 0.0};
+        }
     }
     __syncthreads();
-    return s_jstar;
+    return s_pick;
 }
 
 // Largest value -log2(E/ln2) can take on the 2^-24 lattice (u <= 1 - 2^-24
@@ -93,26 +137,42 @@ __device__ __forceinline__ int decide_lossless(const RaceArgs &a, int b, int L, 
 // log2 weight by more.
 constexpr float kMaxNegLogE = 23.5f;
 
-// Vectors per thread per trip of the race (more loads in flight per thread).
+// Vectors per thread per trip of the race (two measured no faster).
 constexpr int kRaceUnroll = 1;
 
-// Forward declaration: the floor is computed once the first loads are out.
-template <typename T>
-__device__ float race_floor(const T *trow, const T *drow, bool residual, int am, int V, float c,
-                           double lse2_t, double lse2_d, PhiloxKey key, uint32_t pos,
-                           uint32_t seq);
+// The key the race gives the target's top token am (logits xt, xd there),
+// less the screening margin: a floor that the row's best key is known to
+// reach.  -inf when am has no weight (then nothing is screened out).
+__device__ __forceinline__ float race_floor(bool residual, int am, float xt, float xd, float c,
+                                            double lse2_t, double lse2_d, PhiloxKey key,
+                                            uint32_t pos, uint32_t seq) {
+    if (am < 0) return -__builtin_inff();
+    float lw;
+    if (residual) {
+        const float p = hw_exp2(fmaf(xt, c, -static_cast<float>(lse2_t)));
+        const float qq = hw_exp2(fmaf(xd, c, -static_cast<float>(lse2_d)));
+        const float w = p - qq;
+        lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
+    } else {
+        lw = xt * c;
+    }
+    if (!(lw > -__builtin_inff())) return -__builtin_inff();
+    const float e2 = -hw_log2(lattice_u32f(draw_u32(key, static_cast<uint32_t>(am), pos, seq,
+                                                    kTagRace)));
+    return lw - hw_log2(e2) - kScreenMargin;
+}
 
 // Race over vectors [v_lo, v_hi) of one row (pair) with NT threads, R
 // vectors per thread per trip.  residual: w = max(0, p - q) from the target
 // and draft rows; otherwise w = p of the target row.  am: the target's top
-// token, whose key (less the margin) is a floor the row's best is known to
-// reach.  Returns (in thread 0) the best double key and id, or id -1 when no
+// token (am_xt, am_xd: its logits), whose key (less the margin) is a floor
+// the row's best is known to reach.  Returns (in thread 0) the best double key and id, or id -1 when no
 // id of the range can win.
 template <typename T, int NT, int R>
 __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo, int v_hi, int V,
                            float c, double cd, double inv_t, double lse2_t, double lse2_d,
-                           PhiloxKey key, uint32_t pos, uint32_t seq, int am, double *out_key,
-                           int *out_x) {
+                           PhiloxKey key, uint32_t pos, uint32_t seq, int am, float am_xt,
+                           float am_xd, double *out_key, int *out_x) {
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
     constexpr int NW = NT / kWave;
@@ -139,7 +199,7 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
 #pragma unroll
     for (int r = 0; r < R; ++r) tn[r] = dn[r] = make_uint4(0u, 0u, 0u, 0u);
     if (trips > 0) fetch(0, tn, dn);
-    const float floor = race_floor<T>(trow, drow, residual, am, V, c, lse2_t, lse2_d, key, pos, seq);
+    const float floor = race_floor(residual, am, am_xt, am_xd, c, lse2_t, lse2_d, key, pos, seq);
 
     // best: this lane's best screening key; thr: the wave's best less the
     // margin.  An id whose key cannot reach thr is never a candidate, so it
@@ -280,54 +340,29 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     __syncthreads();
 }
 
-// The key the race gives the target's top token am, less the screening
-// margin: a floor that the row's best key is known to reach.  -inf when am
-// has no weight (then nothing is screened out).
-template <typename T>
-__device__ float race_floor(const T *trow, const T *drow, bool residual, int am, int V, float c,
-                           double lse2_t, double lse2_d, PhiloxKey key, uint32_t pos,
-                           uint32_t seq) {
-    using E = Elem<T>;
-    if (am < 0 || am >= V) return -__builtin_inff();
-    const float xt = E::at(trow, am);
-    float lw;
-    if (residual) {
-        const float p = hw_exp2(fmaf(xt, c, -static_cast<float>(lse2_t)));
-        const float qq = hw_exp2(fmaf(E::at(drow, am), c, -static_cast<float>(lse2_d)));
-        const float w = p - qq;
-        lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
-    } else {
-        lw = xt * c;
-    }
-    if (!(lw > -__builtin_inff())) return -__builtin_inff();
-    const float e2 = -hw_log2(lattice_u32f(draw_u32(key, static_cast<uint32_t>(am), pos, seq,
-                                                    kTagRace)));
-    return lw - hw_log2(e2) - kScreenMargin;
-}
-
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     const int seg = blockIdx.x;
     const int b = blockIdx.y;
     const PhiloxKey key = philox_key(a.seed);
     const int L = a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K;
-    const int jstar = decide_lossless(a, b, L, key);
+    const RowPick pk = decide_lossless<T>(a, b, L, key);
+    const int jstar = pk.jstar;
     const bool residual = jstar < L;
     const T *trow = static_cast<const T *>(a.target) +
                     (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
     const T *drow = residual ? static_cast<const T *>(a.draft) +
                                    (static_cast<int64_t>(b) * a.K + jstar) * a.stride
                              : nullptr;
-    const double lt = a.t_lse2[b * (a.K + 1) + jstar];
-    const double ld = residual ? a.d_lse2[b * a.K + jstar] : 0.0;
     const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
     const int v_lo = seg * a.seg_vecs;
     const int v_hi = min(nvec, v_lo + a.seg_vecs);
     double k;
     int x;
     race_range<T, NT, kRaceUnroll>(trow, drow, residual, v_lo, v_hi, a.V, a.c,
-                                   static_cast<double>(a.c), a.inv_t, lt, ld, key, jstar, b,
-                                   a.t_am[b * (a.K + 1) + jstar], &k, &x);
+                                   static_cast<double>(a.c), a.inv_t, pk.lt,
+                                   residual ? pk.ld : 0.0, key, jstar, b, pk.am, pk.xt, pk.xd,
+                                   &k, &x);
     if (threadIdx.x == 0) a.cand[b * a.segs + seg] = RaceCand{k, x, jstar};
 }
 
@@ -365,8 +400,10 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
         const PhiloxKey key = philox_key(a.seed);
         double k;
         int x;
+        const int am = a.t_am[b * (a.K + 1) + jstar];
+        const float am_xt = am >= 0 && am < a.V ? Elem<T>::at(trow, am) : -__builtin_inff();
         race_range<T, NT, 1>(trow, nullptr, false, 0, nvec, a.V, a.c, static_cast<double>(a.c),
-                             a.inv_t, lt, 0.0, key, jstar, b, a.t_am[b * (a.K + 1) + jstar], &k,
+                             a.inv_t, lt, 0.0, key, jstar, b, am, am_xt, -__builtin_inff(), &k,
                              &x);
         if (tid == 0) s_y = x;
         __syncthreads();
