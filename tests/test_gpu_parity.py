@@ -296,6 +296,20 @@ def test_lossless_race_without_floor(dtype):
                 assert y != am[b, 0]
 
 
+@pytest.mark.parametrize("mode", ["lossless", "fly"])
+def test_large_vocabulary(mode):
+    # V = 2^20 + 3 (ragged, 8x the workloads' largest): row statistics, the
+    # race over every id and the FLy resolution, against the oracle
+    V = (1 << 20) + 3
+    if mode == "lossless":
+        batch = W.make(1, B=3, K=2, V=V, stride=V + 5)
+        for seed in (0, 1):
+            _lossless_check(batch, seed=seed)
+    else:
+        batch = W.make(2, B=3, K=3, V=V, stride=V + 5)
+        _fly_check(batch, theta=0.3, window=1)
+
+
 def test_lossless_deterministic_across_streams():
     batch = W.make(3, B=16, K=4, V=20000)
     t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
