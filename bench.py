@@ -41,7 +41,8 @@ METRIC = "verified logits rows/s and achieved HBM GB/s (% peak), V=128256 bf16, 
 HBM_PEAK_GBPS = 8000.0
 # the row pass's kernel, its launch shape and the helpers it compiles from
 ROW_PASS_SOURCES = ["draft_token_verification_vocab_amd/csrc/sv_rowstats.hpp",
-                    "draft_token_verification_vocab_amd/csrc/sv_common.hpp"]
+                    "draft_token_verification_vocab_amd/csrc/sv_common.hpp",
+                    "draft_token_verification_vocab_amd/csrc/sv_philox.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_pass_fly_b256_k8_v128256_bf16.traffic.json")
 VALU_FILE = os.path.join(ROOT, "profiles", "row_pass_valu_fly_b256_k8_v128256_bf16.json")
 

@@ -50,7 +50,7 @@ int race_segments(int32_t B, int32_t V, int32_t dtype) {
 }
 
 struct WsLayout {
-    size_t t_lse2, t_logp2, t_h, t_am, dstats, cand, total;
+    size_t t_lse2, t_logp2, t_h, t_am, dstats, cand, bonus_cnt, bonus_list, total;
 };
 
 WsLayout layout_for(int32_t B, int32_t K, int32_t V, int32_t dtype) {
@@ -70,6 +70,10 @@ WsLayout layout_for(int32_t B, int32_t K, int32_t V, int32_t dtype) {
     off = align_up(off + 24 * n);
     w.cand = off;
     off = align_up(off + sizeof(RaceCand) * static_cast<size_t>(B) * race_segments(B, V, dtype));
+    w.bonus_cnt = off;
+    off = align_up(off + 4 * static_cast<size_t>(B));
+    w.bonus_list = off;
+    off = align_up(off + sizeof(int2) * kMaxBonusCand * static_cast<size_t>(B));
     w.total = off;
     return w;
 }
@@ -114,25 +118,36 @@ spec_status launch_status() {
 // Row-pass dispatch over (dtype, entropy for group 0).  Group 1 (draft rows)
 // never needs the entropy numerator.
 // ---------------------------------------------------------------------------
-template <typename T, bool E0>
+template <typename T, bool E0, bool CAND>
 void launch_rows_t(const RowArgs &a, int nblocks, hipStream_t st) {
-    row_stats_kernel<T, kRowBlock, RowUnroll<T>::value, E0>
+    row_stats_kernel<T, kRowBlock, RowUnroll<T>::value, E0, CAND>
         <<<dim3(nblocks), dim3(kRowBlock), 0, st>>>(a);
 }
 
-void launch_rows(int32_t dtype, const RowArgs &a, int nblocks, bool e0, hipStream_t st) {
-    if (nblocks <= 0) return;
-    if (dtype == SPEC_DTYPE_BF16) {
+template <typename T>
+void launch_rows_dt(const RowArgs &a, int nblocks, bool e0, bool cand, hipStream_t st) {
+    if (cand) {
         if (e0)
-            launch_rows_t<uint16_t, true>(a, nblocks, st);
+            launch_rows_t<T, true, true>(a, nblocks, st);
         else
-            launch_rows_t<uint16_t, false>(a, nblocks, st);
+            launch_rows_t<T, false, true>(a, nblocks, st);
     } else {
         if (e0)
-            launch_rows_t<float, true>(a, nblocks, st);
+            launch_rows_t<T, true, false>(a, nblocks, st);
         else
-            launch_rows_t<float, false>(a, nblocks, st);
+            launch_rows_t<T, false, false>(a, nblocks, st);
     }
+}
+
+// cand: group 0 holds a lossless call's target rows, which also list the
+// bonus candidates (a.seed, a.cand_cnt, a.cand_list set).
+void launch_rows(int32_t dtype, const RowArgs &a, int nblocks, bool e0, hipStream_t st,
+                 bool cand = false) {
+    if (nblocks <= 0) return;
+    if (dtype == SPEC_DTYPE_BF16)
+        launch_rows_dt<uint16_t>(a, nblocks, e0, cand, st);
+    else
+        launch_rows_dt<float>(a, nblocks, e0, cand, st);
 }
 
 RowGroup empty_group() {
@@ -244,7 +259,14 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     ra.inv_ln_v = 1.0 / std::log(static_cast<double>(V));
     const int nrows = ra.nrows0 + (own_draft ? B * K : 0);
     const bool ent0 = !lossless || out->target_entropy != nullptr;
-    launch_rows(p.dtype, ra, nrows, ent0, st);
+    int32_t *bonus_cnt = reinterpret_cast<int32_t *>(w + ws.bonus_cnt);
+    int2 *bonus_list = reinterpret_cast<int2 *>(w + ws.bonus_list);
+    if (lossless) {
+        ra.seed = seed;
+        ra.cand_cnt = bonus_cnt;
+        ra.cand_list = bonus_list;
+    }
+    launch_rows(p.dtype, ra, nrows, ent0, st, lossless);
     if ((s = launch_status()) != SPEC_OK) return s;
 
     if (!lossless) {
@@ -275,6 +297,8 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     const int nvec = (V + elems_per_vec(p.dtype) - 1) / elems_per_vec(p.dtype);
     rg.seg_vecs = (nvec + rg.segs - 1) / rg.segs;
     rg.cand = reinterpret_cast<RaceCand *>(w + ws.cand);
+    rg.bonus_cnt = bonus_cnt;
+    rg.bonus_list = bonus_list;
     const dim3 grid(rg.segs, B);
     if (p.dtype == SPEC_DTYPE_BF16) {
         race_kernel<uint16_t, kRaceBlock><<<grid, dim3(kRaceBlock), 0, st>>>(rg);

@@ -20,6 +20,9 @@ constexpr float kNoMax = -1.0e30f;
 // Terms 2^d with d below this are exactly zero in float; clamping d keeps the
 // entropy accumulator free of 0 * (-inf) for masked (-inf) logits.
 constexpr float kMinExp2 = -200.0f;
+// Most ids a bonus-candidate list (the row pass's list of the ids a draw from
+// p at a row could pick) holds; a row with more is raced in full.
+constexpr int kMaxBonusCand = 64;
 
 // 16-byte streaming load with the non-temporal hint: logits rows are read
 // exactly once, and on gfx950 the hint lifts a one-pass stream from ~6.0 to

@@ -55,6 +55,10 @@ struct RaceArgs {
     int32_t segs;             // segments per row
     int32_t seg_vecs;         // 16-byte vectors per segment
     RaceCand *cand;           // [B][segs]
+    // The row pass's candidate list of row L_b (the only row a draw from p
+    // can use): count (-1 when incomplete) and (id, logit bits) entries.
+    const int32_t *bonus_cnt;  // [B]
+    const int2 *bonus_list;    // [B][kMaxBonusCand]
 };
 
 // Screening margin in log2 units.  Float screening keys carry errors of a
@@ -349,6 +353,42 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     const RowPick pk = decide_lossless<T>(a, b, L, key);
     const int jstar = pk.jstar;
     const bool residual = jstar < L;
+    if (!residual && a.bonus_cnt) {
+        const int n = a.bonus_cnt[b];
+        if (n >= 0) {
+            // A draw from p at row L over the listed ids, which hold every id
+            // that could win it: exact double keys, no second read of the row.
+            if (seg == 0) {
+                const int tid = threadIdx.x;
+                if (tid < kWave) {
+                    double k64 = -__builtin_inf();
+                    int kx = INT_MAX;
+                    if (tid < n) {
+                        const int2 e = a.bonus_list[static_cast<int64_t>(b) * kMaxBonusCand + tid];
+                        const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(e.x),
+                                                              static_cast<uint32_t>(jstar),
+                                                              static_cast<uint32_t>(b), kTagRace));
+                        k64 = static_cast<double>(__int_as_float(e.y)) * a.inv_t - log(-log(u));
+                        kx = e.x;
+                    }
+#pragma unroll
+                    for (int msk = kWave / 2; msk > 0; msk >>= 1) {
+                        const double ok = __shfl_xor(k64, msk, kWave);
+                        const int ox = __shfl_xor(kx, msk, kWave);
+                        if (ok > k64 || (ok == k64 && ox < kx)) {
+                            k64 = ok;
+                            kx = ox;
+                        }
+                    }
+                    if (tid == 0)
+                        a.cand[b * a.segs] = RaceCand{k64, kx == INT_MAX ? -1 : kx, jstar};
+                }
+            } else if (threadIdx.x == 0) {
+                a.cand[b * a.segs + seg] = RaceCand{-__builtin_inf(), -1, jstar};
+            }
+            return;
+        }
+    }
     const T *trow = static_cast<const T *>(a.target) +
                     (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
     const T *drow = residual ? static_cast<const T *>(a.draft) +

@@ -24,6 +24,7 @@
 #pragma once
 
 #include "sv_common.hpp"
+#include "sv_philox.hpp"
 
 namespace sv {
 
@@ -76,7 +77,17 @@ struct RowArgs {
     float c;                  // log2(e) / T
     float pad2_;
     double inv_ln_v;          // 1 / ln V
+    // Bonus candidates (launches with CAND): for row L_b of sequence b, the
+    // ids a race over p at that row could pick (see bonus_candidates).
+    uint64_t seed;
+    int32_t *cand_cnt;  // [B]: number of ids, or -1 when the list is not complete
+    int2 *cand_list;    // [B][kMaxBonusCand]: (id, logit bits)
 };
+
+// Candidates are the ids whose l*c reaches the top token's race key less this
+// (the race's largest gain from a uniform near 1, 23.47, plus both screening
+// margins, rounded up).
+constexpr float kBonusBelow = 24.0f;
 
 // Row j of sequence b is not read when adaptive verification trimmed it.
 __device__ __forceinline__ bool row_trimmed(const RowArgs &a, const RowGroup &g, int b, int j) {
@@ -136,8 +147,15 @@ __device__ __forceinline__ void row_emit(const RowArgs &a, const RowGroup &g, in
         g.logtok2[gidx] = static_cast<double>(ltok) * static_cast<double>(c) - lse2;
 }
 
-template <typename T, int BLOCK, int UNROLL, bool ENT>
-__device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int64_t row) {
+// CAND: target rows of a lossless call; row L_b of each sequence also lists
+// the ids a race over p at that row could pick.  Each thread tracks, besides
+// its max chunk (saved in LDS), the largest maximum of its other chunks (m2,
+// chunk it2) and of the rest (m3): every candidate is then in the max chunk
+// or in chunk it2 (re-read when m2 can reach the threshold), unless m3 can
+// reach it too, and then the list is marked incomplete.
+template <typename T, int BLOCK, int UNROLL, bool ENT, bool CAND>
+__device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int64_t row,
+                                        uint4 (&sh_saved)[UNROLL][BLOCK]) {
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
     constexpr int N = UNROLL * EPV;
@@ -173,7 +191,8 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     float m = kNoMax, mc = kNoMax * c, cs = 0.f, ct = 0.f;
     float s = 0.f, t = 0.f;
     int itb = -1;
-    __shared__ uint4 sh_saved[UNROLL][BLOCK];
+    float m2 = kNoMax, m3 = kNoMax;  // CAND: second chunk maximum, and the rest's
+    int it2 = -1;
 
     // it: the chunk's index; thread tid's chunk `it` starts at vector
     // it*UNROLL*BLOCK + tid.
@@ -215,6 +234,16 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
                     ctsum = fmaf(hw_exp2(d), d, ctsum);
                 }
             }
+        }
+        if (CAND) {
+            // the chunk that is not (or no longer) the max chunk competes for
+            // second place
+            const float dm = up ? m : cm;
+            const int di = up ? itb : it;
+            const bool sec = dm > m2;
+            m3 = fmaxf(m3, sec ? m2 : dm);
+            it2 = sec ? di : it2;
+            m2 = sec ? dm : m2;
         }
         if (up) {
             // A new thread maximum (rare after the first chunks): the old max
@@ -283,12 +312,15 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     // order inside it: vector u-major, lane k-minor), and the lowest id wins.
     __shared__ uint32_t sh_m[NW], sh_p[NW];
     __shared__ double sh_s[NW], sh_t[NW];
+    __shared__ int sh_cnt;                  // CAND: bonus candidates listed
+    __shared__ int sh_lb[NW], sh_bw[NW];    // CAND: per-wave lower bounds, third-chunk flags
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     // m + 0 turns -0 into +0, so that a row maximum of zero is one key and
     // its first id is the lowest of every zero, whatever its sign.
     const uint32_t om = ordered_bits(m + 0.0f);
     const uint32_t wm = wave_max_u32(om);
     if (lane == 0) sh_m[wv] = wm;
+    if (CAND && tid == 0) sh_cnt = 0;
     __syncthreads();
     uint32_t bm = sh_m[0];
 #pragma unroll
@@ -314,6 +346,36 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     const int P = static_cast<int>(~bp);
     const float Mc = M * c;
 
+    // Bonus candidates of row L_b (WG-uniform branch).
+    const bool list_row =
+        CAND && j == (a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K) && P != INT_MAX;
+    // Phase A counts (no writes): ids of the max chunk at or above the
+    // threshold tc, one more when the second chunk can hold some, and whether
+    // a third can.  Rows with too many candidates (flat rows) stop there.
+    float tc = 0.f;
+    bool need2 = false;
+    if (list_row) {
+        // the race's key of the top token, in its units (l*c - log2(E/ln2))
+        const uint32_t w = draw_u32(philox_key(a.seed), static_cast<uint32_t>(P),
+                                    static_cast<uint32_t>(j), static_cast<uint32_t>(b), kTagRace);
+        tc = Mc - hw_log2(-hw_log2(lattice_u32f(w))) - kBonusBelow;
+        int lb = 0;
+        if (v0b >= 0 && m * c >= tc) {
+            float xv[N];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) E::unpack(sh_saved[u][tid], xv + u * EPV);
+#pragma unroll
+            for (int k = 0; k < N; ++k) lb += xv[k] * c >= tc ? 1 : 0;
+        }
+        need2 = it2 >= 0 && m2 * c >= tc;
+        lb += need2 ? 1 : 0;
+        const uint64_t wl = wave_sum_u64(static_cast<uint64_t>(lb));
+        const bool wbad = __ballot(m3 * c >= tc) != 0ull;
+        if (lane == 0) {
+            sh_lb[wv] = static_cast<int>(wl);
+            sh_bw[wv] = wbad ? 1 : 0;
+        }
+    }
     // (2) Every thread rescales its sums to M.  The thread holding the
     // argmax swaps its max chunk for that chunk's other terms, so the block
     // sums are r = sum_{x != argmax} 2^(l_x c - Mc) and the matching entropy
@@ -358,15 +420,71 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
         }
         row_emit<ENT>(a, g, row, M, P, r, to, gather, gidx, ltok);
     }
+    if (CAND && j == (a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K)) {
+        // Phase B: write the list when it is complete and fits.
+        int total = 0, bad = 0;
+        if (list_row) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                total += sh_lb[w];
+                bad |= sh_bw[w];
+            }
+        }
+        const bool fits = list_row && !bad && total <= kMaxBonusCand;
+        if (fits) {
+            int2 *dst = a.cand_list + static_cast<int64_t>(b) * kMaxBonusCand;
+            // every id of a chunk at or above the threshold takes the next slot
+            auto take = [&](const uint4 (&vb)[UNROLL], int v0) {
+                float xv[N];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) E::unpack(vb[u], xv + u * EPV);
+#pragma unroll
+                for (int k = 0; k < N; ++k) {
+                    const int id = (v0 + (k / EPV) * BLOCK) * EPV + (k % EPV);
+                    if (xv[k] * c >= tc && id < V) {
+                        const int o = atomicAdd(&sh_cnt, 1);
+                        if (o < kMaxBonusCand) dst[o] = make_int2(id, __float_as_int(xv[k]));
+                    }
+                }
+            };
+            if (v0b >= 0 && m * c >= tc) {
+                uint4 vb[UNROLL];
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) vb[u] = sh_saved[u][tid];
+                take(vb, v0b);
+            }
+            if (need2) {  // the second chunk, read again
+                uint4 vb[UNROLL];
+                const int v2 = it2 * kChunkVecs + tid;
+                const uint32_t ni = E::pad_word();
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u) {
+                    const int vi = v2 + u * BLOCK;
+                    if (vi < nfull)
+                        vb[u] = vrow[vi];
+                    else if (vi < nvec)
+                        vb[u] = E::partial(rp, vi, V);
+                    else
+                        vb[u] = make_uint4(ni, ni, ni, ni);
+                }
+                take(vb, v2);
+            }
+        }
+        __syncthreads();
+        if (tid == 0) a.cand_cnt[b] = fits && sh_cnt <= kMaxBonusCand ? sh_cnt : -1;
+    }
 }
 
-template <typename T, int BLOCK, int UNROLL, bool ENT0>
+// CAND: group 0 holds a lossless call's target rows (bonus candidates).
+template <typename T, int BLOCK, int UNROLL, bool ENT0, bool CAND>
 __global__ __launch_bounds__(BLOCK) void row_stats_kernel(RowArgs a) {
+    // the max chunks of the workgroup's threads (one buffer for either group)
+    __shared__ uint4 sh_saved[UNROLL][BLOCK];
     const int blk = blockIdx.x;
     if (blk < a.nrows0)
-        row_one<T, BLOCK, UNROLL, ENT0>(a, a.g[0], blk);
+        row_one<T, BLOCK, UNROLL, ENT0, CAND>(a, a.g[0], blk, sh_saved);
     else
-        row_one<T, BLOCK, UNROLL, false>(a, a.g[1], blk - a.nrows0);
+        row_one<T, BLOCK, UNROLL, false, false>(a, a.g[1], blk - a.nrows0, sh_saved);
 }
 
 // Load-only twin of the row pass: the same grid (a workgroup per row), the

@@ -310,6 +310,60 @@ def test_large_vocabulary(mode):
         _fly_check(batch, theta=0.3, window=1)
 
 
+def _all_accept_batch(B, K, V, stride, seed, peaks):
+    # draft == target, so every verified draft is accepted and the step ends
+    # with a draw from p at row L (the bonus row).  Rows: N(0,1) noise far
+    # below a few peaks (log-odds within the race's reach of each other).
+    g = torch.Generator().manual_seed(seed)
+    t = torch.randn(B, K + 1, V, generator=g) - 60.0
+    for b in range(B):
+        for j in range(K + 1):
+            for q, pid in enumerate(peaks(b, j)):
+                t[b, j, pid] = 3.0 - 1.5 * q + 0.3 * torch.rand((), generator=g).item()
+    tb = torch.full((B, K + 1, stride), float("nan"))
+    tb[:, :, :V] = t
+    tb = tb.to(torch.bfloat16)
+    d = tb[:, :K].clone()
+    tok = W.sample_rows(d[:, :, :V], 1.0, torch.Generator().manual_seed(seed + 1))
+    return W.Batch(tb, d, tok, V, 1.0)
+
+
+@pytest.mark.parametrize("layout", ["spread", "same_thread_two_chunks",
+                                    "same_thread_three_chunks", "one_chunk"])
+def test_lossless_bonus_candidate_list(layout):
+    # The row pass lists, for row L, every id a draw from p there could pick;
+    # the race then draws over that list.  The peaks sit where the list must
+    # take them from: different threads, a thread's max chunk and second chunk
+    # (read again), three chunks of one thread (the list is incomplete and the
+    # row is raced in full), or one chunk.  bf16 rows: chunk `it` of thread t
+    # holds vectors it*1024 + t and it*1024 + 512 + t (8 ids each).
+    B, K, V, stride = 12, 3, 20011, 20016
+    if layout == "spread":
+        peaks = lambda b, j: [(97 * b + 13 * j + 1000 * q) % V for q in range(5)]
+    elif layout == "same_thread_two_chunks":
+        peaks = lambda b, j: [8 * (1024 * 0 + 7) + 1, 8 * (1024 * 2 + 7) + 3, 8 * (512 + 7)]
+    elif layout == "same_thread_three_chunks":
+        peaks = lambda b, j: [8 * (1024 * 0 + 5), 8 * (1024 * 1 + 5) + 2, 8 * (1024 * 2 + 5) + 7]
+    else:
+        peaks = lambda b, j: [8 * 9, 8 * 9 + 5, 8 * (512 + 9) + 1]
+    batch = _all_accept_batch(B, K, V, stride, 41, peaks)
+    for seed in range(6):
+        r, o, _, _ = _lossless_check(batch, seed=seed)
+        assert (np_(r.accepted_len) == K).all()
+
+
+def test_lossless_bonus_at_row_64_and_trimmed():
+    # the bonus row is row 64 (K = 64, every draft accepted), and with kept
+    # lengths the draw from p happens at row L < K
+    B, K, V = 4, 64, 3001
+    batch = _all_accept_batch(B, K, V, 3008, 7, lambda b, j: [(31 * j + b) % V, (31 * j + 500) % V])
+    r, o, _, _ = _lossless_check(batch, seed=2)
+    assert (np_(r.accepted_len) == K).all()
+    kept = torch.tensor([0, 5, 63, 64], dtype=torch.int32)
+    r, o, _, _ = _lossless_check(batch, seed=3, kept=kept)
+    assert np_(r.accepted_len).tolist() == [0, 5, 63, 64]
+
+
 def test_lossless_deterministic_across_streams():
     batch = W.make(3, B=16, K=4, V=20000)
     t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
