@@ -13,6 +13,10 @@
 //
 // Rows are streamed with non-temporal 16-byte loads.
 //
+// In a lossless call the target row L_b of each sequence (the only row where a
+// draw from p can happen) also lists the ids such a draw could pick, so that
+// the race need not read that row again (see row_one, CAND).
+//
 // Arithmetic is in base 2: with c = log2(e)/T every term is 2^(l*c - mc),
 // where mc = m*c and m is the running maximum of the raw logits.  A thread
 // reads its share of the row in chunks of UNROLL vectors (UNROLL*8 bfloat16
@@ -78,7 +82,7 @@ struct RowArgs {
     float pad2_;
     double inv_ln_v;          // 1 / ln V
     // Bonus candidates (launches with CAND): for row L_b of sequence b, the
-    // ids a race over p at that row could pick (see bonus_candidates).
+    // ids a race over p at that row could pick (see row_one).
     uint64_t seed;
     int32_t *cand_cnt;  // [B]: number of ids, or -1 when the list is not complete
     int2 *cand_list;    // [B][kMaxBonusCand]: (id, logit bits)
