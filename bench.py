@@ -48,10 +48,16 @@ VALU_FILE = os.path.join(ROOT, "profiles", "row_pass_valu_fly_b256_k8_v128256_bf
 
 
 def row_pass_source_hash() -> str:
+    """Hash of the row pass's sources with comments and blank space removed
+    (an edit to a comment does not change the kernel)."""
+    import re
     h = hashlib.sha256()
     for p in ROW_PASS_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"//[^\n]*", "", text)
+        text = re.sub(r"\s+", " ", text)
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 
