@@ -93,9 +93,9 @@ struct RowArgs {
 // margins, rounded up).
 constexpr float kBonusBelow = 24.0f;
 
-// Row j of sequence b is not read when adaptive verification trimmed it.
-__device__ __forceinline__ bool row_trimmed(const RowArgs &a, const RowGroup &g, int b, int j) {
-    return a.kept_len && j >= clamp_len(a.kept_len[b], a.K) + g.active_extra;
+// L_b: the verified drafts of sequence b (kept_len clamped to [0, K], or K).
+__device__ __forceinline__ int kept_of(const RowArgs &a, int b) {
+    return a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K;
 }
 
 // What a row that was not read reports.
@@ -153,10 +153,10 @@ __device__ __forceinline__ void row_emit(const RowArgs &a, const RowGroup &g, in
 
 // CAND: target rows of a lossless call; row L_b of each sequence also lists
 // the ids a race over p at that row could pick.  Each thread tracks, besides
-// its max chunk (saved in LDS), the largest maximum of its other chunks (m2,
-// chunk it2) and of the rest (m3): every candidate is then in the max chunk
-// or in chunk it2 (re-read when m2 can reach the threshold), unless m3 can
-// reach it too, and then the list is marked incomplete.
+// its max chunk (saved in LDS), the largest maximum m2 of its other chunks
+// (one median-of-three per chunk): when no thread's m2 reaches the threshold,
+// every candidate is in a saved max chunk; otherwise the list is marked
+// incomplete and the race reads the row.
 template <typename T, int BLOCK, int UNROLL, bool ENT, bool CAND>
 __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int64_t row,
                                         uint4 (&sh_saved)[UNROLL][BLOCK]) {
@@ -170,7 +170,8 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
 
     const int b = static_cast<int>(row / g.rows_per_seq);
     const int j = static_cast<int>(row - static_cast<int64_t>(b) * g.rows_per_seq);
-    if (row_trimmed(a, g, b, j)) {  // report "not read"
+    const int Lb = kept_of(a, b);
+    if (a.kept_len && j >= Lb + g.active_extra) {  // trimmed away: report "not read"
         if (tid == 0) write_unread(g, row);
         return;
     }
@@ -195,8 +196,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     float m = kNoMax, mc = kNoMax * c, cs = 0.f, ct = 0.f;
     float s = 0.f, t = 0.f;
     int itb = -1;
-    float m2 = kNoMax, m3 = kNoMax;  // CAND: second chunk maximum, and the rest's
-    int it2 = -1;
+    float m2 = kNoMax;  // CAND: the largest maximum of the other chunks
 
     // it: the chunk's index; thread tid's chunk `it` starts at vector
     // it*UNROLL*BLOCK + tid.
@@ -239,16 +239,9 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
                 }
             }
         }
-        if (CAND) {
-            // the chunk that is not (or no longer) the max chunk competes for
-            // second place
-            const float dm = up ? m : cm;
-            const int di = up ? itb : it;
-            const bool sec = dm > m2;
-            m3 = fmaxf(m3, sec ? m2 : dm);
-            it2 = sec ? di : it2;
-            m2 = sec ? dm : m2;
-        }
+        // m2 = max(m2, the chunk that is not (or no longer) the max chunk):
+        // with m2 <= m that is the median of (m2, cm, m)
+        if (CAND) m2 = __builtin_amdgcn_fmed3f(m2, cm, m);
         if (up) {
             // A new thread maximum (rare after the first chunks): the old max
             // chunk joins the rest, which is rescaled to the new maximum by
@@ -317,7 +310,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     __shared__ uint32_t sh_m[NW], sh_p[NW];
     __shared__ double sh_s[NW], sh_t[NW];
     __shared__ int sh_cnt;                  // CAND: bonus candidates listed
-    __shared__ int sh_lb[NW], sh_bw[NW];    // CAND: per-wave lower bounds, third-chunk flags
+    __shared__ int sh_lb[NW], sh_bw[NW];    // CAND: per-wave holder counts, outside flags
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     // m + 0 turns -0 into +0, so that a row maximum of zero is one key and
     // its first id is the lowest of every zero, whatever its sign.
@@ -351,33 +344,21 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     const float Mc = M * c;
 
     // Bonus candidates of row L_b (WG-uniform branch).
-    const bool list_row =
-        CAND && j == (a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K) && P != INT_MAX;
-    // Phase A counts (no writes): ids of the max chunk at or above the
-    // threshold tc, one more when the second chunk can hold some, and whether
-    // a third can.  Rows with too many candidates (flat rows) stop there.
+    const bool list_row = CAND && j == Lb && P != INT_MAX;
+    // Phase A (row L_b): threads whose saved max chunk holds candidates (at
+    // least one each), and whether a candidate could lie outside the saved
+    // chunks.  Flat rows, with far more than kMaxBonusCand, stop there.
     float tc = 0.f;
-    bool need2 = false;
     if (list_row) {
         // the race's key of the top token, in its units (l*c - log2(E/ln2))
         const uint32_t w = draw_u32(philox_key(a.seed), static_cast<uint32_t>(P),
                                     static_cast<uint32_t>(j), static_cast<uint32_t>(b), kTagRace);
         tc = Mc - hw_log2(-hw_log2(lattice_u32f(w))) - kBonusBelow;
-        int lb = 0;
-        if (v0b >= 0 && m * c >= tc) {
-            float xv[N];
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) E::unpack(sh_saved[u][tid], xv + u * EPV);
-#pragma unroll
-            for (int k = 0; k < N; ++k) lb += xv[k] * c >= tc ? 1 : 0;
-        }
-        need2 = it2 >= 0 && m2 * c >= tc;
-        lb += need2 ? 1 : 0;
-        const uint64_t wl = wave_sum_u64(static_cast<uint64_t>(lb));
-        const bool wbad = __ballot(m3 * c >= tc) != 0ull;
+        const uint64_t holders = __ballot(v0b >= 0 && m * c >= tc);
+        const uint64_t outside = __ballot(m2 * c >= tc);
         if (lane == 0) {
-            sh_lb[wv] = static_cast<int>(wl);
-            sh_bw[wv] = wbad ? 1 : 0;
+            sh_lb[wv] = __popcll(holders);
+            sh_bw[wv] = outside != 0ull ? 1 : 0;
         }
     }
     // (2) Every thread rescales its sums to M.  The thread holding the
@@ -415,17 +396,12 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     }
     __syncthreads();
 
-    if (tid == 0) {
-        double r = 0.0, to = 0.0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            r += sh_s[w];
-            to += sh_t[w];
-        }
-        row_emit<ENT>(a, g, row, M, P, r, to, gather, gidx, ltok);
-    }
-    if (CAND && j == (a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K)) {
-        // Phase B: write the list when it is complete and fits.
+    // Phase B (row L_b, after the wave counts are in): write the list when
+    // it is complete and can fit, before thread 0's double-precision finish,
+    // so that the workgroup's other waves need not wait for that.  Rows whose
+    // list cannot fit skip the barrier.
+    bool fits = false;
+    if (CAND && j == Lb) {
         int total = 0, bad = 0;
         if (list_row) {
 #pragma unroll
@@ -434,7 +410,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
                 bad |= sh_bw[w];
             }
         }
-        const bool fits = list_row && !bad && total <= kMaxBonusCand;
+        fits = list_row && !bad && total <= kMaxBonusCand;
         if (fits) {
             int2 *dst = a.cand_list + static_cast<int64_t>(b) * kMaxBonusCand;
             // every id of a chunk at or above the threshold takes the next slot
@@ -457,25 +433,19 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
                 for (int u = 0; u < UNROLL; ++u) vb[u] = sh_saved[u][tid];
                 take(vb, v0b);
             }
-            if (need2) {  // the second chunk, read again
-                uint4 vb[UNROLL];
-                const int v2 = it2 * kChunkVecs + tid;
-                const uint32_t ni = E::pad_word();
-#pragma unroll
-                for (int u = 0; u < UNROLL; ++u) {
-                    const int vi = v2 + u * BLOCK;
-                    if (vi < nfull)
-                        vb[u] = vrow[vi];
-                    else if (vi < nvec)
-                        vb[u] = E::partial(rp, vi, V);
-                    else
-                        vb[u] = make_uint4(ni, ni, ni, ni);
-                }
-                take(vb, v2);
-            }
+            __syncthreads();
         }
-        __syncthreads();
         if (tid == 0) a.cand_cnt[b] = fits && sh_cnt <= kMaxBonusCand ? sh_cnt : -1;
+    }
+
+    if (tid == 0) {
+        double r = 0.0, to = 0.0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            r += sh_s[w];
+            to += sh_t[w];
+        }
+        row_emit<ENT>(a, g, row, M, P, r, to, gather, gidx, ltok);
     }
 }
 
