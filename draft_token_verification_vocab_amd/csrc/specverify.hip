@@ -299,7 +299,7 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     rg.cand = reinterpret_cast<RaceCand *>(w + ws.cand);
     rg.bonus_cnt = bonus_cnt;
     rg.bonus_list = bonus_list;
-    const dim3 grid(rg.segs, B);
+    const dim3 grid(static_cast<unsigned>(rg.segs) * static_cast<unsigned>(B));
     if (p.dtype == SPEC_DTYPE_BF16) {
         race_kernel<uint16_t, kRaceBlock><<<grid, dim3(kRaceBlock), 0, st>>>(rg);
         race_combine_kernel<uint16_t, kSmallBlock><<<dim3(B), dim3(kSmallBlock), 0, st>>>(

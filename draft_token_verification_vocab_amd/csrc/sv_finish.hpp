@@ -346,8 +346,10 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
 
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
-    const int seg = blockIdx.x;
-    const int b = blockIdx.y;
+    // workgroup i: segment i % segs of sequence i / segs (a 1-D grid, so B is
+    // not bound by the grid's y limit)
+    const int b = static_cast<int>(blockIdx.x) / a.segs;
+    const int seg = static_cast<int>(blockIdx.x) - b * a.segs;
     const PhiloxKey key = philox_key(a.seed);
     const int L = a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K;
     const RowPick pk = decide_lossless<T>(a, b, L, key);

@@ -364,6 +364,19 @@ def test_lossless_bonus_at_row_64_and_trimmed():
     assert np_(r.accepted_len).tolist() == [0, 5, 63, 64]
 
 
+@pytest.mark.parametrize("mode", ["lossless", "fly"])
+def test_batch_beyond_grid_y_limit(mode):
+    # B = 70000 sequences (more than a grid's 65535 y extent): every launch
+    # must index sequences along x
+    B, K, V = 70000, 1, 72
+    if mode == "lossless":
+        batch = W.make(1, B=B, K=K, V=V)
+        _lossless_check(batch, seed=9)
+    else:
+        batch = W.make(2, B=B, K=K, V=V)
+        _fly_check(batch, theta=0.3, window=0)
+
+
 def test_lossless_deterministic_across_streams():
     batch = W.make(3, B=16, K=4, V=20000)
     t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
