@@ -476,7 +476,7 @@ __global__ __launch_bounds__(NT) void fly_kernel(const int32_t *tokens, const in
     // wave-uniform bit masks.
     const int lane = threadIdx.x & (kWave - 1);
     const int b = __builtin_amdgcn_readfirstlane(
-        static_cast<int>((blockIdx.x * NT + threadIdx.x) / kWave));
+        static_cast<int>((static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x) / kWave));
     if (b >= B) return;
     const int L = kept_len ? __builtin_amdgcn_readfirstlane(clamp_len(kept_len[b], K)) : K;
     const int32_t *tok = tokens + static_cast<int64_t>(b) * K;
