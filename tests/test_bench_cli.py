@@ -1,0 +1,30 @@
+"""bench.py's contract that holds without a GPU: one GPU only, and the source
+hash that decides whether recorded counter data still applies (a stale record
+is reported as null, not used)."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_source_hash_ignores_comments_and_spacing(tmp_path, monkeypatch):
+    src = tmp_path / "k.hpp"
+    src.write_text("int f(int x) {  // first\n    return x + 1;\n}\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "ROW_PASS_SOURCES", ["k.hpp"])
+    h0 = bench.row_pass_source_hash()
+    src.write_text("int f(int x) {   // another comment\n  return x + 1;\n}\n")
+    assert bench.row_pass_source_hash() == h0
+    src.write_text("int f(int x) {\n    return x + 2;\n}\n")
+    assert bench.row_pass_source_hash() != h0
