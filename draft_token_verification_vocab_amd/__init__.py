@@ -17,7 +17,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "SpecVerifyError", "lib_path", "load", "verify", "av_score", "av_update", "row_stats",
+    "SpecVerifyError", "lib_path", "load", "verify", "av_score", "av_score_stats", "av_update",
+    "row_stats",
     "workspace_bytes", "draft_stats_bytes", "MODE_LOSSLESS", "MODE_FLY",
 ]
 
@@ -44,7 +45,8 @@ class _VerifyOut(ctypes.Structure):
     _fields_ = [("accepted_len", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
                 ("target_lse", ctypes.c_void_p), ("target_entropy", ctypes.c_void_p),
                 ("target_argmax", ctypes.c_void_p), ("draft_lse", ctypes.c_void_p),
-                ("draft_qmax", ctypes.c_void_p), ("draft_feat", ctypes.c_void_p)]
+                ("draft_qmax", ctypes.c_void_p), ("draft_feat", ctypes.c_void_p),
+                ("draft_stats_out", ctypes.c_void_p)]
 
 
 # Every symbol the header declares, with its ctypes signature.
@@ -57,6 +59,8 @@ _SIGNATURES = {
                                      ctypes.c_size_t, _P]),
     "spec_av_score": (ctypes.c_int32, [_P, _P, ctypes.POINTER(_Params), _P, ctypes.c_float,
                                        _P, _P, _P, _P, _P]),
+    "spec_av_score_stats": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, _P,
+                                             ctypes.c_float, _P, _P, _P, _P]),
     "spec_av_update": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_float, _P, _P]),
     "spec_row_stats": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
@@ -161,6 +165,9 @@ class VerifyResult:
     draft_lse: Optional[torch.Tensor] = None
     draft_qmax: Optional[torch.Tensor] = None
     draft_feat: Optional[torch.Tensor] = None
+    # a draft-statistics buffer (draft_stats_bytes) that a lossless call reading
+    # the draft rows itself also fills
+    draft_stats_out: Optional[torch.Tensor] = None
 
 
 def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
@@ -202,7 +209,7 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
                 out.draft_feat = torch.empty(B, K, dtype=torch.float32, device=dev)
     o = _VerifyOut(*[None if t is None else t.data_ptr() for t in (
         out.accepted_len, out.tokens, out.target_lse, out.target_entropy, out.target_argmax,
-        out.draft_lse, out.draft_qmax, out.draft_feat)])
+        out.draft_lse, out.draft_qmax, out.draft_feat, out.draft_stats_out)])
     need = int(L.spec_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -239,7 +246,7 @@ class VerifyCall:
         self.out = out
         self.vout = _VerifyOut(*[None if t is None else t.data_ptr() for t in (
             out.accepted_len, out.tokens, out.target_lse, out.target_entropy, out.target_argmax,
-            out.draft_lse, out.draft_qmax, out.draft_feat)])
+            out.draft_lse, out.draft_qmax, out.draft_feat, out.draft_stats_out)])
         need = int(self.L.spec_workspace_bytes(ctypes.byref(self.params)))
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -285,13 +292,38 @@ def av_score(draft: torch.Tensor, draft_tokens: torch.Tensor, omega_beta: torch.
     return conf, mask, kept, draft_stats
 
 
+def av_score_stats(draft_stats: torch.Tensor, B: int, K: int, omega_beta: torch.Tensor,
+                   tau: float):
+    """Confidences and trimming from an already filled draft-statistics buffer
+    (no row is read).  Returns (conf [B,K] float, keep_mask [B,K] uint8,
+    kept_len [B] int32)."""
+    for t, n in ((draft_stats, "draft_stats"), (omega_beta, "omega_beta")):
+        _need_cuda(t, n)
+    if draft_stats.numel() * draft_stats.element_size() < draft_stats_bytes(B, K):
+        raise ValueError("draft_stats must hold spec_draft_stats_bytes(B, K) bytes")
+    dev = draft_stats.device
+    conf = torch.empty(B, K, dtype=torch.float32, device=dev)
+    mask = torch.empty(B, K, dtype=torch.uint8, device=dev)
+    kept = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(load().spec_av_score_stats(_ptr(draft_stats), int(B), int(K), _ptr(omega_beta),
+                                      float(tau), _ptr(conf), _ptr(mask), _ptr(kept),
+                                      _stream(dev)), "spec_av_score_stats")
+    return conf, mask, kept
+
+
 class AvStepCall:
     """One adaptive-verification step (score and trim, verify, SGD update)
     with its arguments marshalled once and its buffers allocated once: the
     buffers of one batch of draft and target logits, verified again and again
     (a serving loop that refills them in place, a benchmark).  Calling it
-    enqueues spec_av_score, spec_verify and spec_av_update on the stream that
-    was current at construction; omega_beta is updated in place."""
+    enqueues the step on the stream that was current at construction;
+    omega_beta is updated in place.
+
+    With tau > 0: spec_av_score (draft rows), spec_verify on the kept drafts,
+    spec_av_update.  With tau <= 0 nothing can be trimmed, so spec_verify
+    reads target and draft rows in one pass and exports the draft statistics,
+    spec_av_score_stats scores from them, and spec_av_update follows: the
+    same results with one row pass instead of two."""
 
     def __init__(self, target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
                  omega_beta: torch.Tensor, tau: float, lr: float, *, temperature: float = 1.0,
@@ -308,20 +340,34 @@ class AvStepCall:
         self.stats = torch.empty(max(int(L.spec_draft_stats_bytes(B, K)), 16), dtype=torch.uint8,
                                  device=dev)
         self.params = _params(B, K, V, S, _dtype_code(draft), temperature)
+        self.fused = not (float(tau) > 0.0)
         st = _stream(dev)
-        self.score_args = (_ptr(draft), _ptr(draft_tokens), ctypes.byref(self.params),
-                           _ptr(omega_beta), float(tau), _ptr(self.conf), _ptr(self.mask),
-                           _ptr(self.kept), _ptr(self.stats), st)
-        self.verify = VerifyCall(target, draft, draft_tokens, temperature=temperature,
-                                 kept_len=self.kept, draft_stats=self.stats, vocab=vocab,
-                                 workspace=workspace)
+        if self.fused:
+            out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                               torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+            out.draft_stats_out = self.stats
+            self.verify = VerifyCall(target, draft, draft_tokens, temperature=temperature,
+                                     vocab=vocab, workspace=workspace, out=out)
+            self.score_args = (_ptr(self.stats), int(B), int(K), _ptr(omega_beta), float(tau),
+                               _ptr(self.conf), _ptr(self.mask), _ptr(self.kept), st)
+        else:
+            self.score_args = (_ptr(draft), _ptr(draft_tokens), ctypes.byref(self.params),
+                               _ptr(omega_beta), float(tau), _ptr(self.conf), _ptr(self.mask),
+                               _ptr(self.kept), _ptr(self.stats), st)
+            self.verify = VerifyCall(target, draft, draft_tokens, temperature=temperature,
+                                     kept_len=self.kept, draft_stats=self.stats, vocab=vocab,
+                                     workspace=workspace)
         self.update_args = (_ptr(self.stats), _ptr(self.verify.out.accepted_len),
                             _ptr(self.kept), int(B), int(K), float(lr), _ptr(omega_beta), st)
         self._keep = (target, draft, draft_tokens, omega_beta)
 
     def __call__(self, seed: int = 0) -> VerifyResult:
-        _check(self.L.spec_av_score(*self.score_args), "spec_av_score")
-        r = self.verify(seed)
+        if self.fused:
+            r = self.verify(seed)
+            _check(self.L.spec_av_score_stats(*self.score_args), "spec_av_score_stats")
+        else:
+            _check(self.L.spec_av_score(*self.score_args), "spec_av_score")
+            r = self.verify(seed)
         _check(self.L.spec_av_update(*self.update_args), "spec_av_update")
         return r
 

@@ -216,8 +216,10 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     float *t_h = reinterpret_cast<float *>(w + ws.t_h);
     int32_t *t_am = reinterpret_cast<int32_t *>(w + ws.t_am);
     const size_t n = static_cast<size_t>(B) * K;
-    DraftStats ds = draft_stats_view(
-        own_draft ? static_cast<void *>(w + ws.dstats) : const_cast<void *>(draft_stats), n);
+    if (out->draft_stats_out && !aligned16(out->draft_stats_out)) return SPEC_ERR_ARG;
+    void *own_stats = out->draft_stats_out ? out->draft_stats_out : static_cast<void *>(w + ws.dstats);
+    DraftStats ds =
+        draft_stats_view(own_draft ? own_stats : const_cast<void *>(draft_stats), n);
 
     const float c = log2e_over(p.temperature);
     RowArgs ra{};
@@ -351,6 +353,22 @@ spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,
     if ((s = launch_status()) != SPEC_OK) return s;
     av_score_kernel<<<dim3((B + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock), 0, st>>>(
         ds.feat, B, K, omega_beta, tau, conf, keep_mask, kept_len);
+    return launch_status();
+}
+
+spec_status spec_av_score_stats(const void *draft_stats, int32_t batch, int32_t num_draft,
+                                const float *omega_beta, float tau, float *conf,
+                                uint8_t *keep_mask, int32_t *kept_len, void *stream) {
+    if (batch < 0 || num_draft < 1) return SPEC_ERR_ARG;
+    if (num_draft > 64) return SPEC_ERR_UNSUPPORTED;
+    if (std::isnan(tau)) return SPEC_ERR_ARG;
+    if (batch == 0) return SPEC_OK;
+    if (!draft_stats || !aligned16(draft_stats) || !omega_beta) return SPEC_ERR_ARG;
+    const size_t n = static_cast<size_t>(batch) * num_draft;
+    DraftStats ds = draft_stats_view(const_cast<void *>(draft_stats), n);
+    av_score_kernel<<<dim3((batch + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock), 0,
+                      static_cast<hipStream_t>(stream)>>>(ds.feat, batch, num_draft, omega_beta,
+                                                         tau, conf, keep_mask, kept_len);
     return launch_status();
 }
 

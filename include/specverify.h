@@ -93,6 +93,12 @@ typedef struct spec_verify_out {
     float *draft_lse;        /* [B][K] (only when spec_verify reads draft rows)  */
     float *draft_qmax;       /* [B][K] probability of the draft's top token      */
     float *draft_feat;       /* [B][K] logit(q_max), clamped to <= 126 log 2     */
+    void *draft_stats_out;   /* device or NULL (16-byte aligned): when the call
+                                reads the draft rows itself (lossless mode,
+                                draft_stats NULL), their statistics are written
+                                here as well, in the layout of
+                                spec_draft_stats_bytes, for spec_av_score_stats
+                                and spec_av_update                              */
 } spec_verify_out;
 
 /* Bytes of device workspace spec_verify needs for `params` (0 if invalid). */
@@ -178,6 +184,20 @@ spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,
  * or NULL (= K); omega_beta: device float[K+1], updated in place.  Single
  * workgroup (a wave per position), fixed-order double-precision sums.
  */
+/*
+ * spec_av_score_stats -- the scoring and trimming of spec_av_score from
+ * draft statistics that are already computed (by spec_av_score, or by
+ * spec_verify through draft_stats_out), without reading any draft row:
+ * conf, keep_mask and kept_len as in spec_av_score (each nullable).  With
+ * tau <= 0 nothing is trimmed, so a step can verify first (one row pass over
+ * target and draft rows, exporting the draft statistics) and score after.
+ * draft_stats: device, spec_draft_stats_bytes(batch, num_draft), 16-byte
+ * aligned; omega_beta: device float[K+1].
+ */
+spec_status spec_av_score_stats(const void *draft_stats, int32_t batch, int32_t num_draft,
+                                const float *omega_beta, float tau, float *conf,
+                                uint8_t *keep_mask, int32_t *kept_len, void *stream);
+
 spec_status spec_av_update(const void *draft_stats, const int32_t *accepted_len,
                            const int32_t *kept_len, int32_t batch, int32_t num_draft, float lr,
                            float *omega_beta, void *stream);

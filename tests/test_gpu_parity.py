@@ -436,6 +436,51 @@ def test_av_score_update_parity_c1_recipe():
     assert np.allclose(got, want, rtol=0, atol=1e-5), (got, want)
 
 
+@pytest.mark.parametrize("tau", [0.0, 0.2])
+def test_av_step_call_matches_separate_calls(tau):
+    # AvStepCall with tau <= 0 verifies first (one row pass over target and
+    # draft rows, exporting the draft statistics) and scores from them; with
+    # tau > 0 it scores, trims and verifies.  Either way: bit-identical to the
+    # separate calls, over three steps with carried parameters.
+    batch = W.make(1, B=20, K=5, V=7001, stride=7008)
+    t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
+    B, K = tok.shape
+    ob_a = torch.tensor(W.av_init(1), dtype=torch.float32, device=DEV)
+    ob_b = ob_a.clone()
+    call = sv.AvStepCall(t, d, tok, ob_a, tau, 0.05, vocab=batch.V)
+    assert call.fused == (tau <= 0.0)
+    for step in range(3):
+        r_a = call(step)
+        conf, mask, kept, ds = sv.av_score(d, tok, ob_b, tau, vocab=batch.V)
+        r_b = sv.verify(t, d, tok, seed=step, vocab=batch.V, kept_len=kept, draft_stats=ds)
+        sv.av_update(ds, r_b.accepted_len, kept, ob_b, 0.05, B, K)
+        torch.cuda.synchronize()
+        assert torch.equal(r_a.accepted_len, r_b.accepted_len)
+        assert torch.equal(r_a.tokens, r_b.tokens)
+        assert torch.equal(call.conf, conf) and torch.equal(call.kept, kept)
+        assert torch.equal(call.mask, mask)
+        assert torch.equal(call.stats[:24 * B * K], ds[:24 * B * K])
+        assert torch.equal(ob_a, ob_b)
+
+
+def test_verify_exports_draft_stats():
+    # the draft statistics a lossless call computes itself, exported, equal
+    # those of spec_av_score bit for bit; scoring from them equals spec_av_score
+    batch = W.make(3, B=10, K=4, V=5003, stride=5008)
+    t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
+    B, K = tok.shape
+    ob = torch.tensor(W.av_init(1, K=K), dtype=torch.float32, device=DEV)
+    out = sv.VerifyResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                          torch.empty(B, K + 1, dtype=torch.int32, device=DEV))
+    out.draft_stats_out = torch.zeros(sv.draft_stats_bytes(B, K), dtype=torch.uint8, device=DEV)
+    sv.verify(t, d, tok, seed=1, temperature=0.7, vocab=batch.V, out=out)
+    conf, mask, kept, ds = sv.av_score(d, tok, ob, 0.3, temperature=0.7, vocab=batch.V)
+    c2, m2, k2 = sv.av_score_stats(out.draft_stats_out, B, K, ob, 0.3)
+    torch.cuda.synchronize()
+    assert torch.equal(out.draft_stats_out[:24 * B * K], ds[:24 * B * K])
+    assert torch.equal(c2, conf) and torch.equal(m2, mask) and torch.equal(k2, kept)
+
+
 def test_av_pipeline_full_size_steps():
     # the B=1024 K=8 adaptive-verification pipeline at full size, three steps
     # with fresh inputs, parameters carried over as the pipeline does
