@@ -141,9 +141,6 @@ __device__ __forceinline__ RowPick decide_lossless(const RaceArgs &a, int b, int
 // log2 weight by more.
 constexpr float kMaxNegLogE = 23.5f;
 
-// Vectors per thread per trip of the race (two measured no faster).
-constexpr int kRaceUnroll = 1;
-
 // The key the race gives the target's top token am (logits xt, xd there),
 // less the screening margin: a floor that the row's best key is known to
 // reach.  -inf when am has no weight (then nothing is screened out).
@@ -166,17 +163,17 @@ __device__ __forceinline__ float race_floor(bool residual, int am, float xt, flo
     return lw - hw_log2(e2) - kScreenMargin;
 }
 
-// Race over vectors [v_lo, v_hi) of one row (pair) with NT threads, R
-// vectors per thread per trip.  residual: w = max(0, p - q) from the target
-// and draft rows; otherwise w = p of the target row.  am: the target's top
-// token (am_xt, am_xd: its logits), whose key (less the margin) is a floor
-// the row's best is known to reach.  Returns (in thread 0) the best double key and id, or id -1 when no
-// id of the range can win.
-template <typename T, int NT, int R>
-__device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo, int v_hi, int V,
-                           float c, double cd, double inv_t, double lse2_t, double lse2_d,
-                           PhiloxKey key, uint32_t pos, uint32_t seq, int am, float am_xt,
-                           float am_xd, double *out_key, int *out_x) {
+// Race over vectors [v_lo, v_hi) of one row (pair) with NT threads, one
+// vector per thread per trip.  RES: w = max(0, p - q) from the target and
+// draft rows; otherwise w = p of the target row.  am: the target's top token
+// (am_xt, am_xd: its logits), whose key (less the margin) is a floor the
+// row's best is known to reach.  Returns (in thread 0) the best double key
+// and id, or id -1 when no id of the range can win.
+template <typename T, int NT, bool RES>
+__device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int V, float c,
+                           double cd, double inv_t, double lse2_t, double lse2_d, PhiloxKey key,
+                           uint32_t pos, uint32_t seq, int am, float am_xt, float am_xd,
+                           double *out_key, int *out_x) {
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
     constexpr int NW = NT / kWave;
@@ -186,24 +183,24 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     const uint4 *dv = reinterpret_cast<const uint4 *>(drow);
     const float lt2 = static_cast<float>(lse2_t);
     const float ld2 = static_cast<float>(lse2_d);
-    const int nv = v_hi - v_lo;
-    const int trips = (nv + NT * R - 1) / (NT * R);  // wave-uniform: the skip tests are ballots
-    // Vector r of a thread's trip `it` is v_lo + (it*R + r)*NT + tid.  The
-    // next trip's vectors are loaded before this trip's arithmetic.
-    auto fetch = [&](int it, uint4 (&tq)[R], uint4 (&dq)[R]) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int vi = v_lo + (it * R + r) * NT + tid;
-            const int vl = vi < v_hi ? vi : v_lo;
-            tq[r] = vl < nfull ? load_stream(tv + vl) : E::partial(trow, vl, V);
-            if (residual) dq[r] = vl < nfull ? load_stream(dv + vl) : E::partial(drow, vl, V);
-        }
+    // Whole trips cover full vectors only (every thread has one); one last
+    // trip takes the rest, the row's partial vector included.  The whole
+    // trips' loads are unconditional, so that the wait before a trip's
+    // arithmetic covers its own vectors and not the next trip's.
+    const int v_hf = min(v_hi, nfull);
+    const int nit = v_hf > v_lo ? (v_hf - v_lo) / NT : 0;
+    struct Vec {
+        uint4 t, d;
     };
-    uint4 tn[R], dn[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) tn[r] = dn[r] = make_uint4(0u, 0u, 0u, 0u);
-    if (trips > 0) fetch(0, tn, dn);
-    const float floor = race_floor(residual, am, am_xt, am_xd, c, lse2_t, lse2_d, key, pos, seq);
+    auto load_trip = [&](Vec &q, int it) {
+        const int vi = v_lo + it * NT + tid;
+        q.t = load_stream(tv + vi);
+        if (RES) q.d = load_stream(dv + vi);
+    };
+    Vec qa, qb;
+    qa.t = qa.d = qb.t = qb.d = make_uint4(0u, 0u, 0u, 0u);
+    if (nit > 0) load_trip(qa, 0);
+    const float floor = race_floor(RES, am, am_xt, am_xd, c, lse2_t, lse2_d, key, pos, seq);
 
     // best: this lane's best screening key; thr: the wave's best less the
     // margin.  An id whose key cannot reach thr is never a candidate, so it
@@ -218,60 +215,49 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
     // FMA per id: the key is below lb + 0.5 + (leading ones), so an id is a
     // candidate only if its leading ones reach a; a block of four needs its
     // draw only if some a <= 23 (lb + 23.5 >= thr).
-    const float lsub = residual ? lt2 : 0.f;
+    const float lsub = RES ? lt2 : 0.f;
     float abase = thr - 0.5f + lsub;
-    for (int it = 0; it < trips; ++it) {
-        uint4 tq[R], dq[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            tq[r] = tn[r];
-            dq[r] = dn[r];
-        }
-        if (it + 1 < trips) fetch(it + 1, tn, dn);
+    // One trip over vector vi (live: vi is in the range).  Wave-uniform: the
+    // skip tests are ballots.
+    auto trip = [&](const Vec &q, int vi, bool live) {
         bool evaluated = false;
+        float xt[EPV], av[EPV];
+        E::unpack(q.t, xt);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int vi = v_lo + (it * R + r) * NT + tid;
-            const bool live = vi < v_hi;
-            float xt[EPV], av[EPV];
-            E::unpack(tq[r], xt);
+        for (int k = 0; k < EPV; ++k) av[k] = fmaf(xt[k], -c, abase);
 #pragma unroll
-            for (int k = 0; k < EPV; ++k) av[k] = fmaf(xt[k], -c, abase);
+        for (int blk = 0; blk < EPV / 4; ++blk) {
+            const uint32_t base = static_cast<uint32_t>(live ? vi : v_lo) * EPV + blk * 4;
+            const float amin = fminf(fminf(av[blk * 4], av[blk * 4 + 1]),
+                                     fminf(av[blk * 4 + 2], av[blk * 4 + 3]));
+            const bool need = live && amin <= kMaxNegLogE - 0.5f;
+            if (__ballot(need) == 0ull) continue;  // no lane's block can win: no draws
+            const uint4 rw = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
+            const uint32_t w4[4] = {rw.x, rw.y, rw.z, rw.w};
 #pragma unroll
-            for (int blk = 0; blk < EPV / 4; ++blk) {
-                const uint32_t base = static_cast<uint32_t>(live ? vi : v_lo) * EPV + blk * 4;
-                const float amin = fminf(fminf(av[blk * 4], av[blk * 4 + 1]),
-                                         fminf(av[blk * 4 + 2], av[blk * 4 + 3]));
-                const bool need = live && amin <= kMaxNegLogE - 0.5f;
-                if (__ballot(need) == 0ull) continue;  // no lane's block can win: no draws
-                const uint4 rw = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
-                const uint32_t w4[4] = {rw.x, rw.y, rw.z, rw.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int k = blk * 4 + q;
-                    const bool cand =
-                        need && static_cast<float>(leading_ones(w4[q])) >= av[k];
-                    const int x = static_cast<int>(base) + q;
-                    if (cand && x < V) {
-                        float lw;
-                        if (residual) {
-                            const float p = hw_exp2(fmaf(xt[k], c, -lt2));
-                            const float qq = hw_exp2(fmaf(E::elem(dq[r], k), c, -ld2));
-                            const float w = p - qq;
-                            lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
-                        } else {
-                            lw = xt[k] * c;  // log2 p + the row's normaliser
-                        }
-                        const float e2 = -hw_log2(lattice_u32f(w4[q]));  // E / ln 2 > 0
-                        const float g = lw - hw_log2(e2);
-                        if (g > best) {
-                            best = g;
-                            bx = x;
-                            bt = xt[k];
-                            if (residual) bd = E::elem(dq[r], k);
-                        }
-                        evaluated = true;
+            for (int qi = 0; qi < 4; ++qi) {
+                const int k = blk * 4 + qi;
+                const bool cand = need && static_cast<float>(leading_ones(w4[qi])) >= av[k];
+                const int x = static_cast<int>(base) + qi;
+                if (cand && x < V) {
+                    float lw;
+                    if (RES) {
+                        const float p = hw_exp2(fmaf(xt[k], c, -lt2));
+                        const float qq = hw_exp2(fmaf(E::elem(q.d, k), c, -ld2));
+                        const float w = p - qq;
+                        lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
+                    } else {
+                        lw = xt[k] * c;  // log2 p + the row's normaliser
                     }
+                    const float e2 = -hw_log2(lattice_u32f(w4[qi]));  // E / ln 2 > 0
+                    const float g = lw - hw_log2(e2);
+                    if (g > best) {
+                        best = g;
+                        bx = x;
+                        bt = xt[k];
+                        if (RES) bd = E::elem(q.d, k);
+                    }
+                    evaluated = true;
                 }
             }
         }
@@ -279,6 +265,34 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
             thr = fmaxf(thr, from_ordered_bits(wave_max_u32(ordered_bits(best))) - kScreenMargin);
             abase = thr - 0.5f + lsub;
         }
+    };
+    int it = 0;
+    for (; it + 2 < nit; it += 2) {
+        load_trip(qb, it + 1);
+        trip(qa, v_lo + it * NT + tid, true);
+        load_trip(qa, it + 2);
+        trip(qb, v_lo + (it + 1) * NT + tid, true);
+    }
+    if (it + 1 < nit) {
+        load_trip(qb, it + 1);
+        trip(qa, v_lo + it * NT + tid, true);
+        trip(qb, v_lo + (it + 1) * NT + tid, true);
+    } else if (it < nit) {
+        trip(qa, v_lo + it * NT + tid, true);
+    }
+    if (v_lo + nit * NT < v_hi) {  // the rest of the range, fewer vectors than threads
+        const int vi = v_lo + nit * NT + tid;
+        const bool live = vi < v_hi;
+        Vec q;
+        q.t = q.d = make_uint4(0u, 0u, 0u, 0u);
+        if (vi < v_hf) {
+            q.t = load_stream(tv + vi);
+            if (RES) q.d = load_stream(dv + vi);
+        } else if (live) {
+            q.t = E::partial(trow, vi, V);
+            if (RES) q.d = E::partial(drow, vi, V);
+        }
+        trip(q, vi, live);
     }
 
     // Workgroup maximum of the screening keys.
@@ -302,7 +316,7 @@ __device__ void race_range(const T *trow, const T *drow, bool residual, int v_lo
         const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(bx), pos, seq, kTagRace));
         const double lnE = log(-log(u));
         const double lt = static_cast<double>(bt);
-        if (residual) {
+        if (RES) {
             const double ld = static_cast<double>(bd);
             const double w = exp2(lt * cd - lse2_t) - exp2(ld * cd - lse2_d);
             if (w > 0.0) {
@@ -401,10 +415,14 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     const int v_hi = min(nvec, v_lo + a.seg_vecs);
     double k;
     int x;
-    race_range<T, NT, kRaceUnroll>(trow, drow, residual, v_lo, v_hi, a.V, a.c,
-                                   static_cast<double>(a.c), a.inv_t, pk.lt,
-                                   residual ? pk.ld : 0.0, key, jstar, b, pk.am, pk.xt, pk.xd,
-                                   &k, &x);
+    if (residual)
+        race_range<T, NT, true>(trow, drow, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
+                                a.inv_t, pk.lt, pk.ld, key, jstar, b, pk.am, pk.xt, pk.xd, &k,
+                                &x);
+    else
+        race_range<T, NT, false>(trow, nullptr, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
+                                 a.inv_t, pk.lt, 0.0, key, jstar, b, pk.am, pk.xt, pk.xd, &k,
+                                 &x);
     if (threadIdx.x == 0) a.cand[b * a.segs + seg] = RaceCand{k, x, jstar};
 }
 
@@ -444,9 +462,9 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
         int x;
         const int am = a.t_am[b * (a.K + 1) + jstar];
         const float am_xt = am >= 0 && am < a.V ? Elem<T>::at(trow, am) : -__builtin_inff();
-        race_range<T, NT, 1>(trow, nullptr, false, 0, nvec, a.V, a.c, static_cast<double>(a.c),
-                             a.inv_t, lt, 0.0, key, jstar, b, am, am_xt, -__builtin_inff(), &k,
-                             &x);
+        race_range<T, NT, false>(trow, nullptr, 0, nvec, a.V, a.c, static_cast<double>(a.c),
+                                 a.inv_t, lt, 0.0, key, jstar, b, am, am_xt, -__builtin_inff(),
+                                 &k, &x);
         if (tid == 0) s_y = x;
         __syncthreads();
     }
