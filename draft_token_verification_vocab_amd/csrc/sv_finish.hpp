@@ -358,100 +358,75 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
     __syncthreads();
 }
 
-template <typename T, int NT>
-__global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
-    // workgroup i: segment i % segs of sequence i / segs (a 1-D grid, so B is
-    // not bound by the grid's y limit)
-    const int b = static_cast<int>(blockIdx.x) / a.segs;
-    const int seg = static_cast<int>(blockIdx.x) - b * a.segs;
-    const PhiloxKey key = philox_key(a.seed);
-    const int L = a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K;
-    const RowPick pk = decide_lossless<T>(a, b, L, key);
-    const int jstar = pk.jstar;
-    const bool residual = jstar < L;
-    if (!residual && a.bonus_cnt) {
-        const int n = a.bonus_cnt[b];
-        if (n >= 0) {
-            // A draw from p at row L over the listed ids, which hold every id
-            // that could win it: exact double keys, no second read of the row.
-            if (seg == 0) {
-                const int tid = threadIdx.x;
-                if (tid < kWave) {
-                    double k64 = -__builtin_inf();
-                    int kx = INT_MAX;
-                    if (tid < n) {
-                        const int2 e = a.bonus_list[static_cast<int64_t>(b) * kMaxBonusCand + tid];
-                        const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(e.x),
-                                                              static_cast<uint32_t>(jstar),
-                                                              static_cast<uint32_t>(b), kTagRace));
-                        k64 = static_cast<double>(__int_as_float(e.y)) * a.inv_t - log(-log(u));
-                        kx = e.x;
-                    }
+// A draw from p at row L over the ids the row pass listed, which hold every
+// id that could win it: exact double keys, no second read of the row.  The
+// first wave does it; the key and id (-1: none) land in thread 0.
+__device__ __forceinline__ void race_listed(const RaceArgs &a, int b, int jstar, int n,
+                                            PhiloxKey key, double *out_key, int *out_x) {
+    const int tid = threadIdx.x;
+    if (tid >= kWave) return;
+    double k64 = -__builtin_inf();
+    int kx = INT_MAX;
+    if (tid < n) {
+        const int2 e = a.bonus_list[static_cast<int64_t>(b) * kMaxBonusCand + tid];
+        const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(e.x),
+                                              static_cast<uint32_t>(jstar),
+                                              static_cast<uint32_t>(b), kTagRace));
+        k64 = static_cast<double>(__int_as_float(e.y)) * a.inv_t - log(-log(u));
+        kx = e.x;
+    }
 #pragma unroll
-                    for (int msk = kWave / 2; msk > 0; msk >>= 1) {
-                        const double ok = __shfl_xor(k64, msk, kWave);
-                        const int ox = __shfl_xor(kx, msk, kWave);
-                        if (ok > k64 || (ok == k64 && ox < kx)) {
-                            k64 = ok;
-                            kx = ox;
-                        }
-                    }
-                    if (tid == 0)
-                        a.cand[b * a.segs] = RaceCand{k64, kx == INT_MAX ? -1 : kx, jstar};
-                }
-            } else if (threadIdx.x == 0) {
-                a.cand[b * a.segs + seg] = RaceCand{-__builtin_inf(), -1, jstar};
-            }
-            return;
+    for (int msk = kWave / 2; msk > 0; msk >>= 1) {
+        const double ok = __shfl_xor(k64, msk, kWave);
+        const int ox = __shfl_xor(kx, msk, kWave);
+        if (ok > k64 || (ok == k64 && ox < kx)) {
+            k64 = ok;
+            kx = ox;
         }
     }
-    const T *trow = static_cast<const T *>(a.target) +
-                    (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
-    const T *drow = residual ? static_cast<const T *>(a.draft) +
-                                   (static_cast<int64_t>(b) * a.K + jstar) * a.stride
-                             : nullptr;
-    const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
-    const int v_lo = seg * a.seg_vecs;
-    const int v_hi = min(nvec, v_lo + a.seg_vecs);
-    double k;
-    int x;
-    if (residual)
-        race_range<T, NT, true>(trow, drow, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
-                                a.inv_t, pk.lt, pk.ld, key, jstar, b, pk.am, pk.xt, pk.xd, &k,
-                                &x);
-    else
-        race_range<T, NT, false>(trow, nullptr, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
-                                 a.inv_t, pk.lt, 0.0, key, jstar, b, pk.am, pk.xt, pk.xd, &k,
-                                 &x);
-    if (threadIdx.x == 0) a.cand[b * a.segs + seg] = RaceCand{k, x, jstar};
+    if (tid == 0) {
+        *out_key = k64;
+        *out_x = kx == INT_MAX ? -1 : kx;
+    }
 }
 
-// Best segment per sequence; writes accepted_len and the emitted tokens.  A
-// residual that vanished in floating point (only possible within rounding of
-// u_j = p/q) falls back to a race over p at the same row.
+// The listed candidates of sequence b, or -1 when the race reads the row:
+// only a draw from p (no rejection) at row L can use them.
+__device__ __forceinline__ int listed_count(const RaceArgs &a, int b, bool residual) {
+    return !residual && a.bonus_cnt ? a.bonus_cnt[b] : -1;
+}
+
+// Race over vectors [v_lo, v_hi) of sequence b's row at the decided position.
 template <typename T, int NT>
-__global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int32_t *tokens,
-                                                         int32_t *accepted_len,
-                                                         int32_t *out_tokens) {
-    const int b = blockIdx.x;
+__device__ __forceinline__ void race_decided(const RaceArgs &a, int b, const RowPick &pk,
+                                             bool residual, PhiloxKey key, int v_lo, int v_hi,
+                                             double *k, int *x) {
+    const int jstar = pk.jstar;
+    const T *trow = static_cast<const T *>(a.target) +
+                    (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
+    if (residual) {
+        const T *drow = static_cast<const T *>(a.draft) +
+                        (static_cast<int64_t>(b) * a.K + jstar) * a.stride;
+        race_range<T, NT, true>(trow, drow, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
+                                a.inv_t, pk.lt, pk.ld, key, jstar, b, pk.am, pk.xt, pk.xd, k, x);
+    } else {
+        race_range<T, NT, false>(trow, nullptr, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
+                                 a.inv_t, pk.lt, 0.0, key, jstar, b, pk.am, pk.xt, pk.xd, k, x);
+    }
+}
+
+// Writes accepted_len and the emitted tokens of sequence b, given the race's
+// winner y (valid in thread 0).  A residual that vanished in floating point
+// (y < 0; only possible within rounding of u_j = p/q) falls back to a race
+// over p at the same row.
+template <typename T, int NT>
+__device__ __forceinline__ void emit_sequence(const RaceArgs &a, int b, int jstar, int y,
+                                              const int32_t *tokens, int32_t *accepted_len,
+                                              int32_t *out_tokens) {
     const int tid = threadIdx.x;
     __shared__ int s_y;
-    __shared__ int s_j;
-    if (tid == 0) {
-        double bk = -__builtin_inf();
-        int bx = INT_MAX;
-        for (int s = 0; s < a.segs; ++s) {
-            const RaceCand cnd = a.cand[b * a.segs + s];
-            if (cnd.x >= 0 && (cnd.key > bk || (cnd.key == bk && cnd.x < bx))) {
-                bk = cnd.key;
-                bx = cnd.x;
-            }
-        }
-        s_y = bx == INT_MAX ? -1 : bx;
-        s_j = a.cand[b * a.segs].jstar;
-    }
+    if (tid == 0) s_y = y;
     __syncthreads();
-    const int jstar = s_j;
     if (s_y < 0) {
         const T *trow = static_cast<const T *>(a.target) +
                         (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
@@ -477,6 +452,57 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
             v = s_y;
         out_tokens[b * (a.K + 1) + j] = v;
     }
+}
+
+// Segmented race: workgroup i takes segment i % segs of sequence i / segs (a
+// 1-D grid, so B is not bound by the grid's y limit) and reports its best
+// candidate; race_combine_kernel then picks each sequence's winner.
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
+    const int b = static_cast<int>(blockIdx.x) / a.segs;
+    const int seg = static_cast<int>(blockIdx.x) - b * a.segs;
+    const PhiloxKey key = philox_key(a.seed);
+    const int L = a.kept_len ? clamp_len(a.kept_len[b], a.K) : a.K;
+    const RowPick pk = decide_lossless<T>(a, b, L, key);
+    const int jstar = pk.jstar;
+    const bool residual = jstar < L;
+    const int n = listed_count(a, b, residual);
+    double k = -__builtin_inf();
+    int x = -1;
+    if (n >= 0) {
+        if (seg == 0) race_listed(a, b, jstar, n, key, &k, &x);
+    } else {
+        const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
+        const int v_lo = seg * a.seg_vecs;
+        race_decided<T, NT>(a, b, pk, residual, key, v_lo, min(nvec, v_lo + a.seg_vecs), &k, &x);
+    }
+    if (threadIdx.x == 0) a.cand[b * a.segs + seg] = RaceCand{k, x, jstar};
+}
+
+// Best segment per sequence; writes accepted_len and the emitted tokens.
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int32_t *tokens,
+                                                         int32_t *accepted_len,
+                                                         int32_t *out_tokens) {
+    const int b = blockIdx.x;
+    int y = -1, jstar = 0;
+    if (threadIdx.x == 0) {
+        double bk = -__builtin_inf();
+        int bx = INT_MAX;
+        for (int s = 0; s < a.segs; ++s) {
+            const RaceCand cnd = a.cand[b * a.segs + s];
+            if (cnd.x >= 0 && (cnd.key > bk || (cnd.key == bk && cnd.x < bx))) {
+                bk = cnd.key;
+                bx = cnd.x;
+            }
+        }
+        y = bx == INT_MAX ? -1 : bx;
+        jstar = a.cand[b * a.segs].jstar;
+    }
+    __shared__ int s_j;
+    if (threadIdx.x == 0) s_j = jstar;
+    __syncthreads();
+    emit_sequence<T, NT>(a, b, s_j, y, tokens, accepted_len, out_tokens);
 }
 
 // FLy: a deviation is a draft token different from the target's top token.

@@ -265,15 +265,22 @@ def test_lossless_masked_vocab():
         assert tok[b, acc[b]] % 3 != 0
 
 
+# A short row (two race segments per sequence at these batch sizes) and a
+# long one (34 segments): the segment boundaries and the combine's choice
+# among many segments both get exercised.
+RACE_SHAPES = [(5003, 5008), (70003, 70008)]
+
+
+@pytest.mark.parametrize("V,stride", RACE_SHAPES)
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_lossless_race_without_floor(dtype):
+def test_lossless_race_without_floor(dtype, V, stride):
     # The draft puts far more mass than the target on the target's top token,
     # so max(0, p - q) is 0 there and the race starts with no floor; the
     # target's last 40% of ids are masked (no residual mass in the last
     # segments) and V leaves a ragged last vector.  The first draft token is
     # that top token, so most sequences reject at position 0.
-    B, K, V = 24, 2, 5003
-    batch = W.make(1, B=B, K=K, V=V, stride=5008)
+    B, K = 24, 2
+    batch = W.make(1, B=B, K=K, V=V, stride=stride)
     tgt = batch.target.float()
     dft = batch.draft.float()
     tgt[:, :, int(V * 0.6):V] = -float("inf")
@@ -328,16 +335,17 @@ def _all_accept_batch(B, K, V, stride, seed, peaks):
     return W.Batch(tb, d, tok, V, 1.0)
 
 
+@pytest.mark.parametrize("V,stride", [(20011, 20016), (70003, 70008)])
 @pytest.mark.parametrize("layout", ["spread", "same_thread_two_chunks",
                                     "same_thread_three_chunks", "one_chunk"])
-def test_lossless_bonus_candidate_list(layout):
+def test_lossless_bonus_candidate_list(layout, V, stride):
     # The row pass lists, for row L, every id a draw from p there could pick;
     # the race then draws over that list.  The peaks sit where the list must
     # take them from: different threads, a thread's max chunk and second chunk
     # (read again), three chunks of one thread (the list is incomplete and the
     # row is raced in full), or one chunk.  bf16 rows: chunk `it` of thread t
     # holds vectors it*1024 + t and it*1024 + 512 + t (8 ids each).
-    B, K, V, stride = 12, 3, 20011, 20016
+    B, K = 12, 3
     if layout == "spread":
         peaks = lambda b, j: [(97 * b + 13 * j + 1000 * q) % V for q in range(5)]
     elif layout == "same_thread_two_chunks":
