@@ -61,6 +61,12 @@ def row_pass_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+# The secondary workloads, in the order run_secondary runs them.
+SECONDARY_NAMES = ("lossless_b256_k8_v128256_bf16", "lossless_b1_k4_v32000_f32",
+                   "lossless_av_b64_k5_v128256_bf16", "lossless_t0.7_b512_k4_v152064_bf16",
+                   "av_pipeline_b1024_k8_v128256_bf16_x20", "next_rows")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -78,6 +84,10 @@ def parse():
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device copy three times (a known-size "
                          "kernel for calibrating hardware byte counters)")
+    ap.add_argument("--only", choices=SECONDARY_NAMES,
+                    help="run only this secondary workload, --steps timed steps after "
+                         "--warmup untimed ones, and print its line (for per-workload "
+                         "kernel traces); no headline, roofline or CPU baseline")
     return ap.parse_args()
 
 
@@ -108,6 +118,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.only:
+        out = run_secondary(sv, W, dev, torch.cuda.current_stream(dev), args, only=args.only)
+        print(json.dumps({"workload": args.only, "steps": args.steps, "warmup": args.warmup,
+                          **out[args.only]}), flush=True)
+        return
 
     # ------------------------------------------------------------------ headline
     cfg = W.CONFIGS[2]
@@ -283,98 +299,112 @@ def _timeit(fn, n, warm, stream, torch):
     return a.elapsed_time(b) / n
 
 
-def run_secondary(sv, W, dev, stream, args):
+def run_secondary(sv, W, dev, stream, args, only=None):
+    """Every secondary workload, or only the one named (then timed over
+    --steps steps after --warmup)."""
     import torch
     out = {}
-    n = max(5, min(args.steps, 20))
+    if only is None:
+        n, warm = max(5, min(args.steps, 20)), 2
+    else:
+        n, warm = args.steps, args.warmup
+
+    def want(name):
+        return only is None or only == name
 
     # lossless verification at the headline shape (target + draft rows)
-    b0 = W.gaussian(256, 8, 128256, "bf16", 1.0, seed=77, token_seed=0, device=dev)
-    b1 = W.gaussian(256, 8, 128256, "bf16", 1.0, seed=78, token_seed=1, device=dev)
-    bs = [b0, b1]
-    ws = torch.empty(sv.workspace_bytes(256, 8, 128256), dtype=torch.uint8, device=dev)
-    calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws) for b in bs]
-    res = [c.out for c in calls]
+    if want("lossless_b256_k8_v128256_bf16"):
+        b0 = W.gaussian(256, 8, 128256, "bf16", 1.0, seed=77, token_seed=0, device=dev)
+        b1 = W.gaussian(256, 8, 128256, "bf16", 1.0, seed=78, token_seed=1, device=dev)
+        bs = [b0, b1]
+        ws = torch.empty(sv.workspace_bytes(256, 8, 128256), dtype=torch.uint8, device=dev)
+        calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws) for b in bs]
+        res = [c.out for c in calls]
 
-    def f(i):
-        calls[i % 2](i)
-    ms = _timeit(f, n, 2, stream, torch)
-    rows = 256 * 17
-    byt = rows * 128256 * 2
-    out["lossless_b256_k8_v128256_bf16"] = _line(ms, rows, byt, res)
-    del bs, b0, b1
+        def f(i):
+            calls[i % 2](i)
+        ms = _timeit(f, n, warm, stream, torch)
+        rows = 256 * 17
+        byt = rows * 128256 * 2
+        out["lossless_b256_k8_v128256_bf16"] = _line(ms, rows, byt, res)
+        del bs, b0, b1
 
     # lossless, B=1 K=4 V=32000 float32 (latency: a handful of rows)
     c = W.CONFIGS[0]
-    sets = [W.make(0, device=dev, step=s) for s in range(4)]
-    ws0 = torch.empty(sv.workspace_bytes(1, c["K"], c["V"], dtype=sv.DTYPE_F32), dtype=torch.uint8,
-                      device=dev)
-    calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws0) for b in sets]
-    res = [c.out for c in calls]
+    if want(c["name"]):
+        sets = [W.make(0, device=dev, step=s) for s in range(4)]
+        ws0 = torch.empty(sv.workspace_bytes(1, c["K"], c["V"], dtype=sv.DTYPE_F32),
+                          dtype=torch.uint8, device=dev)
+        calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws0) for b in sets]
+        res = [cl.out for cl in calls]
 
-    def f0(i):
-        calls[i % 4](i)
-    ms = _timeit(f0, n, 2, stream, torch)
-    rows = 2 * c["K"] + 1
-    out[c["name"]] = _line(ms, rows, rows * c["V"] * 4, res)
-    del sets
+        def f0(i):
+            calls[i % 4](i)
+        ms = _timeit(f0, n, warm, stream, torch)
+        rows = 2 * c["K"] + 1
+        out[c["name"]] = _line(ms, rows, rows * c["V"] * 4, res)
+        del sets
 
     # lossless + AV score + one SGD step, B=64 K=5
     c = W.CONFIGS[1]
-    sets = [W.make(1, device=dev, step=s) for s in range(4)]
-    K = c["K"]
-    ob = torch.tensor(W.av_init(1), dtype=torch.float32, device=dev)
-    ws1 = torch.empty(sv.workspace_bytes(64, K, c["V"]), dtype=torch.uint8, device=dev)
-    calls = [sv.AvStepCall(b.target, b.draft, b.tokens, ob, c["av"]["tau"], c["av"]["lr"],
-                           workspace=ws1) for b in sets]
-    res = [cl.verify.out for cl in calls]
+    if want(c["name"]):
+        sets = [W.make(1, device=dev, step=s) for s in range(4)]
+        K = c["K"]
+        ob = torch.tensor(W.av_init(1), dtype=torch.float32, device=dev)
+        ws1 = torch.empty(sv.workspace_bytes(64, K, c["V"]), dtype=torch.uint8, device=dev)
+        calls = [sv.AvStepCall(b.target, b.draft, b.tokens, ob, c["av"]["tau"], c["av"]["lr"],
+                               workspace=ws1) for b in sets]
+        res = [cl.verify.out for cl in calls]
 
-    def f1(i):
-        calls[i % 4](0)
-    ms = _timeit(f1, n, 2, stream, torch)
-    rows = 64 * (2 * K + 1)
-    out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
-    del sets
+        def f1(i):
+            calls[i % 4](0)
+        ms = _timeit(f1, n, warm, stream, torch)
+        rows = 64 * (2 * K + 1)
+        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
+        del sets
 
     # lossless at T = 0.7 on V = 152064, B = 512 K = 4
     c = W.CONFIGS[3]
-    sets = [W.make(3, device=dev, step=s) for s in range(2)]
-    ws3 = torch.empty(sv.workspace_bytes(512, 4, c["V"], temperature=0.7), dtype=torch.uint8,
-                      device=dev)
-    calls = [sv.VerifyCall(b.target, b.draft, b.tokens, temperature=0.7, workspace=ws3)
-             for b in sets]
-    res = [c.out for c in calls]
+    if want(c["name"]):
+        sets = [W.make(3, device=dev, step=s) for s in range(2)]
+        ws3 = torch.empty(sv.workspace_bytes(512, 4, c["V"], temperature=0.7),
+                          dtype=torch.uint8, device=dev)
+        calls = [sv.VerifyCall(b.target, b.draft, b.tokens, temperature=0.7, workspace=ws3)
+                 for b in sets]
+        res = [cl.out for cl in calls]
 
-    def f3(i):
-        calls[i % 2](0)
-    ms = _timeit(f3, n, 2, stream, torch)
-    rows = 512 * 9
-    out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
-    del sets
+        def f3(i):
+            calls[i % 2](0)
+        ms = _timeit(f3, n, warm, stream, torch)
+        rows = 512 * 9
+        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
+        del sets
 
     # full AV pipeline step (score, trimmed verify, update), B=1024 K=8
     c = W.CONFIGS[4]
-    sets = [W.make(4, device=dev, step=s) for s in range(2)]
-    K = c["K"]
-    ob = torch.tensor(W.av_init(4), dtype=torch.float32, device=dev)
-    ws4 = torch.empty(sv.workspace_bytes(1024, K, c["V"]), dtype=torch.uint8, device=dev)
-    calls = [sv.AvStepCall(b.target, b.draft, b.tokens, ob, c["av"]["tau"], c["av"]["lr"],
-                           workspace=ws4) for b in sets]
-    res = [cl.verify.out for cl in calls]
+    if want(c["name"]):
+        sets = [W.make(4, device=dev, step=s) for s in range(2)]
+        K = c["K"]
+        ob = torch.tensor(W.av_init(4), dtype=torch.float32, device=dev)
+        ws4 = torch.empty(sv.workspace_bytes(1024, K, c["V"]), dtype=torch.uint8, device=dev)
+        calls = [sv.AvStepCall(b.target, b.draft, b.tokens, ob, c["av"]["tau"], c["av"]["lr"],
+                               workspace=ws4) for b in sets]
+        res = [cl.verify.out for cl in calls]
 
-    def f4(i):
-        calls[i % 2](i)
-    ms = _timeit(f4, c["steps"], 2, stream, torch)
-    # kept lengths of the last step on each input set
-    kept_all = torch.stack([cl.kept for cl in calls]).float()
-    rows = 1024 * K + int((kept_all + 1).sum().item() / len(calls))
-    line = _line(ms, rows, rows * c["V"] * 2, res)
-    line["mean_kept_len"] = round(float(kept_all.mean().item()), 4)
-    line["omega_beta_after"] = [round(v, 5) for v in ob.tolist()]
-    out[c["name"]] = line
-    del sets
+        def f4(i):
+            calls[i % 2](i)
+        ms = _timeit(f4, c["steps"] if only is None else n, warm, stream, torch)
+        # kept lengths of the last step on each input set
+        kept_all = torch.stack([cl.kept for cl in calls]).float()
+        rows = 1024 * K + int((kept_all + 1).sum().item() / len(calls))
+        line = _line(ms, rows, rows * c["V"] * 2, res)
+        line["mean_kept_len"] = round(float(kept_all.mean().item()), 4)
+        line["omega_beta_after"] = [round(v, 5) for v in ob.tolist()]
+        out[c["name"]] = line
+        del sets
     torch.cuda.synchronize()
-    out["next_rows"] = run_next_rows(sv, W, dev, stream, args)
+    if want("next_rows"):
+        out["next_rows"] = run_next_rows(sv, W, dev, stream, args)
     return out
 
 

@@ -1,6 +1,6 @@
-"""bench.py's contract that holds without a GPU: one GPU only, and the source
-hash that decides whether recorded counter data still applies (a stale record
-is reported as null, not used)."""
+"""bench.py's contract that holds without a GPU: one GPU only, the workload
+names --only accepts, and the source hash that decides whether recorded counter
+data still applies (a stale record is reported as null, not used)."""
 import os
 import subprocess
 import sys
@@ -28,3 +28,14 @@ def test_source_hash_ignores_comments_and_spacing(tmp_path, monkeypatch):
     assert bench.row_pass_source_hash() == h0
     src.write_text("int f(int x) {\n    return x + 2;\n}\n")
     assert bench.row_pass_source_hash() != h0
+
+
+def test_only_names_every_secondary_workload():
+    from draft_token_verification_vocab_amd import workloads as W
+    names = set(bench.SECONDARY_NAMES)
+    for i in (0, 1, 3, 4):
+        assert W.CONFIGS[i]["name"] in names
+    assert "lossless_b256_k8_v128256_bf16" in names and "next_rows" in names
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--only", "nothing"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "invalid choice" in r.stderr
