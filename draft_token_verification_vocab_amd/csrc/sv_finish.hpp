@@ -69,22 +69,22 @@ constexpr float kScreenMargin = 1e-3f;
 struct RowPick {
     int jstar;   // first rejected position (L when all verified drafts pass)
     int am;      // the target's top token at row jstar
-    float xt;    // target logit at am (-inf when am is not a valid id)
-    float xd;    // draft logit at am (residual rows only)
+    int listed;  // ids the row pass listed for a draw from p at row jstar, or -1
+    int pad_;
     double lt;   // target log2-normaliser of row jstar
     double ld;   // draft log2-normaliser of row jstar (residual rows only)
 };
 
-// The accept tests of sequence b and the values the race needs at the first
+// The accept tests of sequence b and what the race needs at the first
 // rejected position, for every workgroup of the sequence (they all agree).
-// The first wave does it: lane j loads row j's inputs (accept ratio, top
-// token, normalisers, the logits at the top token) at once, so that the
-// chosen row's values cost no further round trip; row K = 64 has no lane and
-// is loaded after the decision.
+// The first wave does it: lane j loads row j's accept ratio, top token and
+// normalisers at once (lane 0 also the listed count), so that the decision
+// and the chosen row's values come from one round of loads; row K = 64 has
+// no lane and is loaded after the decision.  The logits at the top token
+// depend on it, so the race loads them together with its first vectors.
 template <typename T>
 __device__ __forceinline__ RowPick decide_lossless(const RaceArgs &a, int b, int L,
                                                    PhiloxKey key) {
-    using E = Elem<T>;
     __shared__ RowPick s_pick;
     const int tid = threadIdx.x;
     const int K = a.K;
@@ -101,17 +101,8 @@ __device__ __forceinline__ RowPick decide_lossless(const RaceArgs &a, int b, int
             am = a.t_am[b * (K + 1) + tid];
             lt = a.t_lse2[b * (K + 1) + tid];
         }
+        const int cnt = a.bonus_cnt ? a.bonus_cnt[b] : -1;
         const uint32_t uw = draw_u32(key, 0u, tid, b, kTagAccept);
-        float xt = -__builtin_inff(), xd = -__builtin_inff();
-        if (tid <= K && am >= 0 && am < a.V) {
-            xt = E::at(static_cast<const T *>(a.target) +
-                           (static_cast<int64_t>(b) * (K + 1) + tid) * a.stride,
-                       am);
-            if (tid < K)
-                xd = E::at(static_cast<const T *>(a.draft) +
-                               (static_cast<int64_t>(b) * K + tid) * a.stride,
-                           am);
-        }
         bool rej = false;
         if (tid < L) {
             const double u = lattice_u64(uw);
@@ -120,16 +111,11 @@ __device__ __forceinline__ RowPick decide_lossless(const RaceArgs &a, int b, int
         }
         const unsigned long long m = __ballot(rej);
         const int jstar = m ? __ffsll(m) - 1 : L;
-        if (tid == jstar) s_pick = RowPick{jstar, am, xt, xd, lt, ld};
+        const int listed = jstar == L ? cnt : -1;  // only a draw from p can use the list
+        if (tid == jstar) s_pick = RowPick{jstar, am, listed, 0, lt, ld};
         if (jstar == kWave && tid == 0) {  // K = 64 and every draft accepted: row 64
             const int r = b * (K + 1) + kWave;
-            const int am64 = a.t_am[r];
-            const float xt64 =
-                am64 >= 0 && am64 < a.V
-                    ? E::at(static_cast<const T *>(a.target) + static_cast<int64_t>(r) * a.stride,
-                            am64)
-                    : -__builtin_inff();
-            s_pick = RowPick{jstar, am64, xt64, -__builtin_inff(), a.t_lse2[r], 0.0};
+            s_pick = RowPick{jstar, a.t_am[r], listed, 0, a.t_lse2[r], 0.0};
         }
     }
     __syncthreads();
@@ -165,15 +151,14 @@ __device__ __forceinline__ float race_floor(bool residual, int am, float xt, flo
 
 // Race over vectors [v_lo, v_hi) of one row (pair) with NT threads, one
 // vector per thread per trip.  RES: w = max(0, p - q) from the target and
-// draft rows; otherwise w = p of the target row.  am: the target's top token
-// (am_xt, am_xd: its logits), whose key (less the margin) is a floor the
-// row's best is known to reach.  Returns (in thread 0) the best double key
-// and id, or id -1 when no id of the range can win.
+// draft rows; otherwise w = p of the target row.  am: the target's top token,
+// whose key (less the margin) is a floor the row's best is known to reach;
+// its logits are loaded together with the first vectors.  Returns (in thread
+// 0) the best double key and id, or id -1 when no id of the range can win.
 template <typename T, int NT, bool RES>
 __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int V, float c,
                            double cd, double inv_t, double lse2_t, double lse2_d, PhiloxKey key,
-                           uint32_t pos, uint32_t seq, int am, float am_xt, float am_xd,
-                           double *out_key, int *out_x) {
+                           uint32_t pos, uint32_t seq, int am, double *out_key, int *out_x) {
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
     constexpr int NW = NT / kWave;
@@ -199,8 +184,13 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
     };
     Vec qa, qb;
     qa.t = qa.d = qb.t = qb.d = make_uint4(0u, 0u, 0u, 0u);
+    // the top token's logits first, so that the floor waits for them alone
+    const bool am_ok = am >= 0 && am < V;
+    const float am_xt = am_ok ? E::at(trow, am) : -__builtin_inff();
+    const float am_xd = RES && am_ok ? E::at(drow, am) : -__builtin_inff();
     if (nit > 0) load_trip(qa, 0);
-    const float floor = race_floor(RES, am, am_xt, am_xd, c, lse2_t, lse2_d, key, pos, seq);
+    const float floor =
+        race_floor(RES, am_ok ? am : -1, am_xt, am_xd, c, lse2_t, lse2_d, key, pos, seq);
 
     // best: this lane's best screening key; thr: the wave's best less the
     // margin.  An id whose key cannot reach thr is never a candidate, so it
@@ -390,12 +380,6 @@ __device__ __forceinline__ void race_listed(const RaceArgs &a, int b, int jstar,
     }
 }
 
-// The listed candidates of sequence b, or -1 when the race reads the row:
-// only a draw from p (no rejection) at row L can use them.
-__device__ __forceinline__ int listed_count(const RaceArgs &a, int b, bool residual) {
-    return !residual && a.bonus_cnt ? a.bonus_cnt[b] : -1;
-}
-
 // Race over vectors [v_lo, v_hi) of sequence b's row at the decided position.
 template <typename T, int NT>
 __device__ __forceinline__ void race_decided(const RaceArgs &a, int b, const RowPick &pk,
@@ -408,10 +392,10 @@ __device__ __forceinline__ void race_decided(const RaceArgs &a, int b, const Row
         const T *drow = static_cast<const T *>(a.draft) +
                         (static_cast<int64_t>(b) * a.K + jstar) * a.stride;
         race_range<T, NT, true>(trow, drow, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
-                                a.inv_t, pk.lt, pk.ld, key, jstar, b, pk.am, pk.xt, pk.xd, k, x);
+                                a.inv_t, pk.lt, pk.ld, key, jstar, b, pk.am, k, x);
     } else {
         race_range<T, NT, false>(trow, nullptr, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
-                                 a.inv_t, pk.lt, 0.0, key, jstar, b, pk.am, pk.xt, pk.xd, k, x);
+                                 a.inv_t, pk.lt, 0.0, key, jstar, b, pk.am, k, x);
     }
 }
 
@@ -436,10 +420,8 @@ __device__ __forceinline__ void emit_sequence(const RaceArgs &a, int b, int jsta
         double k;
         int x;
         const int am = a.t_am[b * (a.K + 1) + jstar];
-        const float am_xt = am >= 0 && am < a.V ? Elem<T>::at(trow, am) : -__builtin_inff();
         race_range<T, NT, false>(trow, nullptr, 0, nvec, a.V, a.c, static_cast<double>(a.c),
-                                 a.inv_t, lt, 0.0, key, jstar, b, am, am_xt, -__builtin_inff(),
-                                 &k, &x);
+                                 a.inv_t, lt, 0.0, key, jstar, b, am, &k, &x);
         if (tid == 0) s_y = x;
         __syncthreads();
     }
@@ -466,7 +448,7 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     const RowPick pk = decide_lossless<T>(a, b, L, key);
     const int jstar = pk.jstar;
     const bool residual = jstar < L;
-    const int n = listed_count(a, b, residual);
+    const int n = pk.listed;
     double k = -__builtin_inf();
     int x = -1;
     if (n >= 0) {
