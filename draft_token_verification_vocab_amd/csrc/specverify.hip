@@ -22,6 +22,7 @@ using namespace sv;
 constexpr int kRaceBlock = 256;
 constexpr int kRaceTargetBlocks = 2048;
 constexpr int kMaxSegs = 64;
+static_assert(kMaxSegs <= kWave, "the combine reads one segment per lane of one wave");
 constexpr int kSmallBlock = 64;
 // FLy resolver: one wave per sequence.
 constexpr int kFlyBlock = 256;

@@ -461,30 +461,36 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     if (threadIdx.x == 0) a.cand[b * a.segs + seg] = RaceCand{k, x, jstar};
 }
 
-// Best segment per sequence; writes accepted_len and the emitted tokens.
+// Best segment per sequence (largest key, then lowest id); writes
+// accepted_len and the emitted tokens.  One wave: lane s reads segment s
+// (segs <= 64), and a shuffle reduction picks the winner.
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int32_t *tokens,
                                                          int32_t *accepted_len,
                                                          int32_t *out_tokens) {
+    static_assert(NT == kWave, "one wave per sequence");
     const int b = blockIdx.x;
-    int y = -1, jstar = 0;
-    if (threadIdx.x == 0) {
-        double bk = -__builtin_inf();
-        int bx = INT_MAX;
-        for (int s = 0; s < a.segs; ++s) {
-            const RaceCand cnd = a.cand[b * a.segs + s];
-            if (cnd.x >= 0 && (cnd.key > bk || (cnd.key == bk && cnd.x < bx))) {
-                bk = cnd.key;
-                bx = cnd.x;
-            }
+    const int lane = threadIdx.x;
+    double bk = -__builtin_inf();
+    int bx = INT_MAX;
+    if (lane < a.segs) {
+        const RaceCand cnd = a.cand[b * a.segs + lane];
+        if (cnd.x >= 0) {
+            bk = cnd.key;
+            bx = cnd.x;
         }
-        y = bx == INT_MAX ? -1 : bx;
-        jstar = a.cand[b * a.segs].jstar;
     }
-    __shared__ int s_j;
-    if (threadIdx.x == 0) s_j = jstar;
-    __syncthreads();
-    emit_sequence<T, NT>(a, b, s_j, y, tokens, accepted_len, out_tokens);
+#pragma unroll
+    for (int msk = kWave / 2; msk > 0; msk >>= 1) {
+        const double ok = __shfl_xor(bk, msk, kWave);
+        const int ox = __shfl_xor(bx, msk, kWave);
+        if (ok > bk || (ok == bk && ox < bx)) {
+            bk = ok;
+            bx = ox;
+        }
+    }
+    const int jstar = a.cand[b * a.segs].jstar;  // the same in every segment
+    emit_sequence<T, NT>(a, b, jstar, bx == INT_MAX ? -1 : bx, tokens, accepted_len, out_tokens);
 }
 
 // FLy: a deviation is a draft token different from the target's top token.
