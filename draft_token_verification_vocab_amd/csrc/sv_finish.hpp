@@ -198,6 +198,7 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
     float best = floor;
     int bx = INT_MAX;
     float bt = 0.f, bd = 0.f;  // the best id's target and draft logits
+    uint32_t bw = 0u;          // and its Philox word
     float thr = floor - kScreenMargin;
     // lb = l*c - lsub bounds the log2 weight: log2 p for a residual row
     // (w = max(0, p - q) <= p), the weight itself (up to the row's constant
@@ -246,6 +247,7 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
                         bx = x;
                         bt = xt[k];
                         if (RES) bd = E::elem(q.d, k);
+                        bw = w4[qi];
                     }
                     evaluated = true;
                 }
@@ -285,25 +287,25 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
         trip(q, vi, live);
     }
 
-    // Workgroup maximum of the screening keys.
+    // Workgroup maximum of the screening keys (DPP within waves, LDS across).
     __shared__ float sh_best[NW];
     __shared__ double sh_key[NW];
     __shared__ int sh_x[NW];
-    float m = best;
-#pragma unroll
-    for (int msk = kWave / 2; msk > 0; msk >>= 1) m = fmaxf(m, __shfl_xor(m, msk, kWave));
     const int lane = tid & (kWave - 1), wv = tid / kWave;
+    const float m = from_ordered_bits(wave_max_u32(ordered_bits(best)));
     if (lane == 0) sh_best[wv] = m;
     __syncthreads();
     float g1 = sh_best[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) g1 = fmaxf(g1, sh_best[w]);
 
-    // Double-precision keys of the candidates within the margin.
+    // Double-precision keys of the candidates within the margin (from the
+    // Philox word kept with each thread's best: no second draw).
     double k64 = -__builtin_inf();
     int kx = INT_MAX;
-    if (bx != INT_MAX && best >= g1 - kScreenMargin) {
-        const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(bx), pos, seq, kTagRace));
+    const bool near = bx != INT_MAX && best >= g1 - kScreenMargin;
+    if (near) {
+        const double u = lattice_u64(bw);
         const double lnE = log(-log(u));
         const double lt = static_cast<double>(bt);
         if (RES) {
@@ -318,19 +320,27 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
             kx = bx;
         }
     }
-#pragma unroll
-    for (int msk = kWave / 2; msk > 0; msk >>= 1) {
-        const double ok = __shfl_xor(k64, msk, kWave);
-        const int ox = __shfl_xor(kx, msk, kWave);
-        if (ok > k64 || (ok == k64 && ox < kx)) {
-            k64 = ok;
-            kx = ox;
+    // The wave's best candidate: usually one lane is near, so its values are
+    // read lane by lane rather than reduced over the whole wave.
+    double wk = -__builtin_inf();
+    int wx = INT_MAX;
+    for (uint64_t nb = __ballot(near); nb != 0ull; nb &= nb - 1ull) {
+        const int l = __builtin_ctzll(nb);
+        const uint64_t kb = static_cast<uint64_t>(__double_as_longlong(k64));
+        // readlane returns a signed int: take each half as 32 unsigned bits
+        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(kb >> 32), l);
+        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(kb), l);
+        const double ok = __longlong_as_double(
+            static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+        const int ox = __builtin_amdgcn_readlane(kx, l);
+        if (ok > wk || (ok == wk && ox < wx)) {
+            wk = ok;
+            wx = ox;
         }
     }
-    __syncthreads();  // sh_best reads are done before thread 0 reuses shared state
-    if (lane == 0) {
-        sh_key[wv] = k64;
-        sh_x[wv] = kx;
+    if (lane == 0) {  // sh_key and sh_x are not the arrays read above: no barrier needed
+        sh_key[wv] = wk;
+        sh_x[wv] = wx;
     }
     __syncthreads();
     if (tid == 0) {
