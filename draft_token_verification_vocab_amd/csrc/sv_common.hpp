@@ -1,6 +1,6 @@
 // sv_common.hpp -- shared device helpers of the specverify HIP library:
-// element traits for 16-byte row loads, the Philox4x32-10 counter-based
-// generator and the fast transcendental wrappers.
+// element traits for 16-byte row loads, the fast transcendental wrappers and
+// the wave reductions (the Philox generator is in sv_philox.hpp).
 #pragma once
 
 #include <hip/hip_runtime.h>
