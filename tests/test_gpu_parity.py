@@ -67,6 +67,24 @@ def test_row_stats_parity(dtype, V, stride, T):
     assert_close(np_(r["feat"]), o["feat"], rel, "feat", abs_floor=rel)
 
 
+@pytest.mark.parametrize("T", [1e-4, 0.05, 5.0, 1e4])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_row_stats_extreme_temperatures(dtype, T):
+    # both ends of the accepted temperature range: rows scaled by up to 1e4
+    # (one-hot to the last ulp) and down to 1e-4 (near uniform)
+    for V, stride in ((1003, 1008), (32000, 32000)):
+        xh = _special_rows(V, dtype, stride, seed=V + 5)
+        r = sv.row_stats(xh.to(DEV), vocab=V, temperature=T, qmax=True, feat=True)
+        torch.cuda.synchronize()
+        o = ref.rows_stats(host_logits(xh), temperature=f32(T), V=V, nthreads=NT)
+        rel = REL_TOL[dtype]
+        assert np.array_equal(np_(r["argmax"]), o["argmax"])
+        assert_close(np_(r["lse"]), o["lse"], rel, "lse")
+        assert_close(np_(r["entropy"]), o["h"], rel, "entropy", abs_floor=1e-12)
+        assert_close(np_(r["qmax"]), o["qmax"], rel, "qmax")
+        assert_close(np_(r["feat"]), o["feat"], rel, "feat", abs_floor=rel)
+
+
 def test_row_stats_reproducible_and_ordered_ties():
     x = torch.zeros(5, 40000, device=DEV, dtype=torch.bfloat16)
     x[0, [39999, 12345, 20000]] = 1.0
@@ -243,6 +261,16 @@ def test_lossless_parity(cfg, B, K, V, stride):
     batch = W.make(cfg, B=B, K=K, V=V, stride=stride)
     _, o, nm, nb = _lossless_check(batch, seed=7)
     _lossless_check(batch, seed=8, draft_stats_path=True)
+
+
+@pytest.mark.parametrize("T", [1e-4, 0.05, 5.0, 1e4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lossless_extreme_temperatures(dtype, T):
+    # the race's float screening at keys scaled by up to 1e4, and near-uniform
+    # rows where every id is a candidate
+    batch = W.gaussian(16, 4, 5003, dtype, T, seed=91, token_seed=3, stride=5008)
+    for seed in range(3):
+        _lossless_check(batch, seed=seed)
 
 
 def test_lossless_kept_len_and_bad_tokens():
