@@ -34,6 +34,11 @@
 
 namespace sv {
 
+// Loads per lane per round in the diagnostics finish kernel: issued together
+// (unconditionally, at clamped indices), so that a lane waits once per batch
+// rather than once per element.
+constexpr int kFinishBatch = 8;
+
 // --------------------------------------------------------------------------
 // Per-position sums over one batch's labels.  The labels of sequence b are its
 // drafts i < min(a_b + 1, L_b): y = 1 for i < a_b (accepted), y = 0 at the
@@ -347,7 +352,15 @@ __global__ __launch_bounds__(kWave) void diag_finish_kernel(DiagWs ws, int regio
                                                             double *out) {
     const int lane = threadIdx.x;
     uint64_t part = 0ull, np = 0ull, nn = 0ull, ls = 0ull;
-    for (int q = lane; q < regions * regions; q += kWave) part += ws.pairs[q];
+    const int npairs = regions * regions;
+    for (int q0 = lane; q0 < npairs; q0 += kFinishBatch * kWave) {
+        uint64_t pv[kFinishBatch];
+#pragma unroll
+        for (int u = 0; u < kFinishBatch; ++u) pv[u] = ws.pairs[min(q0 + u * kWave, npairs - 1)];
+#pragma unroll
+        for (int u = 0; u < kFinishBatch; ++u)
+            if (q0 + u * kWave < npairs) part += pv[u];
+    }
     for (int r = lane; r < regions; r += kWave) {
         np += static_cast<uint64_t>(ws.cnt[2 * r]);
         nn += static_cast<uint64_t>(ws.cnt[2 * r + 1]);
@@ -361,7 +374,15 @@ __global__ __launch_bounds__(kWave) void diag_finish_kernel(DiagWs ws, int regio
     long long ece_fp = 0;
     for (int q = lane; q < nbins; q += kWave) {
         uint64_t v = 0ull;
-        for (int r = 0; r < regions; ++r) v += ws.bins[static_cast<int64_t>(r) * nbins + q];
+        for (int r0 = 0; r0 < regions; r0 += kFinishBatch) {
+            uint64_t bv[kFinishBatch];
+#pragma unroll
+            for (int u = 0; u < kFinishBatch; ++u)
+                bv[u] = ws.bins[static_cast<int64_t>(min(r0 + u, regions - 1)) * nbins + q];
+#pragma unroll
+            for (int u = 0; u < kFinishBatch; ++u)
+                if (r0 + u < regions) v += bv[u];
+        }
         const long long sv = static_cast<long long>(v);
         ece_fp += sv < 0 ? -sv : sv;
     }
