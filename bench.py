@@ -514,11 +514,26 @@ def cpu_baseline(batch, cfg, budget_s):
     ref.verify(tgt[:n1], None, tok[:n1], 0, ref.MODE_FLY, theta=cfg["theta"],
                window=cfg["window"], nthreads=1)
     dt1 = time.perf_counter() - t
+    row_bytes = batch.V * 2
     return {"value": round(rows * reps / total, 1), "unit": "rows/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d of %d sequences (%d target rows) of %s, FLy mode, %d pass(es), %.1f s"
                       % (n, Btot, rows, cfg["name"], reps, total),
-            "single_thread_rows_per_s": round(n1 * (cfg["K"] + 1) / dt1, 1)}
+            "gbps": round(rows * reps * row_bytes / total / 1e9, 3),
+            "single_thread_rows_per_s": round(n1 * (cfg["K"] + 1) / dt1, 1),
+            "host_cpu": _cpu_model(), "host_logical_cpus": os.cpu_count()}
+
+
+def _cpu_model():
+    """The host CPU's model name (Linux), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":
