@@ -263,6 +263,16 @@ def test_lossless_parity(cfg, B, K, V, stride):
     _lossless_check(batch, seed=8, draft_stats_path=True)
 
 
+@pytest.mark.parametrize("V,stride", [(2, 8), (3, 8), (9, 16), (17, 24)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lossless_tiny_vocabularies(dtype, V, stride):
+    # rows of one or a few vectors, most of them the partial last one: the
+    # race's whole trips are empty and only its last trip runs
+    batch = W.gaussian(40, 6, V, dtype, 1.0, seed=V, token_seed=1, stride=stride)
+    for seed in range(4):
+        _lossless_check(batch, seed=seed)
+
+
 @pytest.mark.parametrize("T", [1e-4, 0.05, 5.0, 1e4])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_lossless_extreme_temperatures(dtype, T):
