@@ -409,43 +409,6 @@ __device__ __forceinline__ void race_decided(const RaceArgs &a, int b, const Row
     }
 }
 
-// Writes accepted_len and the emitted tokens of sequence b, given the race's
-// winner y (valid in thread 0).  A residual that vanished in floating point
-// (y < 0; only possible within rounding of u_j = p/q) falls back to a race
-// over p at the same row.
-template <typename T, int NT>
-__device__ __forceinline__ void emit_sequence(const RaceArgs &a, int b, int jstar, int y,
-                                              const int32_t *tokens, int32_t *accepted_len,
-                                              int32_t *out_tokens) {
-    const int tid = threadIdx.x;
-    __shared__ int s_y;
-    if (tid == 0) s_y = y;
-    __syncthreads();
-    if (s_y < 0) {
-        const T *trow = static_cast<const T *>(a.target) +
-                        (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
-        const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
-        const double lt = a.t_lse2[b * (a.K + 1) + jstar];
-        const PhiloxKey key = philox_key(a.seed);
-        double k;
-        int x;
-        const int am = a.t_am[b * (a.K + 1) + jstar];
-        race_range<T, NT, false>(trow, nullptr, 0, nvec, a.V, a.c, static_cast<double>(a.c),
-                                 a.inv_t, lt, 0.0, key, jstar, b, am, &k, &x);
-        if (tid == 0) s_y = x;
-        __syncthreads();
-    }
-    if (tid == 0) accepted_len[b] = jstar;
-    for (int j = tid; j <= a.K; j += NT) {
-        int v = -1;
-        if (j < jstar)
-            v = tokens[b * a.K + j];
-        else if (j == jstar)
-            v = s_y;
-        out_tokens[b * (a.K + 1) + j] = v;
-    }
-}
-
 // Segmented race: workgroup i takes segment i % segs of sequence i / segs (a
 // 1-D grid, so B is not bound by the grid's y limit) and reports its best
 // candidate; race_combine_kernel then picks each sequence's winner.
@@ -472,8 +435,11 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
 }
 
 // Best segment per sequence (largest key, then lowest id); writes
-// accepted_len and the emitted tokens.  One wave: lane s reads segment s
-// (segs <= 64), and a shuffle reduction picks the winner.
+// accepted_len and the emitted tokens.  One wave per sequence: lane s reads
+// segment s's candidate (segs <= 64) and lane j the draft token j (K <= 64),
+// in one round of loads; a shuffle reduction picks the winner.  A residual
+// that vanished in floating point (no candidate anywhere; only possible
+// within rounding of u_j = p/q) falls back to a race over p at the same row.
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int32_t *tokens,
                                                          int32_t *accepted_len,
@@ -481,14 +447,15 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
     static_assert(NT == kWave, "one wave per sequence");
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
+    const int K = a.K;
+    const RaceCand cnd =
+        lane < a.segs ? a.cand[b * a.segs + lane] : RaceCand{-__builtin_inf(), -1, 0};
+    const int tk = lane < K ? tokens[b * K + lane] : -1;
     double bk = -__builtin_inf();
     int bx = INT_MAX;
-    if (lane < a.segs) {
-        const RaceCand cnd = a.cand[b * a.segs + lane];
-        if (cnd.x >= 0) {
-            bk = cnd.key;
-            bx = cnd.x;
-        }
+    if (cnd.x >= 0) {
+        bk = cnd.key;
+        bx = cnd.x;
     }
 #pragma unroll
     for (int msk = kWave / 2; msk > 0; msk >>= 1) {
@@ -499,8 +466,26 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
             bx = ox;
         }
     }
-    const int jstar = a.cand[b * a.segs].jstar;  // the same in every segment
-    emit_sequence<T, NT>(a, b, jstar, bx == INT_MAX ? -1 : bx, tokens, accepted_len, out_tokens);
+    const int jstar = __shfl(cnd.jstar, 0);  // the same in every segment
+    int y = bx == INT_MAX ? -1 : bx;         // every lane holds the reduction's result
+    if (y < 0) {
+        const T *trow = static_cast<const T *>(a.target) +
+                        (static_cast<int64_t>(b) * (K + 1) + jstar) * a.stride;
+        const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
+        const double lt = a.t_lse2[b * (K + 1) + jstar];
+        const PhiloxKey key = philox_key(a.seed);
+        double k;
+        int x = -1;
+        const int am = a.t_am[b * (K + 1) + jstar];
+        race_range<T, NT, false>(trow, nullptr, 0, nvec, a.V, a.c, static_cast<double>(a.c),
+                                 a.inv_t, lt, 0.0, key, jstar, b, am, &k, &x);
+        y = __shfl(x, 0);
+    }
+    if (lane == 0) accepted_len[b] = jstar;
+    for (int j = lane; j <= K; j += NT) {
+        // j < jstar <= 64 only on the first pass, where j == lane holds token j
+        out_tokens[b * (K + 1) + j] = j < jstar ? tk : (j == jstar ? y : -1);
+    }
 }
 
 // FLy: a deviation is a draft token different from the target's top token.
