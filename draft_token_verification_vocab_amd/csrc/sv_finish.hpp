@@ -510,9 +510,10 @@ __global__ __launch_bounds__(NT) void fly_kernel(const int32_t *tokens, const in
     const int32_t *top = am + static_cast<int64_t>(b) * (K + 1);
     const float *hb = h + static_cast<int64_t>(b) * (K + 1);
     const bool live = lane < L;
-    const int32_t tk = live ? tok[lane] : 0;
+    // loaded for every drafted position, so that they do not wait for L
+    const int32_t tk = lane < K ? tok[lane] : 0;
     const int32_t tp = lane < K + 1 ? top[lane] : 0;
-    const float hv = live ? hb[lane] : 0.f;
+    const float hv = lane < K ? hb[lane] : 0.f;
     const uint64_t dev = __ballot(live && tk != tp);
     const uint64_t gate = __ballot(live && hv >= theta);  // NaN entropy fails the gate
 
