@@ -63,6 +63,8 @@ _SIGNATURES = {
                                              ctypes.c_float, _P, _P, _P, _P]),
     "spec_av_update": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_float, _P, _P]),
+    "spec_av_score_update": (ctypes.c_int32, [_P, _P, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_float, _P, _P, _P, _P, _P]),
     "spec_row_stats": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
                                         ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P, _P]),
     "spec_read_probe": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -322,8 +324,9 @@ class AvStepCall:
     With tau > 0: spec_av_score (draft rows), spec_verify on the kept drafts,
     spec_av_update.  With tau <= 0 nothing can be trimmed, so spec_verify
     reads target and draft rows in one pass and exports the draft statistics,
-    spec_av_score_stats scores from them, and spec_av_update follows: the
-    same results with one row pass instead of two."""
+    and spec_av_score_update scores from them and takes the SGD step in one
+    launch: the same results with one row pass instead of two, and four
+    launches instead of five."""
 
     def __init__(self, target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
                  omega_beta: torch.Tensor, tau: float, lr: float, *, temperature: float = 1.0,
@@ -348,8 +351,9 @@ class AvStepCall:
             out.draft_stats_out = self.stats
             self.verify = VerifyCall(target, draft, draft_tokens, temperature=temperature,
                                      vocab=vocab, workspace=workspace, out=out)
-            self.score_args = (_ptr(self.stats), int(B), int(K), _ptr(omega_beta), float(tau),
-                               _ptr(self.conf), _ptr(self.mask), _ptr(self.kept), st)
+            self.score_update_args = (_ptr(self.stats), _ptr(out.accepted_len), int(B), int(K),
+                                      float(lr), _ptr(omega_beta), _ptr(self.conf),
+                                      _ptr(self.mask), _ptr(self.kept), st)
         else:
             self.score_args = (_ptr(draft), _ptr(draft_tokens), ctypes.byref(self.params),
                                _ptr(omega_beta), float(tau), _ptr(self.conf), _ptr(self.mask),
@@ -364,10 +368,10 @@ class AvStepCall:
     def __call__(self, seed: int = 0) -> VerifyResult:
         if self.fused:
             r = self.verify(seed)
-            _check(self.L.spec_av_score_stats(*self.score_args), "spec_av_score_stats")
-        else:
-            _check(self.L.spec_av_score(*self.score_args), "spec_av_score")
-            r = self.verify(seed)
+            _check(self.L.spec_av_score_update(*self.score_update_args), "spec_av_score_update")
+            return r
+        _check(self.L.spec_av_score(*self.score_args), "spec_av_score")
+        r = self.verify(seed)
         _check(self.L.spec_av_update(*self.update_args), "spec_av_update")
         return r
 
@@ -379,6 +383,27 @@ def draft_stats_view(draft_stats: torch.Tensor, B: int, K: int):
     return {"lse2": raw[:8 * n].view(torch.float64), "logq2": raw[8 * n:16 * n].view(torch.float64),
             "qmax": raw[16 * n:20 * n].view(torch.float32),
             "feat": raw[20 * n:24 * n].view(torch.float32)}
+
+
+def av_score_update(draft_stats: torch.Tensor, accepted_len: torch.Tensor,
+                    omega_beta: torch.Tensor, lr: float, B: int, K: int):
+    """For an untrimmed step scored after its verification: the confidences
+    at the current coefficients (every draft kept), then one SGD step, in one
+    launch.  Returns (conf [B,K] float, keep_mask [B,K] uint8, kept_len [B]
+    int32); omega_beta is updated in place."""
+    for t, n in ((draft_stats, "draft_stats"), (accepted_len, "accepted_len"),
+                 (omega_beta, "omega_beta")):
+        _need_cuda(t, n)
+    if draft_stats.numel() * draft_stats.element_size() < draft_stats_bytes(B, K):
+        raise ValueError("draft_stats must hold spec_draft_stats_bytes(B, K) bytes")
+    dev = draft_stats.device
+    conf = torch.empty(B, K, dtype=torch.float32, device=dev)
+    mask = torch.empty(B, K, dtype=torch.uint8, device=dev)
+    kept = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(load().spec_av_score_update(_ptr(draft_stats), _ptr(accepted_len), int(B), int(K),
+                                       float(lr), _ptr(omega_beta), _ptr(conf), _ptr(mask),
+                                       _ptr(kept), _stream(dev)), "spec_av_score_update")
+    return conf, mask, kept
 
 
 def av_update(draft_stats: torch.Tensor, accepted_len: torch.Tensor,

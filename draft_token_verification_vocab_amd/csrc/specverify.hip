@@ -373,6 +373,24 @@ spec_status spec_av_score_stats(const void *draft_stats, int32_t batch, int32_t 
     return launch_status();
 }
 
+spec_status spec_av_score_update(const void *draft_stats, const int32_t *accepted_len,
+                                 int32_t batch, int32_t num_draft, float lr, float *omega_beta,
+                                 float *conf, uint8_t *keep_mask, int32_t *kept_len,
+                                 void *stream) {
+    if (batch < 0 || num_draft < 1) return SPEC_ERR_ARG;
+    if (num_draft > 64) return SPEC_ERR_UNSUPPORTED;
+    if (!std::isfinite(lr)) return SPEC_ERR_ARG;
+    if (batch == 0) return SPEC_OK;
+    if (!draft_stats || !aligned16(draft_stats) || !accepted_len || !omega_beta)
+        return SPEC_ERR_ARG;
+    const size_t n = static_cast<size_t>(batch) * num_draft;
+    DraftStats ds = draft_stats_view(const_cast<void *>(draft_stats), n);
+    av_score_update_kernel<kLabelBlock>
+        <<<dim3(1), dim3(kLabelBlock), 0, static_cast<hipStream_t>(stream)>>>(
+            ds.feat, accepted_len, batch, num_draft, lr, omega_beta, conf, keep_mask, kept_len);
+    return launch_status();
+}
+
 spec_status spec_av_update(const void *draft_stats, const int32_t *accepted_len,
                            const int32_t *kept_len, int32_t batch, int32_t num_draft, float lr,
                            float *omega_beta, void *stream) {

@@ -16,6 +16,12 @@
 
 namespace sv {
 
+// Confidence of a draft with feature f at a position with intercept beta.
+__device__ __forceinline__ double av_confidence(double omega, float f, float beta) {
+    const double z = omega * static_cast<double>(f) + static_cast<double>(beta);
+    return 1.0 / (1.0 + exp(-z));
+}
+
 // One thread per sequence.  feat: [B*K] (draft statistics).
 __global__ void av_score_kernel(const float *feat, int B, int K, const float *omega_beta,
                                 float tau, float *conf, uint8_t *keep_mask, int32_t *kept_len) {
@@ -27,9 +33,7 @@ __global__ void av_score_kernel(const float *feat, int B, int K, const float *om
     bool open = true;
     int L = 0;
     for (int i = 0; i < K; ++i) {
-        const double z = omega * static_cast<double>(feat[b * K + i]) +
-                         static_cast<double>(omega_beta[1 + i]);
-        const double ci = 1.0 / (1.0 + exp(-z));
+        const double ci = av_confidence(omega, feat[b * K + i], omega_beta[1 + i]);
         P *= ci;
         const bool keep = open && (t <= 0.0 || P >= t);
         if (conf) conf[b * K + i] = static_cast<float>(ci);

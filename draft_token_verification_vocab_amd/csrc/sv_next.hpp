@@ -30,6 +30,7 @@
 // earlier, its latest earlier occurrence, and the up to K tokens after it.
 #pragma once
 
+#include "sv_av.hpp"
 #include "sv_common.hpp"
 
 namespace sv {
@@ -109,11 +110,11 @@ __device__ void label_sums(const float *feat, const int32_t *accepted_len,
 }
 
 // One SGD step on the mean log-loss of the batch's labels (the update the
-// adaptive-verification workloads run every step).
+// adaptive-verification workloads run every step), by the whole workgroup.
 template <int NT>
-__global__ __launch_bounds__(NT) void av_sgd_kernel(const float *feat, const int32_t *accepted_len,
-                                                   const int32_t *kept_len, int B, int K, float lr,
-                                                   float *omega_beta) {
+__device__ __forceinline__ void sgd_step(const float *feat, const int32_t *accepted_len,
+                                         const int32_t *kept_len, int B, int K, float lr,
+                                         float *omega_beta) {
     __shared__ LabelSums sums[64];
     label_sums<NT, false>(feat, accepted_len, kept_len, B, K, omega_beta, sums);
     __shared__ double s_n, s_go;
@@ -136,6 +137,36 @@ __global__ __launch_bounds__(NT) void av_sgd_kernel(const float *feat, const int
             omega_beta[1 + threadIdx.x] = static_cast<float>(
                 static_cast<double>(omega_beta[1 + threadIdx.x]) - l * sums[threadIdx.x].r);
     }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void av_sgd_kernel(const float *feat, const int32_t *accepted_len,
+                                                   const int32_t *kept_len, int B, int K, float lr,
+                                                   float *omega_beta) {
+    sgd_step<NT>(feat, accepted_len, kept_len, B, K, lr, omega_beta);
+}
+
+// A step with nothing trimmed, scored after its verification: the
+// confidences of every draft at the coefficients before the update (as
+// av_score_kernel with tau <= 0: every draft kept), then the SGD step, in one
+// launch.  The scores read omega_beta before sgd_step's first barrier, and
+// sgd_step writes it only after that barrier.
+template <int NT>
+__global__ __launch_bounds__(NT) void av_score_update_kernel(const float *feat,
+                                                            const int32_t *accepted_len, int B,
+                                                            int K, float lr, float *omega_beta,
+                                                            float *conf, uint8_t *keep_mask,
+                                                            int32_t *kept_len) {
+    const double omega = static_cast<double>(omega_beta[0]);
+    const int n = B * K;
+    for (int f = threadIdx.x; f < n; f += NT) {
+        const int i = f - (f / K) * K;
+        if (conf) conf[f] = static_cast<float>(av_confidence(omega, feat[f], omega_beta[1 + i]));
+        if (keep_mask) keep_mask[f] = 1;
+    }
+    if (kept_len)
+        for (int b = threadIdx.x; b < B; b += NT) kept_len[b] = K;
+    sgd_step<NT>(feat, accepted_len, nullptr, B, K, lr, omega_beta);
 }
 
 // --------------------------------------------------------------------------

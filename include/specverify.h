@@ -203,6 +203,22 @@ spec_status spec_av_update(const void *draft_stats, const int32_t *accepted_len,
                            float *omega_beta, void *stream);
 
 /*
+ * spec_av_score_update -- for a step with nothing trimmed (tau <= 0), scored
+ * after its verification: spec_av_score_stats with tau <= 0 (every draft
+ * kept; conf, keep_mask and kept_len each nullable) at the coefficients
+ * before the update, then spec_av_update with kept_len NULL, in one launch.
+ * The results equal those two calls in that order, bit for bit.
+ * draft_stats: device, spec_draft_stats_bytes(batch, num_draft), 16-byte
+ * aligned (from spec_verify's draft_stats_out, or spec_av_score);
+ * accepted_len: device int32 [B] from spec_verify; omega_beta: device
+ * float[K+1], updated in place.  Errors as spec_av_update.
+ */
+spec_status spec_av_score_update(const void *draft_stats, const int32_t *accepted_len,
+                                 int32_t batch, int32_t num_draft, float lr, float *omega_beta,
+                                 float *conf, uint8_t *keep_mask, int32_t *kept_len,
+                                 void *stream);
+
+/*
  * Newton (IRLS) refit of the estimator ([AV] section "Ajuste de los
  * Coeficientes").  The pages refit omega and the beta_i after every round of
  * N decoding steps: each step adds its labelled drafts (the same labels as

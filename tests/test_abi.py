@@ -40,7 +40,7 @@ def L():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("spec_verify", "spec_av_score", "spec_av_score_stats", "spec_av_update",
-              "spec_row_stats",
+              "spec_av_score_update", "spec_row_stats",
               "spec_workspace_bytes", "spec_draft_stats_bytes", "spec_status_string",
               "spec_read_probe", "spec_irls_state_bytes", "spec_irls_reset",
               "spec_irls_accumulate", "spec_irls_solve", "spec_av_diagnostics",
@@ -146,6 +146,16 @@ def test_other_entry_points_validate(L):
                                  None, None, None) == -2
     assert L.spec_av_score_stats(ctypes.c_void_p(16), 0, 4, None, 0.2, None, None, None,
                                  None) == 0
+    assert L.spec_av_score_update(None, ctypes.c_void_p(16), 4, 4, 0.05, ctypes.c_void_p(16),
+                                  None, None, None, None) == -1
+    assert L.spec_av_score_update(ctypes.c_void_p(16), None, 4, 4, 0.05, ctypes.c_void_p(16),
+                                  None, None, None, None) == -1
+    assert L.spec_av_score_update(ctypes.c_void_p(16), ctypes.c_void_p(16), 4, 65, 0.05,
+                                  ctypes.c_void_p(16), None, None, None, None) == -2
+    assert L.spec_av_score_update(ctypes.c_void_p(16), ctypes.c_void_p(16), 4, 4,
+                                  float("nan"), ctypes.c_void_p(16), None, None, None,
+                                  None) == -1
+    assert L.spec_av_score_update(None, None, 0, 4, 0.05, None, None, None, None, None) == 0
     assert L.spec_read_probe(ctypes.c_void_p(16), 4, 24, 32, ctypes.c_void_p(16), None) == -1
     assert L.spec_read_probe(ctypes.c_void_p(16), 4, 48, 32, ctypes.c_void_p(16), None) == -1
     assert L.spec_read_probe(ctypes.c_void_p(16), 4, 32, 32, None, None) == -1

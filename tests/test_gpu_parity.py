@@ -509,6 +509,29 @@ def test_av_step_call_matches_separate_calls(tau):
         assert torch.equal(ob_a, ob_b)
 
 
+@pytest.mark.parametrize("B,K", [(20, 5), (300, 7), (64, 64)])
+def test_av_score_update_matches_score_then_update(B, K):
+    # one launch for an untrimmed step's scores and SGD step, against
+    # spec_av_score_stats (tau = 0) followed by spec_av_update (kept NULL):
+    # bit-identical scores, masks, kept lengths and coefficients.  B*K above
+    # the workgroup's 512 threads makes threads score several drafts.
+    g = torch.Generator().manual_seed(B * 100 + K)
+    ds = torch.zeros(sv.draft_stats_bytes(B, K), dtype=torch.uint8)
+    sv.draft_stats_view(ds, B, K)["feat"].copy_(torch.randn(B * K, generator=g) * 1.3 - 1.2)
+    ds = ds.to(DEV)
+    acc = torch.randint(0, K + 1, (B,), generator=g, dtype=torch.int32).to(DEV)
+    ob_a = torch.tensor(W.av_init(1, K=K), dtype=torch.float32, device=DEV)
+    ob_b = ob_a.clone()
+    for step in range(3):
+        c_a, m_a, k_a = sv.av_score_update(ds, acc, ob_a, 0.05, B, K)
+        c_b, m_b, k_b = sv.av_score_stats(ds, B, K, ob_b, 0.0)
+        sv.av_update(ds, acc, None, ob_b, 0.05, B, K)
+        torch.cuda.synchronize()
+        assert torch.equal(c_a, c_b) and torch.equal(m_a, m_b) and torch.equal(k_a, k_b)
+        assert torch.equal(ob_a, ob_b)
+        assert (k_a == K).all() and (m_a == 1).all()
+
+
 def test_verify_exports_draft_stats():
     # the draft statistics a lossless call computes itself, exported, equal
     # those of spec_av_score bit for bit; scoring from them equals spec_av_score
