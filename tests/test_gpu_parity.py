@@ -48,6 +48,9 @@ def _special_rows(V, dtype, stride, seed):
     return xd.to(dtype)
 
 
+# lse is compared relative to max(|lse|, 1) (abs_floor = rel): an error d in
+# lse is a relative error d in every probability exp(l/T - lse), and lse
+# passes through 0, where a purely relative bound would demand more than that.
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("V,stride", [(2, 8), (9, 16), (1003, 1008), (4097, 4104),
                                       (32000, 32000), (128256, 128256), (152064, 152064)])
@@ -60,7 +63,7 @@ def test_row_stats_parity(dtype, V, stride, T):
     o = ref.rows_stats(host_logits(xh), temperature=f32(T), V=V, nthreads=NT)
     rel = REL_TOL[dtype]
     assert np.array_equal(np_(r["argmax"]), o["argmax"])
-    assert_close(np_(r["lse"]), o["lse"], rel, "lse")
+    assert_close(np_(r["lse"]), o["lse"], rel, "lse", abs_floor=rel)
     assert_close(np_(r["entropy"]), o["h"], rel, "entropy", abs_floor=1e-12)
     assert_close(np_(r["qmax"]), o["qmax"], rel, "qmax")
     # logit(q_max) passes through 0: relative to max(|feat|, 1)
@@ -79,7 +82,7 @@ def test_row_stats_extreme_temperatures(dtype, T):
         o = ref.rows_stats(host_logits(xh), temperature=f32(T), V=V, nthreads=NT)
         rel = REL_TOL[dtype]
         assert np.array_equal(np_(r["argmax"]), o["argmax"])
-        assert_close(np_(r["lse"]), o["lse"], rel, "lse")
+        assert_close(np_(r["lse"]), o["lse"], rel, "lse", abs_floor=rel)
         assert_close(np_(r["entropy"]), o["h"], rel, "entropy", abs_floor=1e-12)
         assert_close(np_(r["qmax"]), o["qmax"], rel, "qmax")
         assert_close(np_(r["feat"]), o["feat"], rel, "feat", abs_floor=rel)
@@ -116,7 +119,10 @@ def test_read_probe_folds_every_word():
 # ---------------------------------------------------------------------------
 # FLy
 # ---------------------------------------------------------------------------
-def _fly_check(batch, theta=0.3, window=4, kept=None):
+def _fly_check(batch, theta=0.3, window=4, kept=None, kept_ref=None):
+    # kept_ref: the oracle's kept lengths, when the library's are meant to be
+    # clamped into [0, K] first (the oracle takes only values in range)
+    kept_ref = kept if kept_ref is None else kept_ref
     t = batch.target.to(DEV)
     tok = batch.tokens.to(DEV)
     kept_d = None if kept is None else kept.to(DEV)
@@ -125,14 +131,14 @@ def _fly_check(batch, theta=0.3, window=4, kept=None):
     torch.cuda.synchronize()
     o = ref.verify(host_logits(batch.target), None, np_(batch.tokens), 0, ref.MODE_FLY,
                    theta=f32(theta), window=window, V=batch.V,
-                   kept_len=None if kept is None else np_(kept), nthreads=NT)
+                   kept_len=None if kept_ref is None else np_(kept_ref), nthreads=NT)
     nm, nb = compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ref.NEAR_GATE, "fly")
     rel = REL_TOL[batch.target.dtype]
     assert np.array_equal(np_(r.target_argmax), o["t_argmax"])
-    assert_close(np_(r.target_lse), o["t_lse"], rel, "target lse")
+    assert_close(np_(r.target_lse), o["t_lse"], rel, "target lse", abs_floor=rel)
     assert_close(np_(r.target_entropy), o["t_h"], rel, "target entropy", abs_floor=1e-12)
     check_token_layout(np_(r.accepted_len), np_(r.tokens), np_(batch.tokens),
-                       None if kept is None else np_(kept))
+                       None if kept_ref is None else np_(kept_ref))
     return r, o, nm, nb
 
 
@@ -207,7 +213,8 @@ def test_fly_headline_full_size():
 # ---------------------------------------------------------------------------
 # Lossless
 # ---------------------------------------------------------------------------
-def _lossless_check(batch, seed, kept=None, draft_stats_path=False):
+def _lossless_check(batch, seed, kept=None, draft_stats_path=False, kept_ref=None):
+    kept_ref = kept if kept_ref is None else kept_ref
     t = batch.target.to(DEV)
     d = batch.draft.to(DEV)
     tok = batch.tokens.to(DEV)
@@ -222,19 +229,19 @@ def _lossless_check(batch, seed, kept=None, draft_stats_path=False):
                   draft_stats=ds, stats=True)
     torch.cuda.synchronize()
     o = ref.verify(host_logits(batch.target), host_logits(batch.draft), np_(batch.tokens), seed,
-                   temperature=f32(T), V=batch.V, kept_len=None if kept is None else np_(kept),
-                   nthreads=NT)
+                   temperature=f32(T), V=batch.V,
+                   kept_len=None if kept_ref is None else np_(kept_ref), nthreads=NT)
     nm, nb = compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ALL_NEAR, "lossless")
     rel = REL_TOL[batch.target.dtype]
     assert np.array_equal(np_(r.target_argmax), o["t_argmax"])
-    assert_close(np_(r.target_lse), o["t_lse"], rel, "target lse")
+    assert_close(np_(r.target_lse), o["t_lse"], rel, "target lse", abs_floor=rel)
     assert_close(np_(r.target_entropy), o["t_h"], rel, "target entropy", abs_floor=1e-12)
     if not draft_stats_path:
-        assert_close(np_(r.draft_lse), o["d_lse"], rel, "draft lse")
+        assert_close(np_(r.draft_lse), o["d_lse"], rel, "draft lse", abs_floor=rel)
         assert_close(np_(r.draft_qmax), o["d_qmax"], rel, "draft qmax")
         assert_close(np_(r.draft_feat), o["d_feat"], rel, "draft feat", abs_floor=rel)
     check_token_layout(np_(r.accepted_len), np_(r.tokens), np_(batch.tokens),
-                       None if kept is None else np_(kept))
+                       None if kept_ref is None else np_(kept_ref))
     return r, o, nm, nb
 
 
@@ -593,3 +600,53 @@ def test_invalid_arguments_raise():
         sv.verify(t, d, tok, seed=0, vocab=65)                # V > stride
     with pytest.raises(sv.SpecVerifyError):
         sv.verify(t[:, :, :62].contiguous(), d[:, :, :62].contiguous(), tok, seed=0)  # 248 B rows
+
+
+# ---------------------------------------------------------------------------
+# Randomised configurations: every option at once, drawn from fixed seeds
+# ---------------------------------------------------------------------------
+def _random_batch(rng):
+    mode = str(rng.choice(["lossless", "fly"]))
+    K = int(rng.integers(1, 11)) if rng.random() > 0.1 else 64
+    B = int(rng.integers(1, 49)) if K < 64 else int(rng.integers(1, 5))
+    V = int(np.exp(rng.uniform(np.log(2), np.log(200000))))
+    if B * (2 * K + 1) * V > 3e7:  # keep the oracle's share to a fraction of a second
+        V = max(2, int(3e7 / (B * (2 * K + 1))))
+    stride = (V + 7) // 8 * 8 + 8 * int(rng.integers(0, 3))
+    f32 = bool(rng.random() < 0.5)
+    seed = int(rng.integers(0, 1 << 30))
+    if mode == "lossless":
+        T = float(rng.choice([1.0, 0.7, float(np.exp(rng.uniform(np.log(0.2), np.log(5.0))))]))
+        if rng.random() < 0.5:
+            batch = W.gaussian(B, K, V, "f32" if f32 else "bf16", T, seed=seed, token_seed=1,
+                               stride=stride)
+        else:
+            batch = W.zipf(B, K, V, T, seed=seed, token_seed=1, stride=stride)
+            if f32:
+                batch.target, batch.draft = batch.target.float(), batch.draft.float()
+    else:
+        V = max(V, 5)  # the recipe draws deviations from the top 5
+        stride = max(stride, (V + 7) // 8 * 8)
+        batch = W.fly(B, K, V, seed=seed, stride=stride)
+        if f32:
+            batch.target = batch.target.float()
+    kept = None
+    if rng.random() < 0.4:
+        kept = torch.from_numpy(rng.integers(-1, K + 3, B).astype(np.int32))
+    return mode, batch, kept, rng
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_configurations(case):
+    # mode, recipe, dtype, B, K (up to 64), V (2 to 200000), padded stride,
+    # temperature, kept lengths (some outside [0, K]), FLy threshold and window
+    mode, batch, kept, rng = _random_batch(np.random.default_rng(9000 + case))
+    K = batch.tokens.shape[1]
+    kept_ref = None if kept is None else kept.clamp(0, K)  # the library clamps into [0, K]
+    if mode == "lossless":
+        for seed in range(2):
+            _lossless_check(batch, seed=seed, kept=kept, kept_ref=kept_ref)
+    else:
+        theta = float(rng.uniform(0.0, 1.2))
+        window = int(rng.integers(0, K + 2))
+        _fly_check(batch, theta=theta, window=window, kept=kept, kept_ref=kept_ref)
