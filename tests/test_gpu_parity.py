@@ -656,3 +656,24 @@ def test_random_configurations(case):
         theta = float(rng.uniform(0.0, 1.2))
         window = int(rng.integers(0, K + 2))
         _fly_check(batch, theta=theta, window=window, kept=kept, kept_ref=kept_ref)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_av_steps(case):
+    # adaptive-verification steps (score, trim at a random tau, verify the kept
+    # drafts, SGD update) on random shapes, dtypes and temperatures
+    rng = np.random.default_rng(7000 + case)
+    K = int(rng.integers(1, 13)) if case % 4 else 64
+    B = int(rng.integers(1, 65)) if K < 64 else int(rng.integers(1, 6))
+    V = int(np.exp(rng.uniform(np.log(8), np.log(60000))))
+    V = max(8, min(V, int(2e7 / (B * (2 * K + 1)))))
+    stride = (V + 7) // 8 * 8 + 8 * int(rng.integers(0, 2))
+    dtype = "f32" if rng.random() < 0.5 else "bf16"
+    T = float(rng.choice([1.0, float(np.exp(rng.uniform(np.log(0.5), np.log(2.0))))]))
+    batch = W.gaussian(B, K, V, dtype, T, seed=int(rng.integers(0, 1 << 30)), token_seed=2,
+                       stride=stride)
+    tau = 0.0 if rng.random() < 0.3 else float(rng.uniform(0.02, 0.6))
+    lr = float(rng.uniform(0.01, 0.2))
+    ob0 = [float(rng.uniform(0.3, 1.5))] + [float(v) for v in rng.uniform(-1.0, 1.0, K)]
+    got, want, _, okept = _av_step(batch, ob0, tau=tau, lr=lr, seed=case)
+    assert np.allclose(got, want, rtol=0, atol=1e-5), (got, want)
