@@ -255,3 +255,40 @@ def test_ngram_parity(B, S, alphabet, n_min, n_max, K):
     o = ref.ngram_propose(ctx, np.minimum(gl, S), n_min, n_max, K)
     for k in ("draft", "draft_len", "match_pos", "match_n"):
         assert np.array_equal(np_(r[k]), o[k]), k
+
+
+# ---------------------------------------------------------------------------
+# Randomised shapes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", range(16))
+def test_random_budget_and_ngram(case):
+    # the budgeted trim on random batch shapes and confidence mixes (ties at
+    # 1, near-zero confidences), and prompt lookup on random shapes, alphabets
+    # and n-gram ranges
+    rng = np.random.default_rng(3000 + case)
+    B, K = int(rng.integers(1, 700)), int(rng.integers(1, 17))
+    conf = rng.uniform(0.0, 1.0, (B, K)).astype(np.float32)
+    conf[rng.random((B, K)) < 0.1] = 1.0
+    conf[rng.random((B, K)) < 0.05] = np.float32(1e-6)
+    cost = W.budget_costs(B, K, per_request=float(rng.uniform(0.001, 0.05)),
+                          per_draft=float(rng.uniform(0.0005, 0.01)),
+                          curve=float(rng.uniform(0.1, 5.0)))
+    c_d, cost_d = _to_dev(conf, cost)
+    r = sv.av_budget(c_d, cost_d)
+    o = ref.av_budget(conf, cost)
+    if not o["near"]:
+        assert int(np_(r["budget"])[0]) == o["budget"]
+        assert np.array_equal(np_(r["kept_len"]), o["kept_len"])
+        assert np.array_equal(np_(r["mask"]), o["mask"])
+
+    Bn, S = int(rng.integers(1, 80)), int(rng.integers(1, 3000))
+    alphabet = int(rng.choice([2, 3, 10, 100, 50000]))
+    n_min = int(rng.integers(1, 6))
+    n_max = int(rng.integers(n_min, min(32, n_min + 8) + 1))
+    Kn = int(rng.integers(1, 65))
+    ctx, lens = _contexts(rng, Bn, S, alphabet)
+    c_d, l_d = _to_dev(ctx, lens)
+    rn = sv.ngram_propose(c_d, l_d, n_min, n_max, Kn)
+    on = ref.ngram_propose(ctx, lens, n_min, n_max, Kn)
+    for k in ("draft", "draft_len", "match_pos", "match_n"):
+        assert np.array_equal(np_(rn[k]), on[k]), k
