@@ -28,7 +28,7 @@ def hipcc() -> str:
 
 def compile_command(out: str) -> list[str]:
     return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Wall", "-Wno-unused-function",
+            "-Wall", "-Wextra", "-Wno-unused-function",
             # no packed-fp32 instructions (see the design notes)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),

@@ -133,9 +133,10 @@ __device__ __forceinline__ void sgd_step(const float *feat, const int32_t *accep
         // every thread has read omega_beta (inside label_sums) before the barrier
         if (threadIdx.x == 0)
             omega_beta[0] = static_cast<float>(static_cast<double>(omega_beta[0]) - l * s_go);
-        if (threadIdx.x < K)
-            omega_beta[1 + threadIdx.x] = static_cast<float>(
-                static_cast<double>(omega_beta[1 + threadIdx.x]) - l * sums[threadIdx.x].r);
+        const int t = threadIdx.x;
+        if (t < K)
+            omega_beta[1 + t] =
+                static_cast<float>(static_cast<double>(omega_beta[1 + t]) - l * sums[t].r);
     }
 }
 
@@ -366,12 +367,13 @@ __global__ __launch_bounds__(kDiagTile) void diag_pairs_kernel(DiagWs ws, int re
         if (threadIdx.x == 0) ws.pairs[blockIdx.x] = 0ull;
         return;
     }
-    if (threadIdx.x == 0) acc = 0ull;
-    if (threadIdx.x < nn) zn[threadIdx.x] = ws.zneg[rj * kDiagTile + threadIdx.x];
-    const double zp = threadIdx.x < np ? ws.zpos[ri * kDiagTile + threadIdx.x] : 0.0;
+    const int t = threadIdx.x;
+    if (t == 0) acc = 0ull;
+    if (t < nn) zn[t] = ws.zneg[rj * kDiagTile + t];
+    const double zp = t < np ? ws.zpos[ri * kDiagTile + t] : 0.0;
     __syncthreads();
     unsigned int c = 0;
-    if (threadIdx.x < np)
+    if (t < np)
         for (int k = 0; k < nn; ++k) c += zp > zn[k] ? 2u : (zp == zn[k] ? 1u : 0u);
     const uint64_t wc = wave_sum_u64(c);
     if ((threadIdx.x & (kWave - 1)) == 0) atomicAdd(&acc, static_cast<unsigned long long>(wc));
