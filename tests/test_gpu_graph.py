@@ -112,3 +112,39 @@ def test_av_step_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(ob, want_ob) and torch.equal(out.accepted_len, want_acc)
+
+
+def test_av_step_untrimmed_replays():
+    # the tau <= 0 step: a verify that exports the draft statistics, then the
+    # one-launch score and SGD step, recorded and replayed
+    b = W.make(1, B=40, V=5000, stride=5000)
+    t, d, tok = b.target.to(DEV), b.draft.to(DEV), b.tokens.to(DEV)
+    B, K = tok.shape
+    ob0 = torch.tensor(W.av_init(1), dtype=torch.float32, device=DEV)
+    ob = ob0.clone()
+    ws = torch.empty(sv.workspace_bytes(B, K, 5000), dtype=torch.uint8, device=DEV)
+    out = _result(B, K)
+    out.draft_stats_out = torch.empty(sv.draft_stats_bytes(B, K), dtype=torch.uint8, device=DEV)
+    res = {}
+
+    def step():
+        sv.verify(t, d, tok, seed=2, vocab=5000, workspace=ws, out=out)
+        res["conf"], _, _ = sv.av_score_update(out.draft_stats_out, out.accepted_len, ob, 0.05,
+                                               B, K)
+    step()
+    torch.cuda.synchronize()
+    want_ob, want_acc, want_conf = ob.clone(), out.accepted_len.clone(), res["conf"].clone()
+    ob.copy_(ob0)
+    step()  # warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    ob.copy_(ob0)
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        ob.copy_(ob0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ob, want_ob) and torch.equal(out.accepted_len, want_acc)
+        assert torch.equal(res["conf"], want_conf)
