@@ -20,11 +20,11 @@
 // Arithmetic is in base 2: with c = log2(e)/T every term is 2^(l*c - mc),
 // where mc = m*c and m is the running maximum of the raw logits.  A thread
 // reads its share of the row in chunks of UNROLL vectors (UNROLL*8 bfloat16
-// or UNROLL*4 float logits); terms are summed in float inside a chunk and
-// chunk sums in double.  Each thread keeps the chunk that holds its maximum
-// apart (its sums and its raw data in registers), so the end can replace that
-// chunk by its terms other than the argmax and form 1 - q_max without
-// cancellation, however peaked the row.
+// or UNROLL*4 float logits); a thread sums its terms and its chunk sums in
+// float, and the sums across threads are formed in double.  Each thread keeps
+// the chunk that holds its maximum apart (its sums in registers, its raw data
+// in LDS), so the end can replace that chunk by its terms other than the
+// argmax and form 1 - q_max without cancellation, however peaked the row.
 #pragma once
 
 #include "sv_common.hpp"

@@ -173,18 +173,6 @@ spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,
                           void *stream);
 
 /*
- * spec_av_update -- one online SGD step of the estimator ([AV] section
- * "Ajuste de los Coeficientes" for the labels: drafts up to and including the
- * first rejection; accepted = 1, the first rejected = 0, nothing else
- * labelled).  With N labels over the batch and s_n the pre-step prediction:
- *   omega  -= lr * (1/N) sum_n (s_n - y_n) feat_n
- *   beta_i -= lr * (1/N) sum_{n at position i} (s_n - y_n)
- * N = 0 leaves the parameters unchanged.  draft_stats: filled by
- * spec_av_score; accepted_len: from spec_verify; kept_len: device int32 [B]
- * or NULL (= K); omega_beta: device float[K+1], updated in place.  Single
- * workgroup (a wave per position), fixed-order double-precision sums.
- */
-/*
  * spec_av_score_stats -- the scoring and trimming of spec_av_score from
  * draft statistics that are already computed (by spec_av_score, or by
  * spec_verify through draft_stats_out), without reading any draft row:
@@ -198,6 +186,18 @@ spec_status spec_av_score_stats(const void *draft_stats, int32_t batch, int32_t 
                                 const float *omega_beta, float tau, float *conf,
                                 uint8_t *keep_mask, int32_t *kept_len, void *stream);
 
+/*
+ * spec_av_update -- one online SGD step of the estimator ([AV] section
+ * "Ajuste de los Coeficientes" for the labels: drafts up to and including the
+ * first rejection; accepted = 1, the first rejected = 0, nothing else
+ * labelled).  With N labels over the batch and s_n the pre-step prediction:
+ *   omega  -= lr * (1/N) sum_n (s_n - y_n) feat_n
+ *   beta_i -= lr * (1/N) sum_{n at position i} (s_n - y_n)
+ * N = 0 leaves the parameters unchanged.  draft_stats: filled by
+ * spec_av_score; accepted_len: from spec_verify; kept_len: device int32 [B]
+ * or NULL (= K); omega_beta: device float[K+1], updated in place.  Single
+ * workgroup (a wave per position), fixed-order double-precision sums.
+ */
 spec_status spec_av_update(const void *draft_stats, const int32_t *accepted_len,
                            const int32_t *kept_len, int32_t batch, int32_t num_draft, float lr,
                            float *omega_beta, void *stream);

@@ -72,7 +72,7 @@ def lib():
         L.ref_fly_resolve.argtypes = [ctypes.c_int, ctypes.c_int, f64, P, P, P]
         L.ref_fly_resolve.restype = ctypes.c_int
         L.ref_verify.argtypes = [P, P, P, P, i32, i32, i64, i64, i32, f64, u64, i32, f64, i32,
-                                 P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+                                 P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
         L.ref_verify.restype = ctypes.c_int
         L.ref_av_score.argtypes = [P, i32, i32, P, f64, P, P, P, P]
         L.ref_av_score.restype = None
@@ -169,12 +169,14 @@ def residual(p, q):
 
 
 def fly_resolve(dev, h, W, theta):
+    """Returns (accepted count, near-gate flag, smallest |h - theta| over the
+    evaluated gates)."""
     dev = np.ascontiguousarray(dev, dtype=np.int32)
     h = np.ascontiguousarray(h, dtype=np.float64)
-    near = ctypes.c_int(0)
+    gap = ctypes.c_double(0.0)
     n = lib().ref_fly_resolve(int(dev.shape[0]), int(W), float(theta), _ptr(dev), _ptr(h),
-                              ctypes.byref(near))
-    return int(n), bool(near.value)
+                              ctypes.byref(gap))
+    return int(n), bool(gap.value < 1e-5), float(gap.value)
 
 
 def verify(target, draft, tokens, seed, mode=MODE_LOSSLESS, *, temperature=1.0, theta=0.3,
@@ -198,13 +200,15 @@ def verify(target, draft, tokens, seed, mode=MODE_LOSSLESS, *, temperature=1.0, 
         "t_argmax": np.zeros((B, K + 1), dtype=np.int64),
         "d_lse": np.zeros((B, K)), "d_qmax": np.zeros((B, K)), "d_feat": np.zeros((B, K)),
         "boundary": np.zeros(B, dtype=np.uint32), "race_gap": np.zeros(B),
+        "accept_gap": np.zeros(B), "gate_gap": np.zeros(B),
     }
     rc = lib().ref_verify(_ptr(t), _ptr(d), _ptr(tok), _ptr(kl), B, K, V, stride, dt,
                           float(temperature), int(seed), int(mode), float(theta), int(window),
                           _ptr(r["accepted_len"]), _ptr(r["tokens"]), _ptr(r["t_lse"]),
                           _ptr(r["t_h"]), _ptr(r["t_argmax"]), _ptr(r["d_lse"]),
                           _ptr(r["d_qmax"]), _ptr(r["d_feat"]), _ptr(r["boundary"]),
-                          _ptr(r["race_gap"]), nthreads or default_threads())
+                          _ptr(r["race_gap"]), _ptr(r["accept_gap"]), _ptr(r["gate_gap"]),
+                          nthreads or default_threads())
     if rc != 0:
         raise ValueError("ref_verify rejected its arguments")
     return r

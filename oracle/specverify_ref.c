@@ -271,14 +271,16 @@ void ref_residual(const double *p, const double *q, int64_t V, double *w) {
 /* accepted and the scan resumes after the window.                            */
 /* ------------------------------------------------------------------------ */
 int ref_fly_resolve(int L, int W, double theta, const int32_t *dev, const double *h,
-                    int *gate_near) {
+                    double *gate_gap) {
     int j = 0;
+    if (gate_gap) *gate_gap = INFINITY;
     while (j < L) {
         if (!dev[j]) {
             ++j;
             continue;
         }
-        if (gate_near && fabs(h[j] - theta) < 1e-5) *gate_near = 1;
+        /* distance of this evaluated gate from its threshold */
+        if (gate_gap && fabs(h[j] - theta) < *gate_gap) *gate_gap = fabs(h[j] - theta);
         if (h[j] < theta) return j; /* low entropy: treat as a real error */
         if (j + W > L - 1) return j; /* window cannot be filled */
         for (int k = j + 1; k <= j + W; ++k)
@@ -313,7 +315,7 @@ typedef struct {
     double theta;
     int32_t W;
     int32_t *accepted_len, *out_tokens;
-    double *t_lse, *t_h, *d_lse, *d_qmax, *d_feat, *race_gap;
+    double *t_lse, *t_h, *d_lse, *d_qmax, *d_feat, *race_gap, *accept_gap, *gate_gap;
     int64_t *t_argmax;
     uint32_t *boundary;
     double **scratch; /* per thread: 3*V doubles */
@@ -346,6 +348,7 @@ static void verify_one(verify_ctx *c, int64_t b, double *p, double *q, double *w
     int32_t jstar = L;
     int64_t y = -1;
     double gap = NAN;
+    double agap = INFINITY, ggap = INFINITY; /* nearest evaluated accept test / gate */
     if (c->mode == REF_MODE_LOSSLESS) {
         for (int32_t j = 0; j < L; ++j) {
             int32_t x = tok[j];
@@ -356,6 +359,7 @@ static void verify_one(verify_ctx *c, int64_t b, double *p, double *q, double *w
             }
             double ratio = exp(logp - logq); /* p(x_j)/q(x_j); NaN for a token outside V */
             double u = ref_uniform(c->seed, 0u, (uint32_t)j, (uint32_t)b, REF_TAG_ACCEPT);
+            if (fabs(u - ratio) < agap) agap = fabs(u - ratio); /* NaN ratio: skipped */
             if (fabs(u - ratio) < 1e-5) near |= REF_NEAR_ACCEPT;
             if (!(u < ratio)) {
                 jstar = j;
@@ -386,9 +390,8 @@ static void verify_one(verify_ctx *c, int64_t b, double *p, double *q, double *w
             dev[j] = tok[j] != ts[j].argmax;
             hh[j] = ts[j].h;
         }
-        int gate_near = 0;
-        jstar = ref_fly_resolve(L, c->W, c->theta, dev, hh, &gate_near);
-        if (gate_near) near |= REF_NEAR_GATE;
+        jstar = ref_fly_resolve(L, c->W, c->theta, dev, hh, &ggap);
+        if (ggap < 1e-5) near |= REF_NEAR_GATE;
         y = ts[jstar].argmax;
     }
 
@@ -411,6 +414,8 @@ static void verify_one(verify_ctx *c, int64_t b, double *p, double *q, double *w
     }
     if (c->boundary) c->boundary[b] = near;
     if (c->race_gap) c->race_gap[b] = gap;
+    if (c->accept_gap) c->accept_gap[b] = agap;
+    if (c->gate_gap) c->gate_gap[b] = ggap;
 }
 
 static void verify_range(void *vctx, int64_t lo, int64_t hi, int tid) {
@@ -424,7 +429,8 @@ int ref_verify(const void *target, const void *draft, const int32_t *tokens,
                int32_t dtype, double temperature, uint64_t seed, int32_t mode, double theta,
                int32_t W, int32_t *accepted_len, int32_t *out_tokens, double *t_lse,
                double *t_h, int64_t *t_argmax, double *d_lse, double *d_qmax, double *d_feat,
-               uint32_t *boundary, double *race_gap, int nthreads) {
+               uint32_t *boundary, double *race_gap, double *accept_gap, double *gate_gap,
+               int nthreads) {
     if (B < 0 || K < 1 || V < 2 || stride < V || !(temperature > 0.0)) return -1;
     if (dtype != 0 && dtype != 1) return -1;
     if (mode != REF_MODE_LOSSLESS && mode != REF_MODE_FLY) return -1;
@@ -448,7 +454,8 @@ int ref_verify(const void *target, const void *draft, const int32_t *tokens,
     }
     verify_ctx c = {target, draft, tokens, kept_len, B, K, V, stride, dtype, temperature,
                     seed, mode, theta, W, accepted_len, out_tokens, t_lse, t_h, d_lse,
-                    d_qmax, d_feat, race_gap, t_argmax, boundary, scratch};
+                    d_qmax, d_feat, race_gap, accept_gap, gate_gap, t_argmax, boundary,
+                    scratch};
     parallel_ranges(verify_range, &c, B, nthreads);
     for (int t = 0; t < nthreads; ++t) free(scratch[t]);
     return 0;

@@ -80,24 +80,30 @@ void ref_residual(const double *p, const double *q, int64_t V, double *w);
 
 /* FLy two-level resolver over a draft of length L: dev[j] != 0 marks a
  * deviation from the target's top prediction, h[j] the target's normalised
- * entropy.  Returns the number of accepted draft tokens; *gate_near (nullable)
- * is set to 1 when an evaluated gate had |h - theta| < 1e-5. */
+ * entropy.  Returns the number of accepted draft tokens; *gate_gap (nullable)
+ * receives the smallest |h_j - theta| over the gates the scan evaluated
+ * (+inf when none); the gate is a boundary case when that is below 1e-5. */
 int ref_fly_resolve(int L, int W, double theta, const int32_t *dev, const double *h,
-                    int *gate_near);
+                    double *gate_gap);
 
 /* Full verification of B sequences (see specverify_ref.c for the steps).
  * target: [B][K+1] rows, draft: [B][K] rows (may be NULL in FLy mode), both
  * with the same V, stride and dtype.  tokens: [B][K] draft tokens.
  * kept_len: [B] or NULL (= K).  Outputs: accepted_len [B], out_tokens
  * [B][K+1] (-1 after the last emitted token), optional per-row statistics
- * (NaN / -1 for rows that were not evaluated), boundary bits [B] and the race
- * gap [B] (NaN when no race ran).  Returns 0, or -1 on bad arguments. */
+ * (NaN / -1 for rows that were not evaluated), boundary bits [B], the race
+ * gap [B] ((k1 - k2)/k1 of the two largest race keys; NaN when no race ran),
+ * and the distances behind the other two near-tie bits, each nullable:
+ * accept_gap [B], the smallest |u_j - p/q| over the evaluated accept tests,
+ * and gate_gap [B], the smallest |h_j - theta| over the evaluated FLy gates
+ * (+inf when there were none).  Returns 0, or -1 on bad arguments. */
 int ref_verify(const void *target, const void *draft, const int32_t *tokens,
                const int32_t *kept_len, int32_t B, int32_t K, int64_t V, int64_t stride,
                int32_t dtype, double temperature, uint64_t seed, int32_t mode, double theta,
                int32_t W, int32_t *accepted_len, int32_t *out_tokens, double *t_lse,
                double *t_h, int64_t *t_argmax, double *d_lse, double *d_qmax,
-               double *d_feat, uint32_t *boundary, double *race_gap, int nthreads);
+               double *d_feat, uint32_t *boundary, double *race_gap, double *accept_gap,
+               double *gate_gap, int nthreads);
 
 /* AV scorer and trimming: c = sigmoid(omega*feat + beta_i), P_i = prod c,
  * keep while P_i >= tau (tau <= 0 keeps everything).  feat: [B][K];

@@ -34,7 +34,7 @@ def test_exhaustive_against_characterisation(oracle, L, W):
         for gates in itertools.product([0.1, 0.7], repeat=len(devpos)):
             h = np.full(L, 0.5)
             h[devpos] = gates
-            n, _ = oracle.fly_resolve(np.array(dev), h, W, theta)
+            n = oracle.fly_resolve(np.array(dev), h, W, theta)[0]
             assert n == first_inadmissible(dev, list(h), W, theta), (dev, list(h), W)
 
 
