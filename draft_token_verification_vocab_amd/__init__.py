@@ -27,6 +27,11 @@ MODE_LOSSLESS = 0
 MODE_FLY = 1
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+# boundary-case bits of VerifyResult.boundary (see include/specverify.h)
+NEAR_ACCEPT = 1
+NEAR_RACE = 2
+RESIDUAL_EMPTY = 4
+NEAR_GATE = 8
 
 
 class SpecVerifyError(RuntimeError):
@@ -46,7 +51,7 @@ class _VerifyOut(ctypes.Structure):
                 ("target_lse", ctypes.c_void_p), ("target_entropy", ctypes.c_void_p),
                 ("target_argmax", ctypes.c_void_p), ("draft_lse", ctypes.c_void_p),
                 ("draft_qmax", ctypes.c_void_p), ("draft_feat", ctypes.c_void_p),
-                ("draft_stats_out", ctypes.c_void_p)]
+                ("draft_stats_out", ctypes.c_void_p), ("boundary", ctypes.c_void_p)]
 
 
 # Every symbol the header declares, with its ctypes signature.
@@ -170,16 +175,28 @@ class VerifyResult:
     # a draft-statistics buffer (draft_stats_bytes) that a lossless call reading
     # the draft rows itself also fills
     draft_stats_out: Optional[torch.Tensor] = None
+    # uint32 [B] (as int32): each sequence's boundary-case bits (NEAR_* above)
+    boundary: Optional[torch.Tensor] = None
+
+    def fields(self):
+        """The output pointers in the order of spec_verify_out."""
+        return _VerifyOut(*[None if t is None else t.data_ptr() for t in (
+            self.accepted_len, self.tokens, self.target_lse, self.target_entropy,
+            self.target_argmax, self.draft_lse, self.draft_qmax, self.draft_feat,
+            self.draft_stats_out, self.boundary)])
 
 
 def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: torch.Tensor,
            seed: int, mode: int = MODE_LOSSLESS, *, temperature: float = 1.0,
            fly_theta: float = 0.3, fly_window: int = 4, kept_len: Optional[torch.Tensor] = None,
            draft_stats: Optional[torch.Tensor] = None, vocab: Optional[int] = None,
-           stats: bool = False, workspace: Optional[torch.Tensor] = None,
+           stats: bool = False, boundary: bool = False,
+           workspace: Optional[torch.Tensor] = None,
            out: Optional[VerifyResult] = None) -> VerifyResult:
     """Verify drafts.  target: [B, K+1, S] and draft: [B, K, S] logits (S >= V
-    is the row stride; V defaults to S), draft_tokens: int32 [B, K]."""
+    is the row stride; V defaults to S), draft_tokens: int32 [B, K].
+    stats: also return the per-row statistics; boundary: also return each
+    sequence's boundary-case bits."""
     _need_cuda(target, "target")
     B, K1, S = target.shape
     K = K1 - 1
@@ -209,9 +226,9 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
                 out.draft_lse = torch.empty(B, K, dtype=torch.float32, device=dev)
                 out.draft_qmax = torch.empty(B, K, dtype=torch.float32, device=dev)
                 out.draft_feat = torch.empty(B, K, dtype=torch.float32, device=dev)
-    o = _VerifyOut(*[None if t is None else t.data_ptr() for t in (
-        out.accepted_len, out.tokens, out.target_lse, out.target_entropy, out.target_argmax,
-        out.draft_lse, out.draft_qmax, out.draft_feat, out.draft_stats_out)])
+        if boundary:
+            out.boundary = torch.empty(B, dtype=torch.int32, device=dev)
+    o = out.fields()
     need = int(L.spec_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -246,9 +263,7 @@ class VerifyCall:
             out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
                                torch.empty(B, K + 1, dtype=torch.int32, device=dev))
         self.out = out
-        self.vout = _VerifyOut(*[None if t is None else t.data_ptr() for t in (
-            out.accepted_len, out.tokens, out.target_lse, out.target_entropy, out.target_argmax,
-            out.draft_lse, out.draft_qmax, out.draft_feat, out.draft_stats_out)])
+        self.vout = out.fields()
         need = int(self.L.spec_workspace_bytes(ctypes.byref(self.params)))
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

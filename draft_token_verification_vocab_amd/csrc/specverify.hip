@@ -18,6 +18,10 @@ namespace {
 
 using namespace sv;
 
+static_assert(kNearAccept == SPEC_NEAR_ACCEPT && kNearRace == SPEC_NEAR_RACE &&
+                  kResidualEmpty == SPEC_RESIDUAL_EMPTY && kNearGate == SPEC_NEAR_GATE,
+              "the kernels' boundary bits are the ABI's");
+
 // Race shape and the number of race workgroups to aim for per launch.
 constexpr int kRaceBlock = 256;
 constexpr int kRaceTargetBlocks = 2048;
@@ -277,7 +281,7 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
         fly_kernel<kFlyBlock><<<dim3((B + seqs_per_block - 1) / seqs_per_block), dim3(kFlyBlock), 0,
                                 st>>>(
             draft_tokens, kept_len, t_am, t_h, B, K, p.fly_theta, p.fly_window,
-            out->accepted_len, out->tokens);
+            out->accepted_len, out->tokens, out->boundary);
         return launch_status();
     }
 
@@ -306,11 +310,11 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     if (p.dtype == SPEC_DTYPE_BF16) {
         race_kernel<uint16_t, kRaceBlock><<<grid, dim3(kRaceBlock), 0, st>>>(rg);
         race_combine_kernel<uint16_t, kSmallBlock><<<dim3(B), dim3(kSmallBlock), 0, st>>>(
-            rg, draft_tokens, out->accepted_len, out->tokens);
+            rg, draft_tokens, out->accepted_len, out->tokens, out->boundary);
     } else {
         race_kernel<float, kRaceBlock><<<grid, dim3(kRaceBlock), 0, st>>>(rg);
         race_combine_kernel<float, kSmallBlock><<<dim3(B), dim3(kSmallBlock), 0, st>>>(
-            rg, draft_tokens, out->accepted_len, out->tokens);
+            rg, draft_tokens, out->accepted_len, out->tokens, out->boundary);
     }
     return launch_status();
 }

@@ -25,6 +25,12 @@
 // FLy (page "Training-Free Loosely Speculative Decoding...", section
 // "2. Metodologia", part A): one wave per sequence; deviations and gate
 // passes are two ballots and the scan walks those bit masks.
+//
+// Both rules also log, per sequence, the near-ties where float arithmetic may
+// legitimately decide the other way than exact arithmetic: an evaluated
+// accept test with |u - p/q| < 1e-5, race keys whose two largest lie within
+// 1e-6 relative, a residual that vanished, an evaluated FLy gate with
+// |h - theta| < 1e-5.
 #pragma once
 
 #include "sv_common.hpp"
@@ -32,11 +38,57 @@
 
 namespace sv {
 
+// Boundary-case bits, one word per sequence.
+constexpr uint32_t kNearAccept = 1u;     // an evaluated accept test had |u - p/q| < 1e-5
+constexpr uint32_t kNearRace = 2u;       // the two largest race keys within 1e-6 relative
+constexpr uint32_t kResidualEmpty = 4u;  // max(0, p - q) vanished; the draw used p
+constexpr uint32_t kNearGate = 8u;       // an evaluated FLy gate had |h - theta| < 1e-5
+
+// A segment's race result: its largest key (ln units) with its id, and its
+// second largest key, exact whenever it lies within the screening margin of
+// the largest (below that it is only a lower bound, which decides the
+// near-tie flag the same way).
 struct RaceCand {
     double key;
-    int32_t x;      // -1: no candidate in this segment
-    int32_t jstar;  // verified position the race ran at
+    double key2;
+    int32_t x;     // -1: no candidate in this segment
+    uint32_t info; // verified position the race ran at | boundary bits << 8
 };
+
+// The two largest keys of a set of race candidates and the first one's id
+// (lowest id on equal keys; a key equal to the largest counts as the second).
+struct Top2 {
+    double k1, k2;
+    int x1;
+    __device__ __forceinline__ void init() {
+        k1 = k2 = -__builtin_inf();
+        x1 = INT_MAX;
+    }
+    __device__ __forceinline__ void add(double k, int x) {
+        if (x == INT_MAX) return;  // no candidate
+        if (k > k1 || (k == k1 && x < x1)) {
+            k2 = k1;
+            k1 = k;
+            x1 = x;
+        } else if (k > k2) {
+            k2 = k;
+        }
+    }
+    // Another set's top two: the largest of everything but the winner is the
+    // new second.
+    __device__ __forceinline__ void merge(double ok1, int ox1, double ok2) {
+        add(ok1, ox1);
+        if (ok2 > k2) k2 = ok2;
+    }
+};
+
+// The near-tie test (k1 - k2)/k1 <= 1e-6 on the linear keys w/E, written for
+// keys in ln units: 1 - exp(k2 - k1) <= 1e-6.  No candidate at all counts as
+// a near-tie.
+__device__ __forceinline__ bool near_race(double k1, double k2) {
+    if (!(k1 > -__builtin_inf())) return true;
+    return !(-expm1(k2 - k1) > 1e-6);
+}
 
 struct RaceArgs {
     const void *target;
@@ -67,12 +119,12 @@ constexpr float kScreenMargin = 1e-3f;
 
 // What the race needs of the row it runs on, besides the row itself.
 struct RowPick {
-    int jstar;   // first rejected position (L when all verified drafts pass)
-    int am;      // the target's top token at row jstar
-    int listed;  // ids the row pass listed for a draw from p at row jstar, or -1
-    int pad_;
-    double lt;   // target log2-normaliser of row jstar
-    double ld;   // draft log2-normaliser of row jstar (residual rows only)
+    int jstar;       // first rejected position (L when all verified drafts pass)
+    int am;          // the target's top token at row jstar
+    int listed;      // ids the row pass listed for a draw from p at row jstar, or -1
+    uint32_t flags;  // kNearAccept when an evaluated test sat within 1e-5 of its ratio
+    double lt;       // target log2-normaliser of row jstar
+    double ld;       // draft log2-normaliser of row jstar (residual rows only)
 };
 
 // The accept tests of sequence b and what the race needs at the first
@@ -103,19 +155,23 @@ __device__ __forceinline__ RowPick decide_lossless(const RaceArgs &a, int b, int
         }
         const int cnt = a.bonus_cnt ? a.bonus_cnt[b] : -1;
         const uint32_t uw = draw_u32(key, 0u, tid, b, kTagAccept);
-        bool rej = false;
+        bool rej = false, near = false;
         if (tid < L) {
             const double u = lattice_u64(uw);
             const double ratio = exp2(lp - lq);  // p(x_j)/q(x_j)
             rej = !(u < ratio);
+            near = fabs(u - ratio) < 1e-5;  // false for a NaN ratio
         }
         const unsigned long long m = __ballot(rej);
         const int jstar = m ? __ffsll(m) - 1 : L;
         const int listed = jstar == L ? cnt : -1;  // only a draw from p can use the list
-        if (tid == jstar) s_pick = RowPick{jstar, am, listed, 0, lt, ld};
+        // the tests evaluated are those at positions 0..jstar
+        const unsigned long long done = jstar >= kWave - 1 ? ~0ull : (2ull << jstar) - 1ull;
+        const uint32_t flags = (__ballot(near) & done) != 0ull ? kNearAccept : 0u;
+        if (tid == jstar) s_pick = RowPick{jstar, am, listed, flags, lt, ld};
         if (jstar == kWave && tid == 0) {  // K = 64 and every draft accepted: row 64
             const int r = b * (K + 1) + kWave;
-            s_pick = RowPick{jstar, a.t_am[r], listed, 0, a.t_lse2[r], 0.0};
+            s_pick = RowPick{jstar, a.t_am[r], listed, flags, a.t_lse2[r], 0.0};
         }
     }
     __syncthreads();
@@ -129,7 +185,9 @@ constexpr float kMaxNegLogE = 23.5f;
 
 // The key the race gives the target's top token am (logits xt, xd there),
 // less the screening margin: a floor that the row's best key is known to
-// reach.  -inf when am has no weight (then nothing is screened out).
+// reach.  -inf when am has no weight (then nothing is screened out).  Keys
+// are in log2 units of the normalised weight (log2 p for a draw from p), so
+// they stay small whatever the temperature and the logits' magnitude.
 __device__ __forceinline__ float race_floor(bool residual, int am, float xt, float xd, float c,
                                             double lse2_t, double lse2_d, PhiloxKey key,
                                             uint32_t pos, uint32_t seq) {
@@ -141,7 +199,7 @@ __device__ __forceinline__ float race_floor(bool residual, int am, float xt, flo
         const float w = p - qq;
         lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
     } else {
-        lw = xt * c;
+        lw = fmaf(xt, c, -static_cast<float>(lse2_t));  // log2 p
     }
     if (!(lw > -__builtin_inff())) return -__builtin_inff();
     const float e2 = -hw_log2(lattice_u32f(draw_u32(key, static_cast<uint32_t>(am), pos, seq,
@@ -149,16 +207,25 @@ __device__ __forceinline__ float race_floor(bool residual, int am, float xt, flo
     return lw - hw_log2(e2) - kScreenMargin;
 }
 
+// thr - 0.5 + lsub rounded down to float: the bound tests below compare
+// fmaf(l, -c, this) with small integers, and rounding down keeps them on the
+// side of evaluating an id however large |lsub| is.
+__device__ __forceinline__ float bound_base(float thr, float lsub) {
+    return __double2float_rd(static_cast<double>(thr) - 0.5 + static_cast<double>(lsub));
+}
+
 // Race over vectors [v_lo, v_hi) of one row (pair) with NT threads, one
 // vector per thread per trip.  RES: w = max(0, p - q) from the target and
 // draft rows; otherwise w = p of the target row.  am: the target's top token,
 // whose key (less the margin) is a floor the row's best is known to reach;
 // its logits are loaded together with the first vectors.  Returns (in thread
-// 0) the best double key and id, or id -1 when no id of the range can win.
+// 0) the best double key and id (id -1 when no id of the range can win) and
+// the second largest double key (see RaceCand).
 template <typename T, int NT, bool RES>
 __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int V, float c,
                            double cd, double inv_t, double lse2_t, double lse2_d, PhiloxKey key,
-                           uint32_t pos, uint32_t seq, int am, double *out_key, int *out_x) {
+                           uint32_t pos, uint32_t seq, int am, double *out_key, int *out_x,
+                           double *out_key2) {
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
     constexpr int NW = NT / kWave;
@@ -192,22 +259,21 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
     const float floor =
         race_floor(RES, am_ok ? am : -1, am_xt, am_xd, c, lse2_t, lse2_d, key, pos, seq);
 
-    // best: this lane's best screening key; thr: the wave's best less the
-    // margin.  An id whose key cannot reach thr is never a candidate, so it
-    // needs neither its exact weight nor its logarithms.
-    float best = floor;
-    int bx = INT_MAX;
+    // best, best2: this lane's two best screening keys; thr: the wave's best
+    // less the margin.  An id whose key cannot reach thr is never a candidate,
+    // so it needs neither its exact weight nor its logarithms.
+    float best = floor, best2 = -__builtin_inff();
+    int bx = INT_MAX, b2x = INT_MAX;
     float bt = 0.f, bd = 0.f;  // the best id's target and draft logits
     uint32_t bw = 0u;          // and its Philox word
     float thr = floor - kScreenMargin;
-    // lb = l*c - lsub bounds the log2 weight: log2 p for a residual row
-    // (w = max(0, p - q) <= p), the weight itself (up to the row's constant
-    // normaliser) for a draw from p.  The tests use a = thr - 0.5 - lb, one
-    // FMA per id: the key is below lb + 0.5 + (leading ones), so an id is a
-    // candidate only if its leading ones reach a; a block of four needs its
-    // draw only if some a <= 23 (lb + 23.5 >= thr).
-    const float lsub = RES ? lt2 : 0.f;
-    float abase = thr - 0.5f + lsub;
+    // lb = l*c - lsub bounds the log2 weight: log2 p, and w = max(0, p - q)
+    // <= p for a residual row.  The tests use a = thr - 0.5 - lb, one FMA per
+    // id: the key is below lb + 0.5 + (leading ones), so an id is a candidate
+    // only if its leading ones reach a; a block of four needs its draw only if
+    // some a <= 23 (lb + 23.5 >= thr).
+    const float lsub = lt2;
+    float abase = bound_base(thr, lsub);
     // One trip over vector vi (live: vi is in the range).  Wave-uniform: the
     // skip tests are ballots.
     auto trip = [&](const Vec &q, int vi, bool live) {
@@ -231,23 +297,28 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
                 const bool cand = need && static_cast<float>(leading_ones(w4[qi])) >= av[k];
                 const int x = static_cast<int>(base) + qi;
                 if (cand && x < V) {
+                    const float p = fmaf(xt[k], c, -lt2);  // log2 p
                     float lw;
                     if (RES) {
-                        const float p = hw_exp2(fmaf(xt[k], c, -lt2));
                         const float qq = hw_exp2(fmaf(E::elem(q.d, k), c, -ld2));
-                        const float w = p - qq;
+                        const float w = hw_exp2(p) - qq;
                         lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
                     } else {
-                        lw = xt[k] * c;  // log2 p + the row's normaliser
+                        lw = p;
                     }
                     const float e2 = -hw_log2(lattice_u32f(w4[qi]));  // E / ln 2 > 0
                     const float g = lw - hw_log2(e2);
                     if (g > best) {
+                        best2 = best;
+                        b2x = bx;
                         best = g;
                         bx = x;
                         bt = xt[k];
                         if (RES) bd = E::elem(q.d, k);
                         bw = w4[qi];
+                    } else if (g > best2) {
+                        best2 = g;
+                        b2x = x;
                     }
                     evaluated = true;
                 }
@@ -255,7 +326,7 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
         }
         if (__ballot(evaluated) != 0ull) {
             thr = fmaxf(thr, from_ordered_bits(wave_max_u32(ordered_bits(best))) - kScreenMargin);
-            abase = thr - 0.5f + lsub;
+            abase = bound_base(thr, lsub);
         }
     };
     int it = 0;
@@ -289,7 +360,7 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
 
     // Workgroup maximum of the screening keys (DPP within waves, LDS across).
     __shared__ float sh_best[NW];
-    __shared__ double sh_key[NW];
+    __shared__ double sh_key[NW], sh_key2[NW];
     __shared__ int sh_x[NW];
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     const float m = from_ordered_bits(wave_max_u32(ordered_bits(best)));
@@ -299,94 +370,95 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
 #pragma unroll
     for (int w = 1; w < NW; ++w) g1 = fmaxf(g1, sh_best[w]);
 
-    // Double-precision keys of the candidates within the margin (from the
-    // Philox word kept with each thread's best: no second draw).
-    double k64 = -__builtin_inf();
-    int kx = INT_MAX;
-    const bool near = bx != INT_MAX && best >= g1 - kScreenMargin;
-    if (near) {
-        const double u = lattice_u64(bw);
-        const double lnE = log(-log(u));
-        const double lt = static_cast<double>(bt);
+    // Double-precision keys of the candidates within the margin: a thread's
+    // best from the Philox word kept with it (no second draw), its second
+    // best (rarely within the margin) from its logits and word again.
+    auto exact_key = [&](float lt, float ld, uint32_t word, double *k, int *kx, int x) {
+        const double lnE = log(-log(lattice_u64(word)));
         if (RES) {
-            const double ld = static_cast<double>(bd);
-            const double w = exp2(lt * cd - lse2_t) - exp2(ld * cd - lse2_d);
+            const double w = exp2(static_cast<double>(lt) * cd - lse2_t) -
+                             exp2(static_cast<double>(ld) * cd - lse2_d);
             if (w > 0.0) {
-                k64 = log(w) - lnE;
-                kx = bx;
+                *k = log(w) - lnE;
+                *kx = x;
             }
         } else {
-            k64 = lt * inv_t - lnE;  // ln p(x) + lse: the same for every id
-            kx = bx;
+            *k = static_cast<double>(lt) * inv_t - lnE;  // ln p(x) + lse: the same for every id
+            *kx = x;
         }
-    }
-    // The wave's best candidate: usually one lane is near, so its values are
-    // read lane by lane rather than reduced over the whole wave.
-    double wk = -__builtin_inf();
-    int wx = INT_MAX;
-    for (uint64_t nb = __ballot(near); nb != 0ull; nb &= nb - 1ull) {
-        const int l = __builtin_ctzll(nb);
-        const uint64_t kb = static_cast<uint64_t>(__double_as_longlong(k64));
+    };
+    double k64 = -__builtin_inf(), k64b = -__builtin_inf();
+    int kx = INT_MAX, kxb = INT_MAX;
+    const bool near = bx != INT_MAX && best >= g1 - kScreenMargin;
+    const bool near2 = b2x != INT_MAX && best2 >= g1 - kScreenMargin;
+    if (near) exact_key(bt, bd, bw, &k64, &kx, bx);
+    if (near2)
+        exact_key(E::at(trow, b2x), RES ? E::at(drow, b2x) : 0.f,
+                  draw_u32(key, static_cast<uint32_t>(b2x), pos, seq, kTagRace), &k64b, &kxb,
+                  b2x);
+    // The wave's two best candidates: usually one lane is near, so its values
+    // are read lane by lane rather than reduced over the whole wave.
+    Top2 wt;
+    wt.init();
+    auto read_lane = [](double v, int l) {
+        const uint64_t kb = static_cast<uint64_t>(__double_as_longlong(v));
         // readlane returns a signed int: take each half as 32 unsigned bits
         const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(kb >> 32), l);
         const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(kb), l);
-        const double ok = __longlong_as_double(
-            static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
-        const int ox = __builtin_amdgcn_readlane(kx, l);
-        if (ok > wk || (ok == wk && ox < wx)) {
-            wk = ok;
-            wx = ox;
-        }
+        return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+    };
+    for (uint64_t nb = __ballot(near || near2); nb != 0ull; nb &= nb - 1ull) {
+        const int l = __builtin_ctzll(nb);
+        wt.add(read_lane(k64, l), __builtin_amdgcn_readlane(kx, l));
+        wt.add(read_lane(k64b, l), __builtin_amdgcn_readlane(kxb, l));
     }
-    if (lane == 0) {  // sh_key and sh_x are not the arrays read above: no barrier needed
-        sh_key[wv] = wk;
-        sh_x[wv] = wx;
+    if (lane == 0) {  // sh_key, sh_key2 and sh_x are not the arrays read above: no barrier
+        sh_key[wv] = wt.k1;
+        sh_key2[wv] = wt.k2;
+        sh_x[wv] = wt.x1;
     }
     __syncthreads();
     if (tid == 0) {
-        double bk = sh_key[0];
-        int bxx = sh_x[0];
+        Top2 t;
+        t.init();
 #pragma unroll
-        for (int w = 1; w < NW; ++w)
-            if (sh_key[w] > bk || (sh_key[w] == bk && sh_x[w] < bxx)) {
-                bk = sh_key[w];
-                bxx = sh_x[w];
-            }
-        *out_key = bk;
-        *out_x = bxx == INT_MAX ? -1 : bxx;
+        for (int w = 0; w < NW; ++w) t.merge(sh_key[w], sh_x[w], sh_key2[w]);
+        *out_key = t.k1;
+        *out_x = t.x1 == INT_MAX ? -1 : t.x1;
+        *out_key2 = t.k2;
     }
     __syncthreads();
 }
 
 // A draw from p at row L over the ids the row pass listed, which hold every
 // id that could win it: exact double keys, no second read of the row.  The
-// first wave does it; the key and id (-1: none) land in thread 0.
+// first wave does it; the best key and id (-1: none) and the second key land
+// in thread 0.
 __device__ __forceinline__ void race_listed(const RaceArgs &a, int b, int jstar, int n,
-                                            PhiloxKey key, double *out_key, int *out_x) {
+                                            PhiloxKey key, double *out_key, int *out_x,
+                                            double *out_key2) {
     const int tid = threadIdx.x;
     if (tid >= kWave) return;
-    double k64 = -__builtin_inf();
-    int kx = INT_MAX;
+    Top2 t;
+    t.init();
     if (tid < n) {
         const int2 e = a.bonus_list[static_cast<int64_t>(b) * kMaxBonusCand + tid];
         const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(e.x),
                                               static_cast<uint32_t>(jstar),
                                               static_cast<uint32_t>(b), kTagRace));
-        k64 = static_cast<double>(__int_as_float(e.y)) * a.inv_t - log(-log(u));
-        kx = e.x;
+        t.add(static_cast<double>(__int_as_float(e.y)) * a.inv_t - log(-log(u)), e.x);
     }
 #pragma unroll
     for (int msk = kWave / 2; msk > 0; msk >>= 1) {
-        const double ok = __shfl_xor(k64, msk, kWave);
-        const int ox = __shfl_xor(kx, msk, kWave);
-        if (ok > k64 || (ok == k64 && ox < kx)) {
-            k64 = ok;
-            kx = ox;
-        }
+        const double ok1 = __shfl_xor(t.k1, msk, kWave);
+        const double ok2 = __shfl_xor(t.k2, msk, kWave);
+        const int ox = __shfl_xor(t.x1, msk, kWave);
+        t.merge(ok1, ox, ok2);
     }
     if (tid == 0) {
-        *out_key = k64;
-        *out_x = kx == INT_MAX ? -1 : kx;
+        *out_key = t.k1;
+        *out_x = t.x1 == INT_MAX ? -1 : t.x1;
+        *out_key2 = t.k2;
     }
 }
 
@@ -394,7 +466,7 @@ __device__ __forceinline__ void race_listed(const RaceArgs &a, int b, int jstar,
 template <typename T, int NT>
 __device__ __forceinline__ void race_decided(const RaceArgs &a, int b, const RowPick &pk,
                                              bool residual, PhiloxKey key, int v_lo, int v_hi,
-                                             double *k, int *x) {
+                                             double *k, int *x, double *k2) {
     const int jstar = pk.jstar;
     const T *trow = static_cast<const T *>(a.target) +
                     (static_cast<int64_t>(b) * (a.K + 1) + jstar) * a.stride;
@@ -402,10 +474,10 @@ __device__ __forceinline__ void race_decided(const RaceArgs &a, int b, const Row
         const T *drow = static_cast<const T *>(a.draft) +
                         (static_cast<int64_t>(b) * a.K + jstar) * a.stride;
         race_range<T, NT, true>(trow, drow, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
-                                a.inv_t, pk.lt, pk.ld, key, jstar, b, pk.am, k, x);
+                                a.inv_t, pk.lt, pk.ld, key, jstar, b, pk.am, k, x, k2);
     } else {
         race_range<T, NT, false>(trow, nullptr, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
-                                 a.inv_t, pk.lt, 0.0, key, jstar, b, pk.am, k, x);
+                                 a.inv_t, pk.lt, 0.0, key, jstar, b, pk.am, k, x, k2);
     }
 }
 
@@ -422,66 +494,80 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     const int jstar = pk.jstar;
     const bool residual = jstar < L;
     const int n = pk.listed;
-    double k = -__builtin_inf();
+    double k = -__builtin_inf(), k2 = -__builtin_inf();
     int x = -1;
     if (n >= 0) {
-        if (seg == 0) race_listed(a, b, jstar, n, key, &k, &x);
+        if (seg == 0) race_listed(a, b, jstar, n, key, &k, &x, &k2);
     } else {
         const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
         const int v_lo = seg * a.seg_vecs;
-        race_decided<T, NT>(a, b, pk, residual, key, v_lo, min(nvec, v_lo + a.seg_vecs), &k, &x);
+        race_decided<T, NT>(a, b, pk, residual, key, v_lo, min(nvec, v_lo + a.seg_vecs), &k, &x,
+                            &k2);
     }
-    if (threadIdx.x == 0) a.cand[b * a.segs + seg] = RaceCand{k, x, jstar};
+    if (threadIdx.x == 0)
+        a.cand[b * a.segs + seg] =
+            RaceCand{k, k2, x, static_cast<uint32_t>(jstar) | (pk.flags << 8)};
 }
 
 // Best segment per sequence (largest key, then lowest id); writes
-// accepted_len and the emitted tokens.  One wave per sequence: lane s reads
-// segment s's candidate (segs <= 64) and lane j the draft token j (K <= 64),
-// in one round of loads; a shuffle reduction picks the winner.  A residual
-// that vanished in floating point (no candidate anywhere; only possible
-// within rounding of u_j = p/q) falls back to a race over p at the same row.
+// accepted_len, the emitted tokens and the boundary bits.  One wave per
+// sequence: lane s reads segment s's candidate (segs <= 64) and lane j the
+// draft token j (K <= 64), in one round of loads; a shuffle reduction picks
+// the winner and the second largest key.  A residual that vanished in
+// floating point (no candidate anywhere; only possible within rounding of
+// u_j = p/q) falls back to a race over p at the same row.
 template <typename T, int NT>
 __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int32_t *tokens,
                                                          int32_t *accepted_len,
-                                                         int32_t *out_tokens) {
+                                                         int32_t *out_tokens,
+                                                         uint32_t *boundary) {
     static_assert(NT == kWave, "one wave per sequence");
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     const int K = a.K;
-    const RaceCand cnd =
-        lane < a.segs ? a.cand[b * a.segs + lane] : RaceCand{-__builtin_inf(), -1, 0};
+    const RaceCand cnd = lane < a.segs ? a.cand[b * a.segs + lane]
+                                       : RaceCand{-__builtin_inf(), -__builtin_inf(), -1, 0u};
     const int tk = lane < K ? tokens[b * K + lane] : -1;
-    double bk = -__builtin_inf();
-    int bx = INT_MAX;
+    Top2 t;
+    t.init();
     if (cnd.x >= 0) {
-        bk = cnd.key;
-        bx = cnd.x;
+        t.k1 = cnd.key;
+        t.k2 = cnd.key2;
+        t.x1 = cnd.x;
     }
 #pragma unroll
     for (int msk = kWave / 2; msk > 0; msk >>= 1) {
-        const double ok = __shfl_xor(bk, msk, kWave);
-        const int ox = __shfl_xor(bx, msk, kWave);
-        if (ok > bk || (ok == bk && ox < bx)) {
-            bk = ok;
-            bx = ox;
-        }
+        const double ok1 = __shfl_xor(t.k1, msk, kWave);
+        const double ok2 = __shfl_xor(t.k2, msk, kWave);
+        const int ox = __shfl_xor(t.x1, msk, kWave);
+        t.merge(ok1, ox, ok2);
     }
-    const int jstar = __shfl(cnd.jstar, 0);  // the same in every segment
-    int y = bx == INT_MAX ? -1 : bx;         // every lane holds the reduction's result
+    const uint32_t info = __shfl(cnd.info, 0);  // the same in every segment
+    const int jstar = static_cast<int>(info & 0xFFu);
+    uint32_t flags = info >> 8;
+    int y = t.x1 == INT_MAX ? -1 : t.x1;  // every lane holds the reduction's result
+    double k1 = t.k1, k2 = t.k2;
     if (y < 0) {
         const T *trow = static_cast<const T *>(a.target) +
                         (static_cast<int64_t>(b) * (K + 1) + jstar) * a.stride;
         const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
         const double lt = a.t_lse2[b * (K + 1) + jstar];
         const PhiloxKey key = philox_key(a.seed);
-        double k;
+        double k = -__builtin_inf(), kk2 = -__builtin_inf();
         int x = -1;
         const int am = a.t_am[b * (K + 1) + jstar];
         race_range<T, NT, false>(trow, nullptr, 0, nvec, a.V, a.c, static_cast<double>(a.c),
-                                 a.inv_t, lt, 0.0, key, jstar, b, am, &k, &x);
+                                 a.inv_t, lt, 0.0, key, jstar, b, am, &k, &x, &kk2);
         y = __shfl(x, 0);
+        k1 = __shfl(k, 0);
+        k2 = __shfl(kk2, 0);
+        flags |= kResidualEmpty;
     }
-    if (lane == 0) accepted_len[b] = jstar;
+    if (near_race(k1, k2)) flags |= kNearRace;
+    if (lane == 0) {
+        accepted_len[b] = jstar;
+        if (boundary) boundary[b] = flags;
+    }
     for (int j = lane; j <= K; j += NT) {
         // j < jstar <= 64 only on the first pass, where j == lane holds token j
         out_tokens[b * (K + 1) + j] = j < jstar ? tk : (j == jstar ? y : -1);
@@ -497,7 +583,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void fly_kernel(const int32_t *tokens, const int32_t *kept_len,
                                                  const int32_t *am, const float *h, int B, int K,
                                                  float theta, int W, int32_t *accepted_len,
-                                                 int32_t *out_tokens) {
+                                                 int32_t *out_tokens, uint32_t *boundary) {
     // One wave per sequence: lane k holds position k (K <= 64), the
     // deviation and gate tests become two ballots, and the scan runs on
     // wave-uniform bit masks.
@@ -516,11 +602,14 @@ __global__ __launch_bounds__(NT) void fly_kernel(const int32_t *tokens, const in
     const float hv = lane < K ? hb[lane] : 0.f;
     const uint64_t dev = __ballot(live && tk != tp);
     const uint64_t gate = __ballot(live && hv >= theta);  // NaN entropy fails the gate
+    const uint64_t gnear = __ballot(live && fabsf(hv - theta) < 1e-5f);
 
     int j = 0, jstar = L;
-    uint64_t rest = dev;  // deviations at positions >= j
+    uint64_t rest = dev;   // deviations at positions >= j
+    uint64_t seen = 0ull;  // the deviations whose gate the scan evaluated
     while (rest != 0) {
         j = __builtin_ctzll(rest);
+        seen |= 1ull << j;
         if (!((gate >> j) & 1ull) || j + W > L - 1) {
             jstar = j;
             break;
@@ -534,7 +623,10 @@ __global__ __launch_bounds__(NT) void fly_kernel(const int32_t *tokens, const in
         const int nj = j + W + 1;
         rest = nj >= 64 ? 0ull : (dev & (~0ull << nj));
     }
-    if (lane == 0) accepted_len[b] = jstar;
+    if (lane == 0) {
+        accepted_len[b] = jstar;
+        if (boundary) boundary[b] = (seen & gnear) != 0ull ? kNearGate : 0u;
+    }
     // the stopping row may be row K = 64, which no lane holds
     const int32_t topj = jstar < kWave ? __shfl(tp, jstar) : top[jstar];
     int32_t *ot = out_tokens + static_cast<int64_t>(b) * (K + 1);

@@ -348,14 +348,17 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     // Phase A (row L_b): threads whose saved max chunk holds candidates (at
     // least one each), and whether a candidate could lie outside the saved
     // chunks.  Flat rows, with far more than kMaxBonusCand, stop there.
+    // Thresholds are taken relative to the row maximum, (l - M)*c >= tc, so
+    // that they stay small whatever the temperature and the logits' size.
     float tc = 0.f;
     if (list_row) {
-        // the race's key of the top token, in its units (l*c - log2(E/ln2))
+        // the race's key of the top token, in its units (l*c - log2(E/ln2)),
+        // less M*c
         const uint32_t w = draw_u32(philox_key(a.seed), static_cast<uint32_t>(P),
                                     static_cast<uint32_t>(j), static_cast<uint32_t>(b), kTagRace);
-        tc = Mc - hw_log2(-hw_log2(lattice_u32f(w))) - kBonusBelow;
-        const uint64_t holders = __ballot(v0b >= 0 && m * c >= tc);
-        const uint64_t outside = __ballot(m2 * c >= tc);
+        tc = -hw_log2(-hw_log2(lattice_u32f(w))) - kBonusBelow;
+        const uint64_t holders = __ballot(v0b >= 0 && (m - M) * c >= tc);
+        const uint64_t outside = __ballot((m2 - M) * c >= tc);
         if (lane == 0) {
             sh_lb[wv] = __popcll(holders);
             sh_bw[wv] = outside != 0ull ? 1 : 0;
@@ -421,13 +424,13 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
 #pragma unroll
                 for (int k = 0; k < N; ++k) {
                     const int id = (v0 + (k / EPV) * BLOCK) * EPV + (k % EPV);
-                    if (xv[k] * c >= tc && id < V) {
+                    if ((xv[k] - M) * c >= tc && id < V) {
                         const int o = atomicAdd(&sh_cnt, 1);
                         if (o < kMaxBonusCand) dst[o] = make_int2(id, __float_as_int(xv[k]));
                     }
                 }
             };
-            if (v0b >= 0 && m * c >= tc) {
+            if (v0b >= 0 && (m - M) * c >= tc) {
                 uint4 vb[UNROLL];
 #pragma unroll
                 for (int u = 0; u < UNROLL; ++u) vb[u] = sh_saved[u][tid];

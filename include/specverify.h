@@ -79,6 +79,27 @@ typedef struct spec_params {
     int32_t reserved;   /* must be 0                                         */
 } spec_params;
 
+/* Boundary-case bits of spec_verify_out.boundary.  Each marks a near-tie
+ * where the float32 arithmetic of the row pass may legitimately decide the
+ * other way than exact arithmetic would; outside them accepted_len and the
+ * tokens equal those of an exact evaluation of the rule.
+ *   SPEC_NEAR_ACCEPT     an accept test the sequence evaluated (positions
+ *                        0..accepted_len, the rejected one included) had
+ *                        |u_j - p(x_j)/q(x_j)| < 1e-5 ([SD] section
+ *                        "Математика верификации").
+ *   SPEC_NEAR_RACE       the two largest keys w(x)/E_x of the sequence's
+ *                        sampling race were within 1e-6 relative.
+ *   SPEC_RESIDUAL_EMPTY  after a rejection max(0, p - q) rounded to zero at
+ *                        every id; the token was drawn from p at that row.
+ *   SPEC_NEAR_GATE       (FLy) a gate the scan evaluated had
+ *                        |h_j - theta| < 1e-5 ([FLy] part A). */
+enum {
+    SPEC_NEAR_ACCEPT = 1,
+    SPEC_NEAR_RACE = 2,
+    SPEC_RESIDUAL_EMPTY = 4,
+    SPEC_NEAR_GATE = 8
+};
+
 /* Outputs of spec_verify.  accepted_len and tokens are required; every
  * statistics pointer may be NULL.  Rows that a call does not read (target
  * rows past kept_len, draft rows at or past kept_len) are reported as NaN
@@ -99,6 +120,8 @@ typedef struct spec_verify_out {
                                 here as well, in the layout of
                                 spec_draft_stats_bytes, for spec_av_score_stats
                                 and spec_av_update                              */
+    uint32_t *boundary;      /* [B] or NULL: the sequence's boundary-case bits
+                                (SPEC_NEAR_*, SPEC_RESIDUAL_EMPTY), 0 for none */
 } spec_verify_out;
 
 /* Bytes of device workspace spec_verify needs for `params` (0 if invalid). */

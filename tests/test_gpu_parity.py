@@ -121,7 +121,7 @@ def test_read_probe_folds_every_word():
 # ---------------------------------------------------------------------------
 # FLy
 # ---------------------------------------------------------------------------
-def _fly_check(batch, theta=0.3, window=4, kept=None, kept_ref=None):
+def _fly_check(batch, theta=0.3, window=4, kept=None, kept_ref=None, tally="workload"):
     # kept_ref: the oracle's kept lengths, when the library's are meant to be
     # clamped into [0, K] first (the oracle takes only values in range)
     kept_ref = kept if kept_ref is None else kept_ref
@@ -129,12 +129,14 @@ def _fly_check(batch, theta=0.3, window=4, kept=None, kept_ref=None):
     tok = batch.tokens.to(DEV)
     kept_d = None if kept is None else kept.to(DEV)
     r = sv.verify(t, None, tok, seed=0, mode=sv.MODE_FLY, fly_theta=theta, fly_window=window,
-                  vocab=batch.V, kept_len=kept_d, stats=True)
+                  vocab=batch.V, kept_len=kept_d, stats=True, boundary=True)
     torch.cuda.synchronize()
     o = ref.verify(host_logits(batch.target), None, np_(batch.tokens), 0, ref.MODE_FLY,
                    theta=f32(theta), window=window, V=batch.V,
                    kept_len=None if kept_ref is None else np_(kept_ref), nthreads=NT)
-    nm, nb = compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ref.NEAR_GATE, "fly")
+    nm, nb = compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ref.NEAR_GATE, "fly",
+                               dev_boundary=np_(r.boundary),
+                               kept=None if kept_ref is None else np_(kept_ref), tally=tally)
     rel = REL_TOL[batch.target.dtype]
     assert np.array_equal(np_(r.target_argmax), o["t_argmax"])
     assert_close(np_(r.target_lse), o["t_lse"], rel, "target lse", abs_floor=rel)
@@ -215,7 +217,8 @@ def test_fly_headline_full_size():
 # ---------------------------------------------------------------------------
 # Lossless
 # ---------------------------------------------------------------------------
-def _lossless_check(batch, seed, kept=None, draft_stats_path=False, kept_ref=None):
+def _lossless_check(batch, seed, kept=None, draft_stats_path=False, kept_ref=None,
+                    tally="workload"):
     kept_ref = kept if kept_ref is None else kept_ref
     t = batch.target.to(DEV)
     d = batch.draft.to(DEV)
@@ -228,12 +231,14 @@ def _lossless_check(batch, seed, kept=None, draft_stats_path=False, kept_ref=Non
         ob = torch.zeros(K + 1, device=DEV)
         _, _, _, ds = sv.av_score(d, tok, ob, 0.0, temperature=T, vocab=batch.V)
     r = sv.verify(t, d, tok, seed=seed, temperature=T, vocab=batch.V, kept_len=kept_d,
-                  draft_stats=ds, stats=True)
+                  draft_stats=ds, stats=True, boundary=True)
     torch.cuda.synchronize()
     o = ref.verify(host_logits(batch.target), host_logits(batch.draft), np_(batch.tokens), seed,
                    temperature=f32(T), V=batch.V,
                    kept_len=None if kept_ref is None else np_(kept_ref), nthreads=NT)
-    nm, nb = compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ALL_NEAR, "lossless")
+    nm, nb = compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ALL_NEAR, "lossless",
+                               dev_boundary=np_(r.boundary),
+                               kept=None if kept_ref is None else np_(kept_ref), tally=tally)
     rel = REL_TOL[batch.target.dtype]
     assert np.array_equal(np_(r.target_argmax), o["t_argmax"])
     assert_close(np_(r.target_lse), o["t_lse"], rel, "target lse", abs_floor=rel)
@@ -459,7 +464,7 @@ def _av_step(batch, ob_host, tau, lr, seed):
     ob = torch.tensor(ob_host, dtype=torch.float32, device=DEV)
     conf, mask, kept, ds = sv.av_score(d, tok, ob, tau, temperature=T, vocab=batch.V)
     r = sv.verify(t, d, tok, seed=seed, temperature=T, vocab=batch.V, kept_len=kept,
-                  draft_stats=ds)
+                  draft_stats=ds, boundary=True)
     sv.av_update(ds, r.accepted_len, kept, ob, lr, tok.shape[0], K)
     torch.cuda.synchronize()
     dh = host_logits(batch.draft)
@@ -478,13 +483,17 @@ def _av_step(batch, ob_host, tau, lr, seed):
     same = np_(kept) == okept
     compare_decisions(np_(r.accepted_len)[same], np_(r.tokens)[same],
                       {k: (v[same] if hasattr(v, "shape") and v.shape[:1] == (B,) else v)
-                       for k, v in o.items()}, ALL_NEAR, "av verify")
+                       for k, v in o.items()}, ALL_NEAR, "av verify",
+                      dev_boundary=np_(r.boundary)[same], kept=okept[same])
     new = ref.av_update(feat, o["accepted_len"], okept, ob64, f32(lr))
     return np_(ob), new, o, okept
 
 
-def test_av_score_update_parity_c1_recipe():
-    batch = W.make(1, B=24)
+def test_av_score_update_parity_c1_full_size():
+    # the lossless + adaptive-verification workload at its own size: B=64,
+    # K=5, V=128256, omega = 1, beta_i = 0.5 - 0.3 i, no trimming, one SGD step
+    batch = W.make(1, device=DEV)
+    assert batch.tokens.shape == (64, 5)
     ob0 = W.av_init(1)
     got, want, _, okept = _av_step(batch, ob0, tau=0.0, lr=0.05, seed=0)
     assert np.all(okept == 5)
@@ -559,16 +568,26 @@ def test_verify_exports_draft_stats():
     assert torch.equal(c2, conf) and torch.equal(m2, mask) and torch.equal(k2, kept)
 
 
-def test_av_pipeline_full_size_steps():
-    # the B=1024 K=8 adaptive-verification pipeline at full size, three steps
-    # with fresh inputs, parameters carried over as the pipeline does
+def test_av_pipeline_twenty_steps_full_size():
+    # The adaptive-verification pipeline as configured: B=1024, K=8,
+    # V=128256 bf16, tau=0.2, lr=0.05, 20 steps, each with fresh seeded logits
+    # and the parameters the previous step left (carried on the GPU side, as
+    # the pipeline does; the oracle starts each step from the same values).
+    # After every step omega and beta match the oracle's step to 1e-5.
     ob = W.av_init(4)
-    for step in range(3):
+    hist = np.zeros(9, dtype=np.int64)
+    for step in range(20):
         batch = W.make(4, device=DEV, step=step)
+        assert batch.tokens.shape == (1024, 8)
         got, want, o, okept = _av_step(batch, ob, tau=0.2, lr=0.05, seed=step)
-        assert batch.tokens.shape[0] == 1024
         assert np.allclose(got, want, rtol=0, atol=1e-5), (step, got, want)
+        hist += np.bincount(okept, minlength=9)
         ob = got.tolist()
+        del batch
+        torch.cuda.empty_cache()
+    print("kept-length histogram over 20 steps:", hist.tolist(), "omega/beta:",
+          [round(v, 5) for v in ob])
+    assert hist.sum() == 20 * 1024
 
 
 def test_av_pipeline_c4_recipe_steps():
@@ -578,6 +597,150 @@ def test_av_pipeline_c4_recipe_steps():
         got, want, o, okept = _av_step(batch, ob, tau=0.2, lr=0.05, seed=step)
         assert np.allclose(got, want, rtol=0, atol=1e-5), (step, got, want)
         ob = got.tolist()  # carry the GPU's parameters forward, as the pipeline does
+
+
+# ---------------------------------------------------------------------------
+# The library's boundary-case log on inputs built to sit on a boundary
+# ---------------------------------------------------------------------------
+def _check_constructed(t, d, x, seed, T=1.0, kept=None):
+    """Lossless call on host float32 logits; returns the library's result and
+    the oracle's, compared (flags included)."""
+    r = sv.verify(torch.from_numpy(t).to(DEV), torch.from_numpy(d).to(DEV),
+                  torch.from_numpy(x).to(DEV), seed=seed, temperature=T, boundary=True,
+                  kept_len=None if kept is None else torch.from_numpy(kept).to(DEV))
+    torch.cuda.synchronize()
+    o = ref.verify(t, d, x, seed, temperature=f32(T), kept_len=kept, nthreads=NT)
+    compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ALL_NEAR, "constructed",
+                      dev_boundary=np_(r.boundary), kept=kept, tally="constructed")
+    return r, o
+
+
+def test_boundary_residual_empty_on_device():
+    # identical target and draft rows and out-of-range draft tokens: rejected
+    # at once with p - q = 0 at every id, so the token comes from p itself
+    rng = np.random.default_rng(2)
+    B, K, V = 24, 2, 4000
+    t = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    t[:, :, ::4] = -np.inf
+    d = t[:, :K].copy()
+    x = np.full((B, K), V + 3, dtype=np.int32)
+    x[::3, 0] = -1
+    r, o = _check_constructed(t, d, x, seed=4)
+    bnd = np_(r.boundary)
+    assert np.all(bnd & sv.RESIDUAL_EMPTY) and np.all(o["boundary"] & ref.RESIDUAL_EMPTY)
+    y = np_(r.tokens)[:, 0]
+    assert np.all(y % 4 != 0) and np.array_equal(y, o["tokens"][:, 0])
+
+
+def _race_pair_rows(ia, ib, la, lb, V, residual):
+    """One sequence, K = 1.  residual=False: position 0 always accepted
+    (target = draft row), the draw is from p at row 1, whose only finite
+    logits are la at ia and lb at ib.  residual=True: the draft token has
+    p = 0 (rejected surely) and the draft row has no mass at ia, ib, so the
+    residual race at row 0 runs over those two ids with w = p."""
+    t = np.full((1, 2, V), -np.inf, dtype=np.float32)
+    d = np.full((1, 1, V), -np.inf, dtype=np.float32)
+    if residual:
+        t[0, 0, ia], t[0, 0, ib] = la, lb
+        d[0, 0, 7:V:5] = 0.0
+        x = np.array([[7]], dtype=np.int32)
+        t[0, 1, 0] = 0.0
+    else:
+        t[0, 0] = np.linspace(-1, 1, V, dtype=np.float32)
+        d[0, 0] = t[0, 0]
+        t[0, 1, ia], t[0, 1, ib] = la, lb
+        x = np.array([[5]], dtype=np.int32)
+    return t, d, x
+
+
+@pytest.mark.parametrize("path", ["listed", "raced", "residual"])
+@pytest.mark.parametrize("delta", [1e-7, 1e-3])
+def test_boundary_near_race_on_device(path, delta):
+    # Keys p_a/E_a and p_b/E_b designed delta apart (relative) from the
+    # pinned uniforms: a near-tie at 1e-7, clear at 1e-3.  Three race paths:
+    # a draw from p over the row pass's candidate list, the same draw on a row
+    # too flat to list (the race reads it; 2900 ids sit 22 log2 units
+    # below), and a residual race.  V = 4000 float32 ids, the two in
+    # different race segments.
+    V, seed, ia, ib = 4000, 3, 1234, 3210
+    residual = path == "residual"
+    pos = 0 if residual else 1
+    Ea = -np.log(ref.uniform(seed, ia, pos, 0, ref.TAG_RACE))
+    Eb = -np.log(ref.uniform(seed, ib, pos, 0, ref.TAG_RACE))
+    la = np.float32(np.log(Ea / Eb) + np.log1p(delta))
+    t, d, x = _race_pair_rows(ia, ib, la, 0.0, V, residual)
+    if path == "raced":
+        t[0, 1, 100:1200] = np.float32(-22 * np.log(2.0))
+        t[0, 1, 1300:3100] = np.float32(-22 * np.log(2.0))
+    r, o = _check_constructed(t, d, x, seed)
+    assert np_(r.accepted_len)[0] == (0 if residual else 1)
+    want_near = delta < 1e-6
+    assert bool(o["boundary"][0] & ref.NEAR_RACE) == want_near
+    assert bool(np_(r.boundary)[0] & sv.NEAR_RACE) == want_near
+    if not want_near:
+        assert np_(r.tokens)[0, pos] == ia
+
+
+@pytest.mark.parametrize("off", [3e-6, -3e-6, 2e-4])
+def test_boundary_near_accept_on_device(off):
+    # p(x_0)/q(x_0) placed `off` from the accept test's uniform
+    seed, V = 6, 4096
+    u0 = ref.uniform(seed, 0, 0, 0, ref.TAG_ACCEPT)
+    q = np.full(V, 1.0 / V)
+    p = np.full(V, 0.0)
+    p[0] = q[0] * (u0 + off)
+    p[1:] = (1 - p[0]) / (V - 1)
+    tl = np.log(p).astype(np.float32)
+    t = np.stack([tl, tl])[None]
+    d = np.log(q).astype(np.float32)[None, None]
+    r, o = _check_constructed(t, d, np.zeros((1, 1), dtype=np.int32), seed)
+    want = abs(off) < 1e-5
+    assert bool(np_(r.boundary)[0] & sv.NEAR_ACCEPT) == want
+    assert np_(r.accepted_len)[0] == (1 if off > 0 else 0)
+
+
+@pytest.mark.parametrize("off", [5e-6, 1e-3])
+def test_boundary_near_gate_on_device(off):
+    # theta placed `off` below a flat target row's entropy, a deviation there
+    rng = np.random.default_rng(5)
+    K, V = 4, 30000
+    t = (rng.standard_normal((1, K + 1, V)) * 0.5).astype(np.float32)
+    st = ref.rows_stats(t[0])
+    x = st["argmax"][:K].astype(np.int32).copy()[None]
+    x[0, 1] = (st["argmax"][1] + 1) % V
+    theta = float(np.float32(st["h"][1] - off))
+    r = sv.verify(torch.from_numpy(t).to(DEV), None, torch.from_numpy(x).to(DEV), seed=0,
+                  mode=sv.MODE_FLY, fly_theta=theta, fly_window=1, boundary=True)
+    torch.cuda.synchronize()
+    o = ref.verify(t, None, x, 0, ref.MODE_FLY, theta=theta, window=1, nthreads=NT)
+    compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ref.NEAR_GATE, "gate",
+                      dev_boundary=np_(r.boundary), tally="constructed")
+    assert bool(np_(r.boundary)[0] & sv.NEAR_GATE) == (off < 1e-5)
+    assert np_(r.accepted_len)[0] == K
+
+
+def test_low_temperature_race_screening():
+    # T = 1e-4 with logits near 10: l*c ~ 1.4e5, where a float carries 1.6e-2
+    # of rounding; two ids whose race keys lie 1e-3 apart (within that
+    # rounding) must still be ordered as the exact keys order them, on the
+    # listed path and on the full race path (a row too flat to list).
+    seed, V, T = 8, 6000, 1e-4
+    c = 1.0 / np.float32(T)
+    for pos_pair in ((11, 4000), (4000, 11)):
+        ia, ib = pos_pair
+        Ea = -np.log(ref.uniform(seed, ia, 1, 0, ref.TAG_RACE))
+        Eb = -np.log(ref.uniform(seed, ib, 1, 0, ref.TAG_RACE))
+        # (la - lb)/T = ln(Ea/Eb) + 1e-3
+        lb = np.float32(10.0)
+        la = np.float32(lb + (np.log(Ea / Eb) + 1e-3) / c)
+        t, d, x = _race_pair_rows(ia, ib, la, lb, V, residual=False)
+        r, o = _check_constructed(t, d, x, seed, T=T)
+        assert (o["boundary"][0] & ref.NEAR_RACE) or np_(r.tokens)[0, 1] == o["tokens"][0, 1]
+        # many ids within the race's reach (p about 2^-20 of the two): the
+        # row pass cannot list them, so the race reads the row
+        t[0, 1, 100:3000] = lb - np.float32(20 * 0.69314718 / c)
+        r, o = _check_constructed(t, d, x, seed, T=T)
+        assert (o["boundary"][0] & ref.NEAR_RACE) or np_(r.tokens)[0, 1] == o["tokens"][0, 1]
 
 
 # ---------------------------------------------------------------------------
