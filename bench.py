@@ -21,9 +21,13 @@ Besides the headline it reports:
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload;
   secondary     the other verification workloads (lossless with adaptive
                 verification, lossless at T=0.7 on V=152064, the full
-                adaptive-verification step loop, lossless at the headline
+                adaptive-verification pipeline over 20 steps with a freshly
+                generated input set per step, lossless at the headline
                 shape), each timed the same way, and the estimator's Newton
                 refit, diagnostics, budgeted trimming and prompt lookup.
+Every verification line also carries `boundary`: the sequences the library
+logged as near-ties on its last call per input set, against the verified
+rows (kept length + 1 per sequence).
 """
 from __future__ import annotations
 
@@ -135,7 +139,8 @@ def main():
     bytes_per_step = rows * row_bytes
     ws = torch.empty(sv.workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
     outs = [sv.VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
-                            torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+                            torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+                            boundary=torch.empty(B, dtype=torch.int32, device=dev))
             for _ in sets]
 
     def step(i):
@@ -159,6 +164,7 @@ def main():
     rows_per_s = rows / (ms * 1e-3)
     gbps = bytes_per_step / (ms * 1e-3) / 1e9
     acc_mean = float(torch.cat([o.accepted_len for o in outs]).float().mean().item())
+    headline_boundary = _boundary(outs, [rows] * len(outs))
     log("headline: %.1f us/step, %.3g rows/s, %.0f GB/s" % (ms * 1e3, rows_per_s, gbps))
 
     # ------------------------------------------------------------- roofline
@@ -261,6 +267,7 @@ def main():
         "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "evented_step_us_p10_p50_p90": _pcts(step_us),
         "mean_accepted_len": round(acc_mean, 4),
+        "boundary": headline_boundary,
         "roofline": roofline, "read_ceiling": ceiling, "cpu_baseline": cpu,
         "secondary": secondary,
     }
@@ -318,7 +325,8 @@ def run_secondary(sv, W, dev, stream, args, only=None):
         b1 = W.gaussian(256, 8, 128256, "bf16", 1.0, seed=78, token_seed=1, device=dev)
         bs = [b0, b1]
         ws = torch.empty(sv.workspace_bytes(256, 8, 128256), dtype=torch.uint8, device=dev)
-        calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws) for b in bs]
+        calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws, boundary=True)
+                 for b in bs]
         res = [c.out for c in calls]
 
         def f(i):
@@ -326,7 +334,7 @@ def run_secondary(sv, W, dev, stream, args, only=None):
         ms = _timeit(f, n, warm, stream, torch)
         rows = 256 * 17
         byt = rows * 128256 * 2
-        out["lossless_b256_k8_v128256_bf16"] = _line(ms, rows, byt, res)
+        out["lossless_b256_k8_v128256_bf16"] = _line(ms, rows, byt, res, [256 * 9] * 2)
         del bs, b0, b1
 
     # lossless, B=1 K=4 V=32000 float32 (latency: a handful of rows)
@@ -335,14 +343,15 @@ def run_secondary(sv, W, dev, stream, args, only=None):
         sets = [W.make(0, device=dev, step=s) for s in range(4)]
         ws0 = torch.empty(sv.workspace_bytes(1, c["K"], c["V"], dtype=sv.DTYPE_F32),
                           dtype=torch.uint8, device=dev)
-        calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws0) for b in sets]
+        calls = [sv.VerifyCall(b.target, b.draft, b.tokens, workspace=ws0, boundary=True)
+                 for b in sets]
         res = [cl.out for cl in calls]
 
         def f0(i):
             calls[i % 4](i)
         ms = _timeit(f0, n, warm, stream, torch)
         rows = 2 * c["K"] + 1
-        out[c["name"]] = _line(ms, rows, rows * c["V"] * 4, res)
+        out[c["name"]] = _line(ms, rows, rows * c["V"] * 4, res, [c["K"] + 1] * 4)
         del sets
 
     # lossless + AV score + one SGD step, B=64 K=5
@@ -353,14 +362,14 @@ def run_secondary(sv, W, dev, stream, args, only=None):
         ob = torch.tensor(W.av_init(1), dtype=torch.float32, device=dev)
         ws1 = torch.empty(sv.workspace_bytes(64, K, c["V"]), dtype=torch.uint8, device=dev)
         calls = [sv.AvStepCall(b.target, b.draft, b.tokens, ob, c["av"]["tau"], c["av"]["lr"],
-                               workspace=ws1) for b in sets]
+                               workspace=ws1, boundary=True) for b in sets]
         res = [cl.verify.out for cl in calls]
 
         def f1(i):
             calls[i % 4](0)
         ms = _timeit(f1, n, warm, stream, torch)
         rows = 64 * (2 * K + 1)
-        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
+        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res, [64 * (K + 1)] * 4)
         del sets
 
     # lossless at T = 0.7 on V = 152064, B = 512 K = 4
@@ -369,39 +378,48 @@ def run_secondary(sv, W, dev, stream, args, only=None):
         sets = [W.make(3, device=dev, step=s) for s in range(2)]
         ws3 = torch.empty(sv.workspace_bytes(512, 4, c["V"], temperature=0.7),
                           dtype=torch.uint8, device=dev)
-        calls = [sv.VerifyCall(b.target, b.draft, b.tokens, temperature=0.7, workspace=ws3)
-                 for b in sets]
+        calls = [sv.VerifyCall(b.target, b.draft, b.tokens, temperature=0.7, workspace=ws3,
+                               boundary=True) for b in sets]
         res = [cl.out for cl in calls]
 
         def f3(i):
             calls[i % 2](0)
         ms = _timeit(f3, n, warm, stream, torch)
         rows = 512 * 9
-        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res)
+        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res, [512 * 5] * 2)
         del sets
 
-    # full AV pipeline step (score, trimmed verify, update), B=1024 K=8
+    # full AV pipeline (score, trimmed verify, update), B=1024 K=8: 20 steps,
+    # each on its own freshly generated input set (all 20 resident in HBM,
+    # about 89 GB), with the parameters carried from step to step
     c = W.CONFIGS[4]
     if want(c["name"]):
-        sets = [W.make(4, device=dev, step=s) for s in range(2)]
+        nsets = c["steps"]
+        log("generating %d input sets of %s on the GPU" % (nsets, c["name"]))
+        sets = [W.make(4, device=dev, step=s) for s in range(nsets)]
         K = c["K"]
         ob = torch.tensor(W.av_init(4), dtype=torch.float32, device=dev)
         ws4 = torch.empty(sv.workspace_bytes(1024, K, c["V"]), dtype=torch.uint8, device=dev)
         calls = [sv.AvStepCall(b.target, b.draft, b.tokens, ob, c["av"]["tau"], c["av"]["lr"],
-                               workspace=ws4) for b in sets]
+                               workspace=ws4, boundary=True) for b in sets]
         res = [cl.verify.out for cl in calls]
 
         def f4(i):
-            calls[i % 2](i)
-        ms = _timeit(f4, c["steps"] if only is None else n, warm, stream, torch)
-        # kept lengths of the last step on each input set
-        kept_all = torch.stack([cl.kept for cl in calls]).float()
-        rows = 1024 * K + int((kept_all + 1).sum().item() / len(calls))
-        line = _line(ms, rows, rows * c["V"] * 2, res)
-        line["mean_kept_len"] = round(float(kept_all.mean().item()), 4)
+            calls[i % nsets](i % nsets)
+        nsteps = nsets if only is None else n
+        ms = _timeit(f4, nsteps, warm, stream, torch)
+        # the last step on each input set: its kept lengths, verified rows
+        kept_all = torch.stack([cl.kept for cl in calls])
+        verified = [int((k + 1).sum().item()) for k in kept_all]
+        rows = 1024 * K + int(round(sum(verified) / nsets))
+        line = _line(ms, rows, rows * c["V"] * 2, res, verified)
+        line["input_sets"] = nsets
+        line["mean_kept_len"] = round(float(kept_all.float().mean().item()), 4)
+        line["kept_len_hist"] = torch.bincount(kept_all.flatten().long(),
+                                               minlength=K + 1).tolist()
         line["omega_beta_after"] = [round(v, 5) for v in ob.tolist()]
         out[c["name"]] = line
-        del sets
+        del sets, calls, res
     torch.cuda.synchronize()
     if want("next_rows"):
         out["next_rows"] = run_next_rows(sv, W, dev, stream, args)
@@ -472,13 +490,25 @@ def run_next_rows(sv, W, dev, stream, args):
     return out
 
 
-def _line(ms, rows, byt, res):
+def _line(ms, rows, byt, res, verified_rows):
     import torch
     acc = torch.cat([r.accepted_len for r in res if r is not None]).float().mean().item()
     return {"us_per_step": round(ms * 1e3, 2), "rows_per_step": rows,
             "rows_per_s": round(rows / (ms * 1e-3), 1), "gbps": round(byt / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "mean_accepted_len": round(acc, 4)}
+            "mean_accepted_len": round(acc, 4),
+            "boundary": _boundary(res, verified_rows)}
+
+
+def _boundary(res, verified_rows):
+    """The library's boundary-case log over the last call on each input set:
+    sequences flagged, sequences, verified target rows (kept length + 1 per
+    sequence) and the flagged share of those rows."""
+    flagged = sum(int((r.boundary != 0).sum().item()) for r in res)
+    seqs = sum(int(r.boundary.numel()) for r in res)
+    rows = int(sum(verified_rows))
+    return {"flagged": flagged, "sequences": seqs, "verified_rows": rows,
+            "frac_of_rows": flagged / max(rows, 1)}
 
 
 def cpu_baseline(batch, cfg, budget_s):

@@ -250,7 +250,8 @@ class VerifyCall:
                  temperature: float = 1.0, fly_theta: float = 0.3, fly_window: int = 4,
                  kept_len: Optional[torch.Tensor] = None,
                  draft_stats: Optional[torch.Tensor] = None, vocab: Optional[int] = None,
-                 out: Optional[VerifyResult] = None, workspace: Optional[torch.Tensor] = None):
+                 out: Optional[VerifyResult] = None, workspace: Optional[torch.Tensor] = None,
+                 boundary: bool = False):
         _need_cuda(target, "target")
         B, K1, S = target.shape
         K = K1 - 1
@@ -262,6 +263,8 @@ class VerifyCall:
         if out is None:
             out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
                                torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+        if boundary and out.boundary is None:
+            out.boundary = torch.empty(B, dtype=torch.int32, device=dev)
         self.out = out
         self.vout = out.fields()
         need = int(self.L.spec_workspace_bytes(ctypes.byref(self.params)))
@@ -345,7 +348,8 @@ class AvStepCall:
 
     def __init__(self, target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
                  omega_beta: torch.Tensor, tau: float, lr: float, *, temperature: float = 1.0,
-                 vocab: Optional[int] = None, workspace: Optional[torch.Tensor] = None):
+                 vocab: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                 boundary: bool = False):
         _need_cuda(draft, "draft")
         B, K, S = draft.shape
         V = S if vocab is None else int(vocab)
@@ -365,7 +369,8 @@ class AvStepCall:
                                torch.empty(B, K + 1, dtype=torch.int32, device=dev))
             out.draft_stats_out = self.stats
             self.verify = VerifyCall(target, draft, draft_tokens, temperature=temperature,
-                                     vocab=vocab, workspace=workspace, out=out)
+                                     vocab=vocab, workspace=workspace, out=out,
+                                     boundary=boundary)
             self.score_update_args = (_ptr(self.stats), _ptr(out.accepted_len), int(B), int(K),
                                       float(lr), _ptr(omega_beta), _ptr(self.conf),
                                       _ptr(self.mask), _ptr(self.kept), st)
@@ -375,7 +380,7 @@ class AvStepCall:
                                _ptr(self.kept), _ptr(self.stats), st)
             self.verify = VerifyCall(target, draft, draft_tokens, temperature=temperature,
                                      kept_len=self.kept, draft_stats=self.stats, vocab=vocab,
-                                     workspace=workspace)
+                                     workspace=workspace, boundary=boundary)
         self.update_args = (_ptr(self.stats), _ptr(self.verify.out.accepted_len),
                             _ptr(self.kept), int(B), int(K), float(lr), _ptr(omega_beta), st)
         self._keep = (target, draft, draft_tokens, omega_beta)
