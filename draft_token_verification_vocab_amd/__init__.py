@@ -62,6 +62,9 @@ _SIGNATURES = {
     "spec_verify": (ctypes.c_int32, [_P, _P, _P, _P, _P, ctypes.c_uint64, ctypes.c_int32,
                                      ctypes.POINTER(_Params), ctypes.POINTER(_VerifyOut), _P,
                                      ctypes.c_size_t, _P]),
+    "spec_verify_noalloc": (ctypes.c_int32, [_P, _P, _P, _P, _P, ctypes.c_uint64,
+                                             ctypes.c_int32, ctypes.POINTER(_Params),
+                                             ctypes.POINTER(_VerifyOut), _P]),
     "spec_av_score": (ctypes.c_int32, [_P, _P, ctypes.POINTER(_Params), _P, ctypes.c_float,
                                        _P, _P, _P, _P, _P]),
     "spec_av_score_stats": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, _P,

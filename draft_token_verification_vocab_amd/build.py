@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [os.path.join(HERE, "csrc", "specverify.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "specverify.hip"),
+           os.path.join(HERE, "csrc", "specverify_noalloc.hip")]
 ARCH = os.environ.get("SPECVERIFY_ARCH", "gfx950")
 
 

@@ -176,6 +176,28 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * spec_verify_noalloc -- spec_verify without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Arguments, outputs,
+ * results and errors are those of spec_verify; the scratch spec_verify takes
+ * from the caller's workspace lives instead in a fixed device array of
+ * SPEC_NOALLOC_SCRATCH_BYTES (16 MiB) that each GPU the library runs on holds
+ * until the process ends.  A problem whose spec_workspace_bytes exceeds it
+ * returns SPEC_ERR_UNSUPPORTED before anything is enqueued (at K = 8 that is
+ * about 12000 sequences).  No hipMalloc, hipFree or other allocating call is
+ * made.  The array belongs to the current device, which must be the stream's
+ * device; every call on one GPU shares it, so calls that overlap on one GPU
+ * (other streams, other host threads) race and must be serialised by the
+ * caller.  Nothing in it needs clearing between calls.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+spec_status spec_verify_noalloc(const void *target, const void *draft,
+                                const int32_t *draft_tokens, const int32_t *kept_len,
+                                const void *draft_stats, uint64_t seed, int32_t mode,
+                                const spec_params *params, const spec_verify_out *out,
+                                void *stream);
+
+/*
  * spec_av_score -- adaptive-verification confidence and trimming ([AV]
  * sections "Solucion" and "Puntuar la Distribucion"; survival as the running
  * product over positions from section "Otras Caracteristicas Consideradas").
