@@ -67,6 +67,8 @@ _SIGNATURES = {
                                              ctypes.POINTER(_VerifyOut), _P]),
     "spec_av_score": (ctypes.c_int32, [_P, _P, ctypes.POINTER(_Params), _P, ctypes.c_float,
                                        _P, _P, _P, _P, _P]),
+    "spec_av_score_prefix": (ctypes.c_int32, [_P, _P, ctypes.POINTER(_Params), _P,
+                                              ctypes.c_float, _P, _P, _P, _P, _P]),
     "spec_av_score_stats": (ctypes.c_int32, [_P, ctypes.c_int32, ctypes.c_int32, _P,
                                              ctypes.c_float, _P, _P, _P, _P]),
     "spec_av_update": (ctypes.c_int32, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32,
@@ -286,9 +288,11 @@ class VerifyCall:
 
 def av_score(draft: torch.Tensor, draft_tokens: torch.Tensor, omega_beta: torch.Tensor,
              tau: float, *, temperature: float = 1.0, vocab: Optional[int] = None,
-             draft_stats: Optional[torch.Tensor] = None):
+             draft_stats: Optional[torch.Tensor] = None, prefix: bool = False):
     """Adaptive-verification confidences.  Returns (conf [B,K] float,
-    keep_mask [B,K] uint8, kept_len [B] int32, draft_stats buffer)."""
+    keep_mask [B,K] uint8, kept_len [B] int32, draft_stats buffer).
+    prefix: spec_av_score_prefix, which reads each sequence's rows only up to
+    its first trimmed position (conf and statistics past it are NaN)."""
     _need_cuda(draft, "draft")
     B, K, S = draft.shape
     V = S if vocab is None else int(vocab)
@@ -309,9 +313,10 @@ def av_score(draft: torch.Tensor, draft_tokens: torch.Tensor, omega_beta: torch.
         draft_stats = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     elif draft_stats.numel() * draft_stats.element_size() < need:
         raise ValueError("draft_stats must hold spec_draft_stats_bytes(B, K) = %d bytes" % need)
-    _check(L.spec_av_score(_ptr(draft), _ptr(draft_tokens), ctypes.byref(p), _ptr(omega_beta),
-                           float(tau), _ptr(conf), _ptr(mask), _ptr(kept), _ptr(draft_stats),
-                           _stream(dev)), "spec_av_score")
+    fn = L.spec_av_score_prefix if prefix else L.spec_av_score
+    _check(fn(_ptr(draft), _ptr(draft_tokens), ctypes.byref(p), _ptr(omega_beta), float(tau),
+              _ptr(conf), _ptr(mask), _ptr(kept), _ptr(draft_stats), _stream(dev)),
+           "spec_av_score_prefix" if prefix else "spec_av_score")
     return conf, mask, kept, draft_stats
 
 
@@ -343,16 +348,19 @@ class AvStepCall:
     omega_beta is updated in place.
 
     With tau > 0: spec_av_score (draft rows), spec_verify on the kept drafts,
-    spec_av_update.  With tau <= 0 nothing can be trimmed, so spec_verify
-    reads target and draft rows in one pass and exports the draft statistics,
-    and spec_av_score_update scores from them and takes the SGD step in one
-    launch: the same results with one row pass instead of two, and four
-    launches instead of five."""
+    spec_av_update.  prefix=True scores with spec_av_score_prefix instead,
+    which stops reading each sequence's draft rows after its first trimmed
+    position: the step's results are the same (only kept drafts are verified
+    and labelled), conf past the trim point is NaN.  With tau <= 0 nothing can
+    be trimmed, so spec_verify reads target and draft rows in one pass and
+    exports the draft statistics, and spec_av_score_update scores from them
+    and takes the SGD step in one launch: the same results with one row pass
+    instead of two, and four launches instead of five."""
 
     def __init__(self, target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
                  omega_beta: torch.Tensor, tau: float, lr: float, *, temperature: float = 1.0,
                  vocab: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                 boundary: bool = False):
+                 boundary: bool = False, prefix: bool = False):
         _need_cuda(draft, "draft")
         B, K, S = draft.shape
         V = S if vocab is None else int(vocab)
@@ -378,6 +386,7 @@ class AvStepCall:
                                       float(lr), _ptr(omega_beta), _ptr(self.conf),
                                       _ptr(self.mask), _ptr(self.kept), st)
         else:
+            self.score_fn = L.spec_av_score_prefix if prefix else L.spec_av_score
             self.score_args = (_ptr(draft), _ptr(draft_tokens), ctypes.byref(self.params),
                                _ptr(omega_beta), float(tau), _ptr(self.conf), _ptr(self.mask),
                                _ptr(self.kept), _ptr(self.stats), st)
@@ -393,7 +402,7 @@ class AvStepCall:
             r = self.verify(seed)
             _check(self.L.spec_av_score_update(*self.score_update_args), "spec_av_score_update")
             return r
-        _check(self.L.spec_av_score(*self.score_args), "spec_av_score")
+        _check(self.score_fn(*self.score_args), "spec_av_score")
         r = self.verify(seed)
         _check(self.L.spec_av_update(*self.update_args), "spec_av_update")
         return r

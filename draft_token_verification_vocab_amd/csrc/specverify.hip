@@ -361,6 +361,43 @@ spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,
     return launch_status();
 }
 
+spec_status spec_av_score_prefix(const void *draft, const int32_t *draft_tokens,
+                                 const spec_params *params, const float *omega_beta, float tau,
+                                 float *conf, uint8_t *keep_mask, int32_t *kept_len,
+                                 void *draft_stats, void *stream) {
+    spec_status s = check_params(params);
+    if (s != SPEC_OK) return s;
+    const spec_params &p = *params;
+    if (std::isnan(tau)) return SPEC_ERR_ARG;
+    if (p.batch == 0) return SPEC_OK;
+    if (!draft || !aligned16(draft) || !draft_tokens || !omega_beta || !draft_stats ||
+        !aligned16(draft_stats))
+        return SPEC_ERR_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int32_t B = p.batch, K = p.num_draft;
+    const size_t n = static_cast<size_t>(B) * K;
+    DraftStats ds = draft_stats_view(draft_stats, n);
+    PrefixArgs pa{};
+    pa.draft = draft;
+    pa.stride = p.row_stride;
+    pa.V = p.vocab;
+    pa.K = K;
+    pa.tokens = draft_tokens;
+    pa.c = log2e_over(p.temperature);
+    pa.inv_ln_v = 1.0 / std::log(static_cast<double>(p.vocab));
+    pa.lse2 = ds.lse2;
+    pa.logq2 = ds.logq2;
+    pa.qmax = ds.qmax;
+    pa.feat = ds.feat;
+    if (p.dtype == SPEC_DTYPE_BF16)
+        av_prefix_kernel<uint16_t, kRowBlock, RowUnroll<uint16_t>::value>
+            <<<dim3(B), dim3(kRowBlock), 0, st>>>(pa, omega_beta, tau, conf, keep_mask, kept_len);
+    else
+        av_prefix_kernel<float, kRowBlock, RowUnroll<float>::value>
+            <<<dim3(B), dim3(kRowBlock), 0, st>>>(pa, omega_beta, tau, conf, keep_mask, kept_len);
+    return launch_status();
+}
+
 spec_status spec_av_score_stats(const void *draft_stats, int32_t batch, int32_t num_draft,
                                 const float *omega_beta, float tau, float *conf,
                                 uint8_t *keep_mask, int32_t *kept_len, void *stream) {

@@ -157,14 +157,15 @@ __device__ __forceinline__ void row_emit(const RowArgs &a, const RowGroup &g, in
 // (one median-of-three per chunk): when no thread's m2 reaches the threshold,
 // every candidate is in a saved max chunk; otherwise the list is marked
 // incomplete and the race reads the row.
+// tid: threadIdx.x (a caller that loops over rows passes it through an
+// opaque copy, so that values derived from it are not kept live across rows).
 template <typename T, int BLOCK, int UNROLL, bool ENT, bool CAND>
 __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int64_t row,
-                                        uint4 (&sh_saved)[UNROLL][BLOCK]) {
+                                        uint4 (&sh_saved)[UNROLL][BLOCK], const int tid) {
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
     constexpr int N = UNROLL * EPV;
     constexpr int NW = BLOCK / kWave;
-    const int tid = threadIdx.x;
     const int V = a.V;
     const float c = a.c;
 
@@ -459,9 +460,9 @@ __global__ __launch_bounds__(BLOCK) void row_stats_kernel(RowArgs a) {
     __shared__ uint4 sh_saved[UNROLL][BLOCK];
     const int blk = blockIdx.x;
     if (blk < a.nrows0)
-        row_one<T, BLOCK, UNROLL, ENT0, CAND>(a, a.g[0], blk, sh_saved);
+        row_one<T, BLOCK, UNROLL, ENT0, CAND>(a, a.g[0], blk, sh_saved, threadIdx.x);
     else
-        row_one<T, BLOCK, UNROLL, false, false>(a, a.g[1], blk - a.nrows0, sh_saved);
+        row_one<T, BLOCK, UNROLL, false, false>(a, a.g[1], blk - a.nrows0, sh_saved, threadIdx.x);
 }
 
 // Load-only twin of the row pass: the same grid (a workgroup per row), the

@@ -218,6 +218,24 @@ spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,
                           void *stream);
 
 /*
+ * spec_av_score_prefix -- spec_av_score for a step that uses the kept drafts
+ * only (verification, labels, refits): each sequence's draft rows are read in
+ * order and reading stops after the first trimmed position, whose row
+ * decides the trim ([AV] footnote 1: a trimmed position is not verified, the
+ * target samples there).  kept_len, keep_mask, and conf and draft_stats for
+ * positions 0..min(kept_len, K-1) equal spec_av_score's bit for bit;
+ * positions after the first trimmed one are not read: conf and their draft
+ * statistics are NaN, keep_mask 0.  With tau <= 0 nothing is trimmed and
+ * every row is read.  One workgroup per sequence, so it pays off when B is
+ * large (hundreds of sequences or more) and most sequences trim early.
+ * Arguments and errors as spec_av_score.
+ */
+spec_status spec_av_score_prefix(const void *draft, const int32_t *draft_tokens,
+                                 const spec_params *params, const float *omega_beta, float tau,
+                                 float *conf, uint8_t *keep_mask, int32_t *kept_len,
+                                 void *draft_stats, void *stream);
+
+/*
  * spec_av_score_stats -- the scoring and trimming of spec_av_score from
  * draft statistics that are already computed (by spec_av_score, or by
  * spec_verify through draft_stats_out), without reading any draft row:

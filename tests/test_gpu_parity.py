@@ -550,6 +550,51 @@ def test_av_score_update_matches_score_then_update(B, K):
         assert (k_a == K).all() and (m_a == 1).all()
 
 
+@pytest.mark.parametrize("dtype,tau,K", [("bf16", 0.2, 8), ("f32", 0.35, 5), ("bf16", 0.0, 3),
+                                         ("bf16", 0.02, 64), ("f32", 0.9, 4)])
+def test_av_score_prefix_matches_full_scoring(dtype, tau, K):
+    # spec_av_score_prefix stops reading a sequence's draft rows after its
+    # first trimmed position: kept lengths and masks equal spec_av_score's,
+    # and so do the confidences and draft statistics of every position up to
+    # that first trimmed one, bit for bit; the positions after it are NaN
+    B = 48 if K < 64 else 6
+    batch = W.gaussian(B, K, 7001, dtype, 1.0, seed=K, token_seed=1, stride=7008)
+    d, tok = batch.draft.to(DEV), batch.tokens.to(DEV)
+    ob = torch.tensor(W.av_init(4, K=K), dtype=torch.float32, device=DEV)
+    c0, m0, k0, s0 = sv.av_score(d, tok, ob, tau, vocab=batch.V)
+    c1, m1, k1, s1 = sv.av_score(d, tok, ob, tau, vocab=batch.V, prefix=True)
+    torch.cuda.synchronize()
+    assert torch.equal(k0, k1) and torch.equal(m0, m1)
+    kept = np_(k0)
+    if tau > 0:
+        assert (kept < K).any()  # some sequences trim
+    read = np.arange(K)[None, :] <= np.minimum(kept, K - 1)[:, None]  # rows the prefix read
+    v0 = sv.draft_stats_view(s0, B, K)
+    v1 = sv.draft_stats_view(s1, B, K)
+    pairs = [(c0, c1)] + [(v0[n], v1[n]) for n in ("lse2", "logq2", "qmax", "feat")]
+    for a, b in pairs:
+        a, b = np_(a).reshape(B, K), np_(b).reshape(B, K)
+        assert np.array_equal(a[read].view(np.uint8), b[read].view(np.uint8))
+        assert np.isnan(b[~read]).all()
+
+
+def test_av_step_call_prefix_matches_separate_calls():
+    # the step with prefix scoring: same kept lengths, tokens and coefficients
+    # as the step with full scoring, over three steps
+    batch = W.make(4, B=96, V=6001, stride=6008)
+    t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
+    ob_a = torch.tensor(W.av_init(4), dtype=torch.float32, device=DEV)
+    ob_b = ob_a.clone()
+    ca = sv.AvStepCall(t, d, tok, ob_a, 0.2, 0.05, vocab=batch.V, prefix=True)
+    cb = sv.AvStepCall(t, d, tok, ob_b, 0.2, 0.05, vocab=batch.V)
+    for step in range(3):
+        ra = ca(step)
+        rb = cb(step)
+        torch.cuda.synchronize()
+        assert torch.equal(ra.accepted_len, rb.accepted_len) and torch.equal(ra.tokens, rb.tokens)
+        assert torch.equal(ca.kept, cb.kept) and torch.equal(ob_a, ob_b)
+
+
 def test_verify_exports_draft_stats():
     # the draft statistics a lossless call computes itself, exported, equal
     # those of spec_av_score bit for bit; scoring from them equals spec_av_score
