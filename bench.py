@@ -400,19 +400,25 @@ def run_secondary(sv, W, dev, stream, args, only=None):
         K = c["K"]
         ob = torch.tensor(W.av_init(4), dtype=torch.float32, device=dev)
         ws4 = torch.empty(sv.workspace_bytes(1024, K, c["V"]), dtype=torch.uint8, device=dev)
+        # scoring reads each sequence's draft rows up to its first trimmed
+        # position (the rows after it are neither verified nor labelled)
         calls = [sv.AvStepCall(b.target, b.draft, b.tokens, ob, c["av"]["tau"], c["av"]["lr"],
-                               workspace=ws4, boundary=True) for b in sets]
+                               workspace=ws4, boundary=True, prefix=True) for b in sets]
         res = [cl.verify.out for cl in calls]
 
         def f4(i):
             calls[i % nsets](i % nsets)
         nsteps = nsets if only is None else n
         ms = _timeit(f4, nsteps, warm, stream, torch)
-        # the last step on each input set: its kept lengths, verified rows
+        # the last step on each input set: its kept lengths; rows read are the
+        # draft rows up to each trim point and the target rows 0..kept
         kept_all = torch.stack([cl.kept for cl in calls])
         verified = [int((k + 1).sum().item()) for k in kept_all]
-        rows = 1024 * K + int(round(sum(verified) / nsets))
+        drafts_read = [int(torch.clamp(k + 1, max=K).sum().item()) for k in kept_all]
+        rows = int(round((sum(verified) + sum(drafts_read)) / nsets))
         line = _line(ms, rows, rows * c["V"] * 2, res, verified)
+        line["draft_rows_read_per_step"] = round(sum(drafts_read) / nsets, 1)
+        line["draft_rows_per_step"] = 1024 * K
         line["input_sets"] = nsets
         line["mean_kept_len"] = round(float(kept_all.float().mean().item()), 4)
         line["kept_len_hist"] = torch.bincount(kept_all.flatten().long(),

@@ -455,14 +455,16 @@ def test_lossless_deterministic_across_streams():
 # ---------------------------------------------------------------------------
 # Adaptive verification
 # ---------------------------------------------------------------------------
-def _av_step(batch, ob_host, tau, lr, seed):
+def _av_step(batch, ob_host, tau, lr, seed, prefix=False):
     """One GPU step (score, verify, update) and the oracle's step on the same
-    inputs and the same starting parameters."""
+    inputs and the same starting parameters.  prefix: score with
+    spec_av_score_prefix (confidences past each trim point are not read)."""
     K = batch.tokens.shape[1]
     T = batch.temperature
     t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
     ob = torch.tensor(ob_host, dtype=torch.float32, device=DEV)
-    conf, mask, kept, ds = sv.av_score(d, tok, ob, tau, temperature=T, vocab=batch.V)
+    conf, mask, kept, ds = sv.av_score(d, tok, ob, tau, temperature=T, vocab=batch.V,
+                                       prefix=prefix)
     r = sv.verify(t, d, tok, seed=seed, temperature=T, vocab=batch.V, kept_len=kept,
                   draft_stats=ds, boundary=True)
     sv.av_update(ds, r.accepted_len, kept, ob, lr, tok.shape[0], K)
@@ -477,6 +479,10 @@ def _av_step(batch, ob_host, tau, lr, seed):
                    V=batch.V, kept_len=okept, nthreads=NT)
     o["boundary"] |= onear
     rel = REL_TOL[batch.target.dtype]
+    if prefix:  # positions up to each first trimmed one were read; the rest are NaN
+        read = np.arange(K)[None, :] <= np.minimum(np_(kept), K - 1)[:, None]
+        assert np.isnan(np_(conf)[~read]).all()
+        oconf = np.where(read, oconf, np.nan)
     assert_close(np_(conf), oconf, rel, "confidence")
     kept_ok = (np_(kept) == okept) | ((onear & ref.NEAR_TRIM) != 0)
     assert kept_ok.all(), "kept_len differs outside the trim boundary set"
@@ -618,13 +624,16 @@ def test_av_pipeline_twenty_steps_full_size():
     # V=128256 bf16, tau=0.2, lr=0.05, 20 steps, each with fresh seeded logits
     # and the parameters the previous step left (carried on the GPU side, as
     # the pipeline does; the oracle starts each step from the same values).
-    # After every step omega and beta match the oracle's step to 1e-5.
+    # After every step omega and beta match the oracle's step to 1e-5.  The
+    # steps score as the benchmark does, reading draft rows up to each trim
+    # point only (even steps) and every draft row (odd steps).
     ob = W.av_init(4)
     hist = np.zeros(9, dtype=np.int64)
     for step in range(20):
         batch = W.make(4, device=DEV, step=step)
         assert batch.tokens.shape == (1024, 8)
-        got, want, o, okept = _av_step(batch, ob, tau=0.2, lr=0.05, seed=step)
+        got, want, o, okept = _av_step(batch, ob, tau=0.2, lr=0.05, seed=step,
+                                       prefix=step % 2 == 0)
         assert np.allclose(got, want, rtol=0, atol=1e-5), (step, got, want)
         hist += np.bincount(okept, minlength=9)
         ob = got.tolist()
