@@ -100,6 +100,8 @@ spec_status check_logits_shape(int32_t V, int64_t stride, int32_t dtype, float t
     if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return SPEC_ERR_ARG;
     if (V < 2 || stride < V) return SPEC_ERR_ARG;
     if ((stride * elem_size(dtype)) % 16 != 0) return SPEC_ERR_ARG;
+    // rows are addressed with 32-bit byte offsets
+    if (static_cast<int64_t>(V) * elem_size(dtype) > INT32_MAX) return SPEC_ERR_UNSUPPORTED;
     if (!(temperature >= 1e-4f && temperature <= 1e4f)) return SPEC_ERR_ARG;
     return SPEC_OK;
 }
@@ -651,7 +653,7 @@ spec_status spec_read_probe(const void *logits, int64_t rows, int64_t row_bytes,
     if (rows < 0 || row_bytes < 0 || row_bytes % 16 != 0 || row_stride_bytes % 16 != 0 ||
         row_bytes > row_stride_bytes)
         return SPEC_ERR_ARG;
-    if (rows > INT32_MAX) return SPEC_ERR_UNSUPPORTED;
+    if (rows > INT32_MAX || row_bytes > INT32_MAX) return SPEC_ERR_UNSUPPORTED;
     if (rows == 0) return SPEC_OK;
     if (!logits || !aligned16(logits) || !sink) return SPEC_ERR_ARG;
     read_probe_kernel<kRowBlock, RowUnroll<uint16_t>::value>

@@ -38,6 +38,35 @@ __device__ __forceinline__ uint4 load_stream_at(const void *base, uint32_t byte_
     return load_stream(reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + byte_off));
 }
 
+// Buffer-addressed streaming loads: a resource descriptor over `bytes` bytes
+// at `base` (raw buffer, no stride; the third descriptor word is the gfx9
+// family's data-format field), then 16-byte non-temporal loads at a per-lane
+// byte offset `voff` plus a wave-uniform byte offset `soff`.  A loop that
+// advances only `soff` keeps its addressing in scalar registers: no 64-bit
+// vector address arithmetic per load.  Every load must lie inside the
+// described range.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes),
+                                             0x00020000);
+}
+constexpr int kCachePolicyNT = 2;  // the non-temporal bit of a buffer load's cache policy
+__device__ __forceinline__ uint4 load_stream_buf(buf_rsrc r, uint32_t voff, uint32_t soff) {
+    const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff),
+                                                          static_cast<int>(soff), kCachePolicyNT);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Maximum of three floats in one v_max3_f32.  Written as an instruction so
+// that a chain of them stays a chain: the compiler neither inserts operand
+// canonicalisations (logits enter as reinterpreted integer bits) nor reshapes
+// the chain into a tree of two-input maxima.  Operands are not NaN.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Raw hardware transcendentals (v_exp_f32 / v_log_f32: base 2, ~1 ulp).
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }

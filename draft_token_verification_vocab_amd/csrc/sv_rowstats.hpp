@@ -45,7 +45,6 @@ template <>
 struct RowUnroll<float> {
     static constexpr int value = 4;
 };
-
 // One group of rows processed by the same launch (target rows and draft rows
 // share a launch).  Row j of sequence b is row b*rows_per_seq + j.
 struct RowGroup {
@@ -205,9 +204,11 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
         float x[N];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) E::unpack(buf[u], x + u * EPV);
-        float cm = x[0];
+        // the chunk maximum in a chain of three-input maxima
+        float cm = max3f(x[0], x[1], x[2]);
 #pragma unroll
-        for (int k = 1; k < N; ++k) cm = fmaxf(cm, x[k]);
+        for (int k = 3; k + 1 < N; k += 2) cm = max3f(cm, x[k], x[k + 1]);
+        if (N % 2 == 0) cm = max3f(cm, x[N - 1], x[N - 1]);
         const bool up = cm > m;
         const float mcn = up ? cm * c : mc;
         // Terms of this chunk against the (possibly new) maximum.
@@ -270,24 +271,72 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     constexpr int kChunkVecs = UNROLL * BLOCK;
     const int nit = nfull / kChunkVecs;
     // The next chunk's loads are issued before this chunk's arithmetic, so
-    // every wave keeps a chunk in flight while it computes; two register
-    // buffers take turns (no copies).
+    // every wave keeps chunks in flight while it computes; register buffers
+    // take turns (no copies).
+    // Loads are buffer-addressed over the row's full vectors: the chunk's
+    // byte offset is wave-uniform (a scalar register), each lane's offset
+    // inside the chunk is fixed.
+    const buf_rsrc rs = make_rsrc(rp, static_cast<uint32_t>(nfull) * 16u);
     auto load_chunk = [&](uint4 (&buf)[UNROLL], int it) {
-        const uint4 *cp = vrow + static_cast<int64_t>(it) * kChunkVecs;
+        const uint32_t soff = static_cast<uint32_t>(it) * (kChunkVecs * 16u);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            buf[u] = load_stream_at(cp, static_cast<uint32_t>(tid + u * BLOCK) * 16u);
+            buf[u] = load_stream_buf(rs, static_cast<uint32_t>(tid + u * BLOCK) * 16u, soff);
     };
-    uint4 bufA[UNROLL], bufB[UNROLL];
-    if (nit > 0) load_chunk(bufA, 0);
-    int it = 0;
-    for (; it + 1 < nit; it += 2) {
-        load_chunk(bufB, it + 1);
-        consume(bufA, it);
-        if (it + 2 < nit) load_chunk(bufA, it + 2);
-        consume(bufB, it + 1);
+    // The loops below issue their loads unconditionally: a load under a
+    // branch makes the compiler's wait before the following chunk's
+    // arithmetic cover that load too, which drains the prefetch.  The last
+    // chunks are peeled off the loops instead.
+    if constexpr (ENT && !CAND) {
+        // Two chunks in flight: three register buffers take turns.  The
+        // entropy variant's registers hold the workgroups per compute unit at
+        // three; the third buffer fits under the same count and puts half as
+        // many bytes again in flight.
+        uint4 b0[UNROLL], b1[UNROLL], b2[UNROLL];
+        if (nit >= 2) {
+            load_chunk(b0, 0);
+            load_chunk(b1, 1);
+            int it = 0;
+            for (; it + 5 <= nit; it += 3) {  // loads it+2 .. it+4, all < nit
+                load_chunk(b2, it + 2);
+                consume(b0, it);
+                load_chunk(b0, it + 3);
+                consume(b1, it + 1);
+                load_chunk(b1, it + 4);
+                consume(b2, it + 2);
+            }
+            // 2, 3 or 4 chunks left; b0 and b1 hold the first two
+            const int rem = nit - it;
+            if (rem >= 3) load_chunk(b2, it + 2);
+            consume(b0, it);
+            if (rem >= 4) load_chunk(b0, it + 3);
+            consume(b1, it + 1);
+            if (rem >= 3) consume(b2, it + 2);
+            if (rem >= 4) consume(b0, it + 3);
+        } else if (nit == 1) {
+            load_chunk(b0, 0);
+            consume(b0, 0);
+        }
+    } else {
+        // One chunk in flight: two register buffers take turns.
+        uint4 bufA[UNROLL], bufB[UNROLL];
+        if (nit >= 1) load_chunk(bufA, 0);
+        int it = 0;
+        for (; it + 3 <= nit; it += 2) {  // loads it+1 and it+2, both < nit
+            load_chunk(bufB, it + 1);
+            consume(bufA, it);
+            load_chunk(bufA, it + 2);
+            consume(bufB, it + 1);
+        }
+        // 0, 1 or 2 chunks left; bufA holds the first
+        if (it + 1 < nit) {
+            load_chunk(bufB, it + 1);
+            consume(bufA, it);
+            consume(bufB, it + 1);
+        } else if (it < nit) {
+            consume(bufA, it);
+        }
     }
-    if (it < nit) consume(bufA, it);
     const int v = nit * kChunkVecs + tid;
     if (v < nvec) {  // the last, partly filled chunk of this thread
         uint4 buf[UNROLL];
@@ -466,23 +515,34 @@ __global__ __launch_bounds__(BLOCK) void row_stats_kernel(RowArgs a) {
 }
 
 // Load-only twin of the row pass: the same grid (a workgroup per row), the
-// same workgroup shape and the same non-temporal 16-byte loads, with the data
-// folded by XOR so that nothing is optimised away.
+// same workgroup shape and the same buffer-addressed non-temporal 16-byte
+// loads in whole chunks, with the data folded by XOR so that nothing is
+// optimised away.
 template <int BLOCK, int UNROLL>
 __global__ __launch_bounds__(BLOCK) void read_probe_kernel(const void *base, int64_t row_vecs,
                                                           int64_t stride_vecs, uint32_t *sink) {
     const uint4 *row = static_cast<const uint4 *>(base) + blockIdx.x * stride_vecs;
     const int tid = threadIdx.x;
+    const buf_rsrc rs = make_rsrc(row, static_cast<uint32_t>(row_vecs) * 16u);
+    constexpr int kChunkVecs = UNROLL * BLOCK;
+    const int nit = static_cast<int>(row_vecs / kChunkVecs);
     uint32_t acc = 0;
-    for (int64_t v = tid; v < row_vecs; v += static_cast<int64_t>(UNROLL) * BLOCK) {
+    for (int it = 0; it < nit; ++it) {
+        const uint32_t soff = static_cast<uint32_t>(it) * (kChunkVecs * 16u);
         uint4 b[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int64_t j = v + static_cast<int64_t>(u) * BLOCK;
-            b[u] = j < row_vecs ? load_stream(row + j) : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int u = 0; u < UNROLL; ++u)
+            b[u] = load_stream_buf(rs, static_cast<uint32_t>(tid + u * BLOCK) * 16u, soff);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) acc ^= b[u].x ^ b[u].y ^ b[u].z ^ b[u].w;
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {  // the rest, one vector per lane and u
+        const int64_t j = static_cast<int64_t>(nit) * kChunkVecs + tid + u * BLOCK;
+        if (j < row_vecs) {
+            const uint4 b = load_stream_buf(rs, static_cast<uint32_t>(j) * 16u, 0u);
+            acc ^= b.x ^ b.y ^ b.z ^ b.w;
+        }
     }
     // XOR over the workgroup: lanes through shuffles, waves through LDS
 #pragma unroll

@@ -70,7 +70,8 @@ enum { SPEC_MODE_LOSSLESS = 0, SPEC_MODE_FLY = 1 };
 typedef struct spec_params {
     int32_t batch;      /* B >= 0                                            */
     int32_t num_draft;  /* K, 1 <= K <= 64                                   */
-    int32_t vocab;      /* V >= 2                                            */
+    int32_t vocab;      /* V >= 2; a row of V elements must be < 2 GiB      */
+                        /* (SPEC_ERR_UNSUPPORTED otherwise)                  */
     int32_t dtype;      /* SPEC_DTYPE_F32 or SPEC_DTYPE_BF16                 */
     int64_t row_stride; /* elements between consecutive rows, >= V           */
     float temperature;  /* T, 1e-4 <= T <= 1e4                               */
@@ -395,7 +396,8 @@ spec_status spec_row_stats(const void *logits, int64_t rows, int32_t vocab, int6
  * as the row pass, but with almost no arithmetic, and stores the XOR of each
  * row's 32-bit words in sink[row].  Its bandwidth is the ceiling the row pass
  * can reach on the same rows.  logits: device, 16-byte aligned; row_bytes and
- * row_stride_bytes: multiples of 16, row_bytes <= row_stride_bytes;
+ * row_stride_bytes: multiples of 16, row_bytes <= row_stride_bytes
+ * (row_bytes beyond 2^31 - 1: SPEC_ERR_UNSUPPORTED);
  * sink: device uint32 [rows].  Asynchronous on `stream`.
  */
 spec_status spec_read_probe(const void *logits, int64_t rows, int64_t row_bytes,

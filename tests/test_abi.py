@@ -77,7 +77,10 @@ def test_workspace_query(L):
     (dict(num_draft=0), -1), (dict(num_draft=65), -2), (dict(vocab=1), -1),
     (dict(row_stride=1000), -1), (dict(row_stride=1028), -1), (dict(dtype=7), -1),
     (dict(temperature=0.0), -1), (dict(temperature=float("nan")), -1), (dict(batch=-1), -1),
-    (dict(reserved=1), -1)])
+    (dict(reserved=1), -1),
+    # rows are addressed with 32-bit byte offsets: a row must stay below 2 GiB
+    (dict(vocab=1 << 29, row_stride=1 << 29, dtype=0), -2),
+    (dict(vocab=1 << 30, row_stride=1 << 30, dtype=1), -2)])
 def test_verify_rejects_bad_params_on_host(L, kw, status):
     p = _params(**kw)
     out = sv._VerifyOut()
@@ -160,6 +163,8 @@ def test_other_entry_points_validate(L):
     assert L.spec_read_probe(ctypes.c_void_p(16), 4, 48, 32, ctypes.c_void_p(16), None) == -1
     assert L.spec_read_probe(ctypes.c_void_p(16), 4, 32, 32, None, None) == -1
     assert L.spec_read_probe(None, 0, 32, 32, None, None) == 0
+    assert L.spec_read_probe(ctypes.c_void_p(16), 4, 1 << 31, 1 << 31, ctypes.c_void_p(16),
+                             None) == -2
     for s in (0, -1, -2, -3, -4, 99):
         assert isinstance(L.spec_status_string(s), bytes)
 
