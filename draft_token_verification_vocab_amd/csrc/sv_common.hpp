@@ -67,6 +67,16 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
+// x * y rounded to float.  Device code is compiled with floating-point
+// contraction on, which may fuse a product into a following add or subtract
+// even when the product has other uses; where the rounded product itself is
+// the operand (a log2-normaliser m*c whose rounding residue is tracked
+// apart), it must stay a separate multiply.
+__device__ __forceinline__ float mul_rn(float x, float y) {
+#pragma clang fp contract(off)
+    return x * y;
+}
+
 // Raw hardware transcendentals (v_exp_f32 / v_log_f32: base 2, ~1 ulp).
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -219,6 +229,41 @@ __device__ __forceinline__ void wave_keyed_add(unsigned long long *sh, int key, 
         if (lane == leader) atomicAdd(&sh[q], static_cast<unsigned long long>(sum));
         todo &= ~grp;
     }
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_pull_f(float v) {
+    return __uint_as_float(dpp_pull<CTRL, ROWS>(__float_as_uint(v)));
+}
+
+// Sum of a float over the wave (each lane's value counts once).
+__device__ __forceinline__ float wave_sum_f32(float x) {
+    x += dpp_pull_f<0x111, 0xF>(x);  // row_shr:1
+    x += dpp_pull_f<0x112, 0xF>(x);  // row_shr:2
+    x += dpp_pull_f<0x114, 0xF>(x);  // row_shr:4
+    x += dpp_pull_f<0x118, 0xF>(x);  // row_shr:8
+    x += dpp_pull_f<0x142, 0xA>(x);  // row_bcast15
+    x += dpp_pull_f<0x143, 0xC>(x);  // row_bcast31
+    return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 63));
+}
+
+// Sums of two floats over the wave, step by step together, so that the two
+// dependency chains interleave.
+__device__ __forceinline__ void wave_sum2_f32(float &x, float &y) {
+    x += dpp_pull_f<0x111, 0xF>(x);
+    y += dpp_pull_f<0x111, 0xF>(y);
+    x += dpp_pull_f<0x112, 0xF>(x);
+    y += dpp_pull_f<0x112, 0xF>(y);
+    x += dpp_pull_f<0x114, 0xF>(x);
+    y += dpp_pull_f<0x114, 0xF>(y);
+    x += dpp_pull_f<0x118, 0xF>(x);
+    y += dpp_pull_f<0x118, 0xF>(y);
+    x += dpp_pull_f<0x142, 0xA>(x);
+    y += dpp_pull_f<0x142, 0xA>(y);
+    x += dpp_pull_f<0x143, 0xC>(x);
+    y += dpp_pull_f<0x143, 0xC>(y);
+    x = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 63));
+    y = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(y), 63));
 }
 
 // Maximum of a non-negative double over the wave (such doubles order like

@@ -115,11 +115,16 @@ __device__ __forceinline__ void row_emit(const RowArgs &a, const RowGroup &g, in
                                          int P, double r, double to, bool gather, int gidx,
                                          float ltok) {
     const float c = a.c;
-    const float Mc = M * c;
+    const float Mc = mul_rn(M, c);
     // The argmax term is 2^r0 with r0 = M*c - Mc, the rounding residue of Mc
     // (exact in float); the row's sum of terms is 2^r0 + r.
     const double r0 = static_cast<double>(fmaf(M, c, -Mc));
-    const double e0 = exp2(r0);
+    // 2^r0: the residue is tiny unless M*c is very large, and then a short
+    // series is exact to double rounding (the next term is below 1e-26)
+    const double xr = r0 * kLn2;
+    const double e0 = fabs(r0) < 0x1p-16
+                          ? 1.0 + xr * (1.0 + xr * (0.5 + xr * (1.0 / 6.0 + xr * (1.0 / 24.0))))
+                          : exp2(r0);
     const double rho = r / e0;      // (1 - q_max) / q_max
     const double l1p = log1p(rho);  // ln(sum / 2^r0)
     const double lse2 = static_cast<double>(Mc) + r0 + l1p * kLog2eD;
@@ -186,14 +191,13 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
 
     const int nfull = V / EPV;
     const int nvec = (V + EPV - 1) / EPV;
-    const uint4 *vrow = reinterpret_cast<const uint4 *>(rp);
 
     // Thread state.  s, t: sums outside the chunk that holds the maximum;
     // cs, ct: that chunk's sums; itb: its index.  Its raw data is kept in
     // LDS (sh_saved), out of the registers.
     // A thread adds a few tens of chunk sums of one sign, so float carries
     // them to ~1e-6; the sums over threads are formed in double.
-    float m = kNoMax, mc = kNoMax * c, cs = 0.f, ct = 0.f;
+    float m = kNoMax, mc = mul_rn(kNoMax, c), cs = 0.f, ct = 0.f;
     float s = 0.f, t = 0.f;
     int itb = -1;
     float m2 = kNoMax;  // CAND: the largest maximum of the other chunks
@@ -210,7 +214,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
         for (int k = 3; k + 1 < N; k += 2) cm = max3f(cm, x[k], x[k + 1]);
         if (N % 2 == 0) cm = max3f(cm, x[N - 1], x[N - 1]);
         const bool up = cm > m;
-        const float mcn = up ? cm * c : mc;
+        const float mcn = up ? mul_rn(cm, c) : mc;
         // Terms of this chunk against the (possibly new) maximum.
         float s4[4], t4[4];
 #pragma unroll
@@ -271,8 +275,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     constexpr int kChunkVecs = UNROLL * BLOCK;
     const int nit = nfull / kChunkVecs;
     // The next chunk's loads are issued before this chunk's arithmetic, so
-    // every wave keeps chunks in flight while it computes; register buffers
-    // take turns (no copies).
+    // every wave keeps a chunk in flight while it computes.
     // Loads are buffer-addressed over the row's full vectors: the chunk's
     // byte offset is wave-uniform (a scalar register), each lane's offset
     // inside the chunk is fixed.
@@ -283,44 +286,41 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
         for (int u = 0; u < UNROLL; ++u)
             buf[u] = load_stream_buf(rs, static_cast<uint32_t>(tid + u * BLOCK) * 16u, soff);
     };
-    // The loops below issue their loads unconditionally: a load under a
-    // branch makes the compiler's wait before the following chunk's
-    // arithmetic cover that load too, which drains the prefetch.  The last
-    // chunks are peeled off the loops instead.
-    if constexpr (ENT && !CAND) {
-        // Two chunks in flight: three register buffers take turns.  The
-        // entropy variant's registers hold the workgroups per compute unit at
-        // three; the third buffer fits under the same count and puts half as
-        // many bytes again in flight.
-        uint4 b0[UNROLL], b1[UNROLL], b2[UNROLL];
-        if (nit >= 2) {
-            load_chunk(b0, 0);
-            load_chunk(b1, 1);
-            int it = 0;
-            for (; it + 5 <= nit; it += 3) {  // loads it+2 .. it+4, all < nit
-                load_chunk(b2, it + 2);
-                consume(b0, it);
-                load_chunk(b0, it + 3);
-                consume(b1, it + 1);
-                load_chunk(b1, it + 4);
-                consume(b2, it + 2);
-            }
-            // 2, 3 or 4 chunks left; b0 and b1 hold the first two
-            const int rem = nit - it;
-            if (rem >= 3) load_chunk(b2, it + 2);
-            consume(b0, it);
-            if (rem >= 4) load_chunk(b0, it + 3);
-            consume(b1, it + 1);
-            if (rem >= 3) consume(b2, it + 2);
-            if (rem >= 4) consume(b0, it + 3);
-        } else if (nit == 1) {
-            load_chunk(b0, 0);
-            consume(b0, 0);
+    // Each thread's last chunk (index nit) is partly filled: its vector
+    // v + u*BLOCK is a full vector (below nfull), the row's ragged last
+    // vector (nfull, when V is not a multiple of the vector) or past the end
+    // (padding).  Its full vectors are loaded together with the chunk before
+    // it, so that no wave waits a whole memory latency at the end of the row:
+    // every lane loads, with its offset clamped into the row's full vectors,
+    // and lanes past them then take the ragged vector or padding.
+    const int v = nit * kChunkVecs + tid;
+    const uint32_t ni = E::pad_word();
+    auto load_last = [&](uint4 (&buf)[UNROLL]) {  // needs nfull >= 1
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int vi = v + u * BLOCK;
+            const int vc = vi < nfull ? vi : nfull - 1;
+            buf[u] = load_stream_buf(rs, static_cast<uint32_t>(vc) * 16u, 0u);
         }
-    } else {
-        // One chunk in flight: two register buffers take turns.
-        uint4 bufA[UNROLL], bufB[UNROLL];
-        if (nit >= 1) load_chunk(bufA, 0);
+    };
+    auto consume_last = [&](uint4 (&buf)[UNROLL]) {
+        if (v < nvec) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int vi = v + u * BLOCK;
+                if (vi >= nfull)
+                    buf[u] = vi < nvec ? E::partial(rp, vi, V) : make_uint4(ni, ni, ni, ni);
+            }
+            consume(buf, nit);
+        }
+    };
+    // One chunk in flight: two register buffers take turns.  The loop issues
+    // its loads unconditionally: a load under a branch makes the compiler's
+    // wait before the following chunk's arithmetic cover that load too, which
+    // drains the prefetch.  The last full chunks are peeled off the loop.
+    uint4 bufA[UNROLL], bufB[UNROLL];
+    if (nit >= 1) {
+        load_chunk(bufA, 0);
         int it = 0;
         for (; it + 3 <= nit; it += 2) {  // loads it+1 and it+2, both < nit
             load_chunk(bufB, it + 1);
@@ -328,31 +328,26 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
             load_chunk(bufA, it + 2);
             consume(bufB, it + 1);
         }
-        // 0, 1 or 2 chunks left; bufA holds the first
-        if (it + 1 < nit) {
+        if (it + 1 < nit) {  // two full chunks left, the first in bufA
             load_chunk(bufB, it + 1);
             consume(bufA, it);
+            load_last(bufA);
             consume(bufB, it + 1);
-        } else if (it < nit) {
+        } else {  // one full chunk left, in bufA
+            load_last(bufB);
             consume(bufA, it);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) bufA[u] = bufB[u];
         }
-    }
-    const int v = nit * kChunkVecs + tid;
-    if (v < nvec) {  // the last, partly filled chunk of this thread
-        uint4 buf[UNROLL];
-        const uint32_t ni = E::pad_word();
+    } else {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int vi = v + u * BLOCK;
-            if (vi < nfull)
-                buf[u] = vrow[vi];
-            else if (vi < nvec)
-                buf[u] = E::partial(rp, vi, V);
-            else
-                buf[u] = make_uint4(ni, ni, ni, ni);
+            bufA[u] = vi < nfull ? load_stream_buf(rs, static_cast<uint32_t>(vi) * 16u, 0u)
+                                 : make_uint4(ni, ni, ni, ni);
         }
-        consume(buf, nit);
     }
+    consume_last(bufA);
 
     // (1) Row maximum M (a 32-bit max of the ordered bits), then its first
     // id: only threads whose maximum is M search their max chunk (element
@@ -391,7 +386,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
 #pragma unroll
     for (int w = 1; w < NW; ++w) bp = sh_p[w] > bp ? sh_p[w] : bp;
     const int P = static_cast<int>(~bp);
-    const float Mc = M * c;
+    const float Mc = mul_rn(M, c);
 
     // Bonus candidates of row L_b (WG-uniform branch).
     const bool list_row = CAND && j == Lb && P != INT_MAX;
@@ -418,34 +413,55 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     // argmax swaps its max chunk for that chunk's other terms, so the block
     // sums are r = sum_{x != argmax} 2^(l_x c - Mc) and the matching entropy
     // numerator t_o.
-    double X, Y = 0.0;
-    if (pos == P && P != INT_MAX) {
-        float os = 0.f, ot = 0.f;
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            const int id = (v0b + (k / EPV) * BLOCK) * EPV + (k % EPV);
-            if (id != P) {
-                float d = fmaf(xs[k], c, -Mc);
-                if (ENT) d = fmaxf(d, kMinExp2);
-                const float e = hw_exp2(d);
-                os += e;
-                if (ENT) ot = fmaf(e, d, ot);
-            }
+    // Every term has one sign (terms >= 0, exponents <= 0 relative to M),
+    // so float sums over a thread and over a wave lose at most a few ulps;
+    // the sums over waves are double.
+    const float dl = mc - Mc;
+    const float al = hw_exp2(dl);
+    const float st = s + cs;
+    float X = al * st, Y = 0.f;
+    if (ENT) Y = al * (t + ct + dl * st);
+    // The wave holding the argmax replaces its holder's value: s plus the
+    // max chunk's terms other than P.  Lane k < N of that wave takes element
+    // k of the holder's saved chunk from LDS, and a DPP sum over lanes 0..15
+    // adds them, instead of one lane adding sixteen terms in turn.
+    const uint64_t hold = __ballot(pos == P && P != INT_MAX);
+    if (hold != 0ull) {
+        const int hl = __ffsll(static_cast<long long>(hold)) - 1;
+        const int v0h = __builtin_amdgcn_readlane(v0b, hl);
+        float e = 0.f, ed = 0.f;
+        if (lane < N) {
+            const int u = lane / EPV, q = lane % EPV;
+            const T *saved = reinterpret_cast<const T *>(&sh_saved[0][0]);
+            const float x = E::at(saved, (u * BLOCK + wv * kWave + hl) * EPV + q);
+            float d = fmaf(x, c, -Mc);
+            if (ENT) d = fmaxf(d, kMinExp2);
+            e = (v0h + u * BLOCK) * EPV + q != P ? hw_exp2(d) : 0.f;
+            if (ENT) ed = e * d;
         }
-        X = static_cast<double>(s) + static_cast<double>(os);
-        if (ENT) Y = static_cast<double>(t) + static_cast<double>(ot);
-    } else {
-        const float dl = mc - Mc;
-        const double al = static_cast<double>(hw_exp2(dl));
-        const double st = s + static_cast<double>(cs);
-        X = al * st;
-        if (ENT) Y = al * (t + static_cast<double>(ct) + static_cast<double>(dl) * st);
+        static_assert(N == 16, "the argmax chunk's terms are summed over one DPP row");
+        e += dpp_pull_f<0x111, 0xF>(e);  // row_shr:1 .. 8: lane 15 ends with lanes 0..15
+        ed += dpp_pull_f<0x111, 0xF>(ed);
+        e += dpp_pull_f<0x112, 0xF>(e);
+        ed += dpp_pull_f<0x112, 0xF>(ed);
+        e += dpp_pull_f<0x114, 0xF>(e);
+        ed += dpp_pull_f<0x114, 0xF>(ed);
+        e += dpp_pull_f<0x118, 0xF>(e);
+        ed += dpp_pull_f<0x118, 0xF>(ed);
+        const float os = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(e), 15));
+        const float ot = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ed), 15));
+        if (lane == hl) {
+            X = s + os;
+            if (ENT) Y = t + ot;
+        }
     }
-    const double wx = wave_sum_f64(X);
-    const double wy = ENT ? wave_sum_f64(Y) : 0.0;
+    if (ENT)
+        wave_sum2_f32(X, Y);
+    else
+        X = wave_sum_f32(X);
     if (lane == 0) {
-        sh_s[wv] = wx;
-        sh_t[wv] = wy;
+        sh_s[wv] = static_cast<double>(X);
+        sh_t[wv] = static_cast<double>(Y);
     }
     __syncthreads();
 
