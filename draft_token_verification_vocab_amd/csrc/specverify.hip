@@ -239,7 +239,7 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     gt.lse = out->target_lse;
     gt.entropy = out->target_entropy;
     gt.argmax = out->target_argmax;
-    gt.lse2 = t_lse2;
+    gt.lse2 = lossless ? t_lse2 : nullptr;  // the FLy resolver reads only h and the top token
     gt.logtok2 = t_logp2;
     gt.h_int = t_h;
     gt.am_int = t_am;

@@ -119,13 +119,19 @@ __device__ __forceinline__ void row_emit(const RowArgs &a, const RowGroup &g, in
     // The argmax term is 2^r0 with r0 = M*c - Mc, the rounding residue of Mc
     // (exact in float); the row's sum of terms is 2^r0 + r.
     const double r0 = static_cast<double>(fmaf(M, c, -Mc));
-    // 2^r0: the residue is tiny unless M*c is very large, and then a short
-    // series is exact to double rounding (the next term is below 1e-26)
+    // 2^r0 and 2^-r0: the residue is tiny unless M*c is very large, and then
+    // short series are exact to double rounding (the next term is below
+    // 1e-26)
     const double xr = r0 * kLn2;
-    const double e0 = fabs(r0) < 0x1p-16
-                          ? 1.0 + xr * (1.0 + xr * (0.5 + xr * (1.0 / 6.0 + xr * (1.0 / 24.0))))
-                          : exp2(r0);
-    const double rho = r / e0;      // (1 - q_max) / q_max
+    double e0, ie0;
+    if (fabs(r0) < 0x1p-16) {
+        e0 = 1.0 + xr * (1.0 + xr * (0.5 + xr * (1.0 / 6.0 + xr * (1.0 / 24.0))));
+        ie0 = 1.0 - xr * (1.0 - xr * (0.5 - xr * (1.0 / 6.0 - xr * (1.0 / 24.0))));
+    } else {
+        e0 = exp2(r0);
+        ie0 = 1.0 / e0;
+    }
+    const double rho = r * ie0;     // (1 - q_max) / q_max
     const double l1p = log1p(rho);  // ln(sum / 2^r0)
     const double lse2 = static_cast<double>(Mc) + r0 + l1p * kLog2eD;
     if (g.lse2) g.lse2[row] = lse2;
@@ -133,16 +139,20 @@ __device__ __forceinline__ void row_emit(const RowArgs &a, const RowGroup &g, in
     const int am = P == INT_MAX ? -1 : P;
     if (g.argmax) g.argmax[row] = am;
     if (g.am_int) g.am_int[row] = am;
+    // q_max = 1 / (1 + rho), the one division
+    const bool want_q = g.qmax || g.qmax_int;
+    const double inv1p = ENT || want_q ? 1.0 / (1.0 + rho) : 0.0;
     if (ENT) {
         // H = ln(sum) - ln2 * (sum of term*exponent) / sum, rewritten around
-        // the argmax term: H = ln(1 + rho) + ln2 (r0 r - t_o) / (2^r0 + r).
-        const double H = l1p + kLn2 * (r0 * r - to) / (e0 + r);
+        // the argmax term: H = ln(1 + rho) + ln2 (r0 r - t_o) / (2^r0 + r)
+        //                    = ln(1 + rho) + ln2 (r0 rho - t_o 2^-r0) q_max.
+        const double H = l1p + kLn2 * (r0 * rho - to * ie0) * inv1p;
         const float h = static_cast<float>(H * a.inv_ln_v);
         if (g.entropy) g.entropy[row] = h;
         if (g.h_int) g.h_int[row] = h;
     }
-    if (g.qmax || g.qmax_int) {
-        const float qm = static_cast<float>(1.0 / (1.0 + rho));
+    if (want_q) {
+        const float qm = static_cast<float>(inv1p);
         if (g.qmax) g.qmax[row] = qm;
         if (g.qmax_int) g.qmax_int[row] = qm;
     }
