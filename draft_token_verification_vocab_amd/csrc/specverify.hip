@@ -42,13 +42,12 @@ constexpr int kNgramUnroll = 8;
 size_t align_up(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 int elem_size(int32_t dtype) { return dtype == SPEC_DTYPE_F32 ? 4 : 2; }
-int elems_per_vec(int32_t dtype) { return 16 / elem_size(dtype); }
 
-int race_segments(int32_t B, int32_t V, int32_t dtype) {
+int race_segments(int32_t B, int32_t V) {
     if (B <= 0) return 1;
-    const int nvec = (V + elems_per_vec(dtype) - 1) / elems_per_vec(dtype);
+    const int ngroups = (V + kRaceGroup - 1) / kRaceGroup;
     int segs = (kRaceTargetBlocks + B - 1) / B;
-    const int max_by_len = nvec / kRaceBlock;  // keep at least one vector per thread
+    const int max_by_len = ngroups / kRaceBlock;  // keep at least one group per thread
     if (segs > max_by_len) segs = max_by_len;
     if (segs > kMaxSegs) segs = kMaxSegs;
     return segs < 1 ? 1 : segs;
@@ -58,7 +57,7 @@ struct WsLayout {
     size_t t_lse2, t_logp2, t_h, t_am, dstats, cand, bonus_cnt, bonus_list, total;
 };
 
-WsLayout layout_for(int32_t B, int32_t K, int32_t V, int32_t dtype) {
+WsLayout layout_for(int32_t B, int32_t K, int32_t V) {
     const size_t rows_t = static_cast<size_t>(B) * (K + 1);
     const size_t n = static_cast<size_t>(B) * K;
     WsLayout w;
@@ -74,7 +73,7 @@ WsLayout layout_for(int32_t B, int32_t K, int32_t V, int32_t dtype) {
     w.dstats = off;
     off = align_up(off + 24 * n);
     w.cand = off;
-    off = align_up(off + sizeof(RaceCand) * static_cast<size_t>(B) * race_segments(B, V, dtype));
+    off = align_up(off + sizeof(RaceCand) * static_cast<size_t>(B) * race_segments(B, V));
     w.bonus_cnt = off;
     off = align_up(off + 4 * static_cast<size_t>(B));
     w.bonus_list = off;
@@ -182,7 +181,7 @@ const char *spec_status_string(int32_t status) {
 
 size_t spec_workspace_bytes(const spec_params *p) {
     if (check_params(p) != SPEC_OK) return 0;
-    return layout_for(p->batch, p->num_draft, p->vocab, p->dtype).total;
+    return layout_for(p->batch, p->num_draft, p->vocab).total;
 }
 
 size_t spec_draft_stats_bytes(int32_t batch, int32_t num_draft) {
@@ -212,7 +211,7 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     if (lossless && (!draft || !aligned16(draft))) return SPEC_ERR_ARG;
     if (draft_stats && !aligned16(draft_stats)) return SPEC_ERR_ARG;
     const int32_t B = p.batch, K = p.num_draft, V = p.vocab;
-    const WsLayout ws = layout_for(B, K, V, p.dtype);
+    const WsLayout ws = layout_for(B, K, V);
     if (!workspace || workspace_bytes < ws.total) return SPEC_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SPEC_ERR_ARG;
 
@@ -302,9 +301,9 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     rg.c = c;
     rg.inv_t = 1.0 / static_cast<double>(p.temperature);
     rg.seed = seed;
-    rg.segs = race_segments(B, V, p.dtype);
-    const int nvec = (V + elems_per_vec(p.dtype) - 1) / elems_per_vec(p.dtype);
-    rg.seg_vecs = (nvec + rg.segs - 1) / rg.segs;
+    rg.segs = race_segments(B, V);
+    const int ngroups = (V + kRaceGroup - 1) / kRaceGroup;
+    rg.seg_groups = (ngroups + rg.segs - 1) / rg.segs;
     rg.cand = reinterpret_cast<RaceCand *>(w + ws.cand);
     rg.bonus_cnt = bonus_cnt;
     rg.bonus_list = bonus_list;

@@ -105,7 +105,7 @@ struct RaceArgs {
     double inv_t;             // 1/T in double
     uint64_t seed;
     int32_t segs;             // segments per row
-    int32_t seg_vecs;         // 16-byte vectors per segment
+    int32_t seg_groups;       // groups of eight ids per segment
     RaceCand *cand;           // [B][segs]
     // The row pass's candidate list of row L_b (the only row a draw from p
     // can use): count (-1 when incomplete) and (id, logit bits) entries.
@@ -202,8 +202,7 @@ __device__ __forceinline__ float race_floor(bool residual, int am, float xt, flo
         lw = fmaf(xt, c, -static_cast<float>(lse2_t));  // log2 p
     }
     if (!(lw > -__builtin_inff())) return -__builtin_inff();
-    const float e2 = -hw_log2(lattice_u32f(draw_u32(key, static_cast<uint32_t>(am), pos, seq,
-                                                    kTagRace)));
+    const float e2 = -hw_log2(lattice_u32f(race_word(key, static_cast<uint32_t>(am), pos, seq)));
     return lw - hw_log2(e2) - kScreenMargin;
 }
 
@@ -214,43 +213,57 @@ __device__ __forceinline__ float bound_base(float thr, float lsub) {
     return __double2float_rd(static_cast<double>(thr) - 0.5 + static_cast<double>(lsub));
 }
 
-// Race over vectors [v_lo, v_hi) of one row (pair) with NT threads, one
-// vector per thread per trip.  RES: w = max(0, p - q) from the target and
-// draft rows; otherwise w = p of the target row.  am: the target's top token,
-// whose key (less the margin) is a floor the row's best is known to reach;
-// its logits are loaded together with the first vectors.  Returns (in thread
-// 0) the best double key and id (id -1 when no id of the range can win) and
-// the second largest double key (see RaceCand).
+// Ids are raced in groups of eight (one bfloat16 vector, two float vectors),
+// the ids one screening block serves.
+constexpr int kRaceGroup = 8;
+template <typename T>
+constexpr int group_vecs() {
+    return kRaceGroup / Elem<T>::kPerVec;
+}
+
+// Race over groups [g_lo, g_hi) of one row (pair) with NT threads, one group
+// per thread per trip.  RES: w = max(0, p - q) from the target and draft
+// rows; otherwise w = p of the target row.  am: the target's top token, whose
+// key (less the margin) is a floor the row's best is known to reach; its
+// logits are loaded together with the first groups.  Returns (in thread 0)
+// the best double key and id (id -1 when no id of the range can win) and the
+// second largest double key (see RaceCand).
 template <typename T, int NT, bool RES>
-__device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int V, float c,
+__device__ void race_range(const T *trow, const T *drow, int g_lo, int g_hi, int V, float c,
                            double cd, double inv_t, double lse2_t, double lse2_d, PhiloxKey key,
                            uint32_t pos, uint32_t seq, int am, double *out_key, int *out_x,
                            double *out_key2) {
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
+    constexpr int G = group_vecs<T>();
     constexpr int NW = NT / kWave;
     const int tid = threadIdx.x;
     const int nfull = V / EPV;
+    const int nvec = (V + EPV - 1) / EPV;
     const uint4 *tv = reinterpret_cast<const uint4 *>(trow);
     const uint4 *dv = reinterpret_cast<const uint4 *>(drow);
     const float lt2 = static_cast<float>(lse2_t);
     const float ld2 = static_cast<float>(lse2_d);
-    // Whole trips cover full vectors only (every thread has one); one last
-    // trip takes the rest, the row's partial vector included.  The whole
-    // trips' loads are unconditional, so that the wait before a trip's
-    // arithmetic covers its own vectors and not the next trip's.
-    const int v_hf = min(v_hi, nfull);
-    const int nit = v_hf > v_lo ? (v_hf - v_lo) / NT : 0;
-    struct Vec {
-        uint4 t, d;
+    // Whole trips cover groups of full vectors only (every thread has one);
+    // one last trip takes the rest, the row's partial vector included.  The
+    // whole trips' loads are unconditional, so that the wait before a trip's
+    // arithmetic covers its own group and not the next trip's.
+    const int g_hf = min(g_hi, nfull / G);
+    const int nit = g_hf > g_lo ? (g_hf - g_lo) / NT : 0;
+    struct Grp {
+        uint4 t[G], d[G];
     };
-    auto load_trip = [&](Vec &q, int it) {
-        const int vi = v_lo + it * NT + tid;
-        q.t = load_stream(tv + vi);
-        if (RES) q.d = load_stream(dv + vi);
+    auto load_trip = [&](Grp &q, int it) {
+        const int gi = g_lo + it * NT + tid;
+#pragma unroll
+        for (int v = 0; v < G; ++v) {
+            q.t[v] = load_stream(tv + gi * G + v);
+            if (RES) q.d[v] = load_stream(dv + gi * G + v);
+        }
     };
-    Vec qa, qb;
-    qa.t = qa.d = qb.t = qb.d = make_uint4(0u, 0u, 0u, 0u);
+    Grp qa, qb;
+#pragma unroll
+    for (int v = 0; v < G; ++v) qa.t[v] = qa.d[v] = qb.t[v] = qb.d[v] = make_uint4(0u, 0u, 0u, 0u);
     // the top token's logits first, so that the floor waits for them alone
     const bool am_ok = am >= 0 && am < V;
     const float am_xt = am_ok ? E::at(trow, am) : -__builtin_inff();
@@ -265,48 +278,70 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
     float best = floor, best2 = -__builtin_inff();
     int bx = INT_MAX, b2x = INT_MAX;
     float bt = 0.f, bd = 0.f;  // the best id's target and draft logits
-    uint32_t bw = 0u;          // and its Philox word
+    uint32_t bw = 0u;          // and its race word
     float thr = floor - kScreenMargin;
     // lb = l*c - lsub bounds the log2 weight: log2 p, and w = max(0, p - q)
     // <= p for a residual row.  The tests use a = thr - 0.5 - lb, one FMA per
-    // id: the key is below lb + 0.5 + (leading ones), so an id is a candidate
-    // only if its leading ones reach a; a block of four needs its draw only if
-    // some a <= 23 (lb + 23.5 >= thr).
+    // id: the key is below lb + 0.5 + (leading ones of the race word), so an
+    // id is a candidate only if its leading ones reach a.
     const float lsub = lt2;
     float abase = bound_base(thr, lsub);
-    // One trip over vector vi (live: vi is in the range).  Wave-uniform: the
+    // One trip over group gi (live: gi is in the range).  Wave-uniform: the
     // skip tests are ballots.
-    auto trip = [&](const Vec &q, int vi, bool live) {
+    //  - A group none of whose ids has a <= 23 (lb + 23.5 < thr) draws
+    //    nothing.
+    //  - Otherwise its screening block gives each id's 16 high word bits and
+    //    so its leading ones when below 16: an id with fewer than a is out.
+    //  - A block of four ids draws its race stream only if one of them is
+    //    still in (at least a leading ones, or at least 16 of them); then the
+    //    exact count decides.
+    auto trip = [&](const Grp &q, int gi, bool live) {
         bool evaluated = false;
-        float xt[EPV], av[EPV];
-        E::unpack(q.t, xt);
+        float xt[kRaceGroup], av[kRaceGroup];
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) av[k] = fmaf(xt[k], -c, abase);
+        for (int v = 0; v < G; ++v) E::unpack(q.t[v], xt + v * EPV);
 #pragma unroll
-        for (int blk = 0; blk < EPV / 4; ++blk) {
-            const uint32_t base = static_cast<uint32_t>(live ? vi : v_lo) * EPV + blk * 4;
-            const float amin = fminf(fminf(av[blk * 4], av[blk * 4 + 1]),
-                                     fminf(av[blk * 4 + 2], av[blk * 4 + 3]));
-            const bool need = live && amin <= kMaxNegLogE - 0.5f;
-            if (__ballot(need) == 0ull) continue;  // no lane's block can win: no draws
-            const uint4 rw = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
-            const uint32_t w4[4] = {rw.x, rw.y, rw.z, rw.w};
+        for (int k = 0; k < kRaceGroup; ++k) av[k] = fmaf(xt[k], -c, abase);
+        float amin = av[0];
+#pragma unroll
+        for (int k = 1; k < kRaceGroup; ++k) amin = fminf(amin, av[k]);
+        const bool need = live && amin <= kMaxNegLogE - 0.5f;
+        if (__ballot(need) == 0ull) return;  // no lane's group can win: no draws
+        const uint32_t x0 = static_cast<uint32_t>(live ? gi : g_lo) * kRaceGroup;
+        const uint4 sw = philox10(make_uint4(x0 >> 3, pos, seq, kTagScreen), key);
+#pragma unroll
+        for (int blk = 0; blk < kRaceGroup / 4; ++blk) {
+            bool maybe[4];
+            bool any = false;
 #pragma unroll
             for (int qi = 0; qi < 4; ++qi) {
                 const int k = blk * 4 + qi;
-                const bool cand = need && static_cast<float>(leading_ones(w4[qi])) >= av[k];
+                const int n16 = leading_ones16(screen_half(sw, static_cast<uint32_t>(k)));
+                maybe[qi] = need && (n16 == 16 || static_cast<float>(n16) >= av[k]);
+                any |= maybe[qi];
+            }
+            if (__ballot(any) == 0ull) continue;
+            const uint32_t base = x0 + blk * 4;
+            const uint4 rw = philox10(make_uint4(base >> 2, pos, seq, kTagRace), key);
+#pragma unroll
+            for (int qi = 0; qi < 4; ++qi) {
+                const int k = blk * 4 + qi;
+                const uint32_t word = race_word_of(screen_half(sw, static_cast<uint32_t>(k)),
+                                                   pick_word(rw, static_cast<uint32_t>(qi)));
+                const bool cand = maybe[qi] && static_cast<float>(leading_ones(word)) >= av[k];
                 const int x = static_cast<int>(base) + qi;
                 if (cand && x < V) {
                     const float p = fmaf(xt[k], c, -lt2);  // log2 p
                     float lw;
+                    const float xd = RES ? E::elem(q.d[k / EPV], k % EPV) : 0.f;
                     if (RES) {
-                        const float qq = hw_exp2(fmaf(E::elem(q.d, k), c, -ld2));
+                        const float qq = hw_exp2(fmaf(xd, c, -ld2));
                         const float w = hw_exp2(p) - qq;
                         lw = w > 0.f ? hw_log2(w) : -__builtin_inff();
                     } else {
                         lw = p;
                     }
-                    const float e2 = -hw_log2(lattice_u32f(w4[qi]));  // E / ln 2 > 0
+                    const float e2 = -hw_log2(lattice_u32f(word));  // E / ln 2 > 0
                     const float g = lw - hw_log2(e2);
                     if (g > best) {
                         best2 = best;
@@ -314,8 +349,8 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
                         best = g;
                         bx = x;
                         bt = xt[k];
-                        if (RES) bd = E::elem(q.d, k);
-                        bw = w4[qi];
+                        if (RES) bd = xd;
+                        bw = word;
                     } else if (g > best2) {
                         best2 = g;
                         b2x = x;
@@ -332,30 +367,35 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
     int it = 0;
     for (; it + 2 < nit; it += 2) {
         load_trip(qb, it + 1);
-        trip(qa, v_lo + it * NT + tid, true);
+        trip(qa, g_lo + it * NT + tid, true);
         load_trip(qa, it + 2);
-        trip(qb, v_lo + (it + 1) * NT + tid, true);
+        trip(qb, g_lo + (it + 1) * NT + tid, true);
     }
     if (it + 1 < nit) {
         load_trip(qb, it + 1);
-        trip(qa, v_lo + it * NT + tid, true);
-        trip(qb, v_lo + (it + 1) * NT + tid, true);
+        trip(qa, g_lo + it * NT + tid, true);
+        trip(qb, g_lo + (it + 1) * NT + tid, true);
     } else if (it < nit) {
-        trip(qa, v_lo + it * NT + tid, true);
+        trip(qa, g_lo + it * NT + tid, true);
     }
-    if (v_lo + nit * NT < v_hi) {  // the rest of the range, fewer vectors than threads
-        const int vi = v_lo + nit * NT + tid;
-        const bool live = vi < v_hi;
-        Vec q;
-        q.t = q.d = make_uint4(0u, 0u, 0u, 0u);
-        if (vi < v_hf) {
-            q.t = load_stream(tv + vi);
-            if (RES) q.d = load_stream(dv + vi);
-        } else if (live) {
-            q.t = E::partial(trow, vi, V);
-            if (RES) q.d = E::partial(drow, vi, V);
+    if (g_lo + nit * NT < g_hi) {  // the rest of the range, fewer groups than threads
+        const int gi = g_lo + nit * NT + tid;
+        const bool live = gi < g_hi;
+        Grp q;
+        const uint32_t ni = E::pad_word();
+#pragma unroll
+        for (int v = 0; v < G; ++v) {
+            const int vi = gi * G + v;
+            q.t[v] = q.d[v] = make_uint4(ni, ni, ni, ni);
+            if (live && vi < nfull) {
+                q.t[v] = load_stream(tv + vi);
+                if (RES) q.d[v] = load_stream(dv + vi);
+            } else if (live && vi < nvec) {
+                q.t[v] = E::partial(trow, vi, V);
+                if (RES) q.d[v] = E::partial(drow, vi, V);
+            }
         }
-        trip(q, vi, live);
+        trip(q, gi, live);
     }
 
     // Workgroup maximum of the screening keys (DPP within waves, LDS across).
@@ -394,8 +434,7 @@ __device__ void race_range(const T *trow, const T *drow, int v_lo, int v_hi, int
     if (near) exact_key(bt, bd, bw, &k64, &kx, bx);
     if (near2)
         exact_key(E::at(trow, b2x), RES ? E::at(drow, b2x) : 0.f,
-                  draw_u32(key, static_cast<uint32_t>(b2x), pos, seq, kTagRace), &k64b, &kxb,
-                  b2x);
+                  race_word(key, static_cast<uint32_t>(b2x), pos, seq), &k64b, &kxb, b2x);
     // The wave's two best candidates: usually one lane is near, so its values
     // are read lane by lane rather than reduced over the whole wave.
     Top2 wt;
@@ -443,9 +482,9 @@ __device__ __forceinline__ void race_listed(const RaceArgs &a, int b, int jstar,
     t.init();
     if (tid < n) {
         const int2 e = a.bonus_list[static_cast<int64_t>(b) * kMaxBonusCand + tid];
-        const double u = lattice_u64(draw_u32(key, static_cast<uint32_t>(e.x),
-                                              static_cast<uint32_t>(jstar),
-                                              static_cast<uint32_t>(b), kTagRace));
+        const double u = lattice_u64(race_word(key, static_cast<uint32_t>(e.x),
+                                               static_cast<uint32_t>(jstar),
+                                               static_cast<uint32_t>(b)));
         t.add(static_cast<double>(__int_as_float(e.y)) * a.inv_t - log(-log(u)), e.x);
     }
 #pragma unroll
@@ -462,10 +501,10 @@ __device__ __forceinline__ void race_listed(const RaceArgs &a, int b, int jstar,
     }
 }
 
-// Race over vectors [v_lo, v_hi) of sequence b's row at the decided position.
+// Race over groups [g_lo, g_hi) of sequence b's row at the decided position.
 template <typename T, int NT>
 __device__ __forceinline__ void race_decided(const RaceArgs &a, int b, const RowPick &pk,
-                                             bool residual, PhiloxKey key, int v_lo, int v_hi,
+                                             bool residual, PhiloxKey key, int g_lo, int g_hi,
                                              double *k, int *x, double *k2) {
     const int jstar = pk.jstar;
     const T *trow = static_cast<const T *>(a.target) +
@@ -473,10 +512,10 @@ __device__ __forceinline__ void race_decided(const RaceArgs &a, int b, const Row
     if (residual) {
         const T *drow = static_cast<const T *>(a.draft) +
                         (static_cast<int64_t>(b) * a.K + jstar) * a.stride;
-        race_range<T, NT, true>(trow, drow, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
+        race_range<T, NT, true>(trow, drow, g_lo, g_hi, a.V, a.c, static_cast<double>(a.c),
                                 a.inv_t, pk.lt, pk.ld, key, jstar, b, pk.am, k, x, k2);
     } else {
-        race_range<T, NT, false>(trow, nullptr, v_lo, v_hi, a.V, a.c, static_cast<double>(a.c),
+        race_range<T, NT, false>(trow, nullptr, g_lo, g_hi, a.V, a.c, static_cast<double>(a.c),
                                  a.inv_t, pk.lt, 0.0, key, jstar, b, pk.am, k, x, k2);
     }
 }
@@ -499,9 +538,9 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
     if (n >= 0) {
         if (seg == 0) race_listed(a, b, jstar, n, key, &k, &x, &k2);
     } else {
-        const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
-        const int v_lo = seg * a.seg_vecs;
-        race_decided<T, NT>(a, b, pk, residual, key, v_lo, min(nvec, v_lo + a.seg_vecs), &k, &x,
+        const int ngroups = (a.V + kRaceGroup - 1) / kRaceGroup;
+        const int g_lo = seg * a.seg_groups;
+        race_decided<T, NT>(a, b, pk, residual, key, g_lo, min(ngroups, g_lo + a.seg_groups), &k, &x,
                             &k2);
     }
     if (threadIdx.x == 0)
@@ -550,13 +589,13 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
     if (y < 0) {
         const T *trow = static_cast<const T *>(a.target) +
                         (static_cast<int64_t>(b) * (K + 1) + jstar) * a.stride;
-        const int nvec = (a.V + Elem<T>::kPerVec - 1) / Elem<T>::kPerVec;
+        const int ngroups = (a.V + kRaceGroup - 1) / kRaceGroup;
         const double lt = a.t_lse2[b * (K + 1) + jstar];
         const PhiloxKey key = philox_key(a.seed);
         double k = -__builtin_inf(), kk2 = -__builtin_inf();
         int x = -1;
         const int am = a.t_am[b * (K + 1) + jstar];
-        race_range<T, NT, false>(trow, nullptr, 0, nvec, a.V, a.c, static_cast<double>(a.c),
+        race_range<T, NT, false>(trow, nullptr, 0, ngroups, a.V, a.c, static_cast<double>(a.c),
                                  a.inv_t, lt, 0.0, key, jstar, b, am, &k, &x, &kk2);
         y = __shfl(x, 0);
         k1 = __shfl(k, 0);

@@ -42,6 +42,7 @@ __device__ __forceinline__ uint4 philox10(uint4 c, PhiloxKey k) {
 // Stream tags (fourth counter word).
 constexpr uint32_t kTagAccept = 1u;
 constexpr uint32_t kTagRace = 2u;
+constexpr uint32_t kTagScreen = 3u;
 
 __device__ __forceinline__ uint32_t pick_word(const uint4 &r, uint32_t w) {
     return w == 0 ? r.x : (w == 1 ? r.y : (w == 2 ? r.z : r.w));
@@ -51,6 +52,24 @@ __device__ __forceinline__ uint32_t pick_word(const uint4 &r, uint32_t w) {
 __device__ __forceinline__ uint32_t draw_u32(PhiloxKey k, uint32_t x, uint32_t pos, uint32_t seq,
                                              uint32_t tag) {
     return pick_word(philox10(make_uint4(x >> 2, pos, seq, tag), k), x & 3u);
+}
+
+// The race's word for id x is made of two independent draws: its high 16
+// bits come from the screening stream, whose block at counter
+// (x>>3, pos, seq, kTagScreen) serves eight consecutive ids (half x&1 of word
+// (x>>1)&3), its low 16 bits are the high half of the race stream's draw.
+// A sampler can bound an id's largest key from the screening bits alone, one
+// block per eight ids, and draw the race stream only for ids that could win.
+__device__ __forceinline__ uint32_t screen_half(const uint4 &s, uint32_t x) {
+    return (pick_word(s, (x >> 1) & 3u) >> (16u * (x & 1u))) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t race_word_of(uint32_t hi16, uint32_t race_draw) {
+    return (hi16 << 16) | (race_draw >> 16);
+}
+__device__ __forceinline__ uint32_t race_word(PhiloxKey k, uint32_t x, uint32_t pos,
+                                              uint32_t seq) {
+    const uint4 s = philox10(make_uint4(x >> 3, pos, seq, kTagScreen), k);
+    return race_word_of(screen_half(s, x), draw_u32(k, x, pos, seq, kTagRace));
 }
 
 // The 23 leading bits on the odd points of the 2^-24 grid: (2k+1) 2^-24,
@@ -67,5 +86,10 @@ __device__ __forceinline__ double lattice_u64(uint32_t r) {
 // E = -ln u >= 1 - u, -log2(E / ln 2) <= 1 + n + log2(ln 2) < 0.472 + n.
 // Counts at most 31 (the bound only needs min(., 23)): ~r | 1 is never 0.
 __device__ __forceinline__ int leading_ones(uint32_t r) { return __builtin_clz(~r | 1u); }
+// Leading one bits of a race word known from its high 16 bits alone: exact
+// below 16; 16 means "at least 16".
+__device__ __forceinline__ int leading_ones16(uint32_t hi16) {
+    return __builtin_clz(~(hi16 << 16) | 1u);
+}
 
 }  // namespace sv

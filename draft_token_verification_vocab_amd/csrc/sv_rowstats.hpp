@@ -409,8 +409,8 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     if (list_row) {
         // the race's key of the top token, in its units (l*c - log2(E/ln2)),
         // less M*c
-        const uint32_t w = draw_u32(philox_key(a.seed), static_cast<uint32_t>(P),
-                                    static_cast<uint32_t>(j), static_cast<uint32_t>(b), kTagRace);
+        const uint32_t w = race_word(philox_key(a.seed), static_cast<uint32_t>(P),
+                                     static_cast<uint32_t>(j), static_cast<uint32_t>(b));
         tc = -hw_log2(-hw_log2(lattice_u32f(w))) - kBonusBelow;
         const uint64_t holders = __ballot(v0b >= 0 && (m - M) * c >= tc);
         const uint64_t outside = __ballot((m2 - M) * c >= tc);

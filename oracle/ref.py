@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify_ref.so")
 
 TAG_ACCEPT = 1
 TAG_RACE = 2
+TAG_SCREEN = 3
 NEAR_ACCEPT = 1
 NEAR_RACE = 2
 RESIDUAL_EMPTY = 4
@@ -60,6 +61,10 @@ def lib():
         L.ref_draw_u32.restype = u32
         L.ref_uniform.argtypes = [u64, u32, u32, u32, u32]
         L.ref_uniform.restype = f64
+        L.ref_race_u32.argtypes = [u64, u32, u32, u32]
+        L.ref_race_u32.restype = u32
+        L.ref_race_uniform.argtypes = [u64, u32, u32, u32]
+        L.ref_race_uniform.restype = f64
         L.ref_rows_stats.argtypes = [P, i64, i64, i64, ctypes.c_int, f64, P, P, P, P, P, P, P,
                                      ctypes.c_int]
         L.ref_rows_stats.restype = ctypes.c_int
@@ -127,6 +132,14 @@ def draw_u32(seed, x, pos, b, tag):
 
 def uniform(seed, x, pos, b, tag):
     return float(lib().ref_uniform(seed, x, pos, b, tag))
+
+
+def race_u32(seed, x, pos, b):
+    return int(lib().ref_race_u32(seed, x, pos, b))
+
+
+def race_uniform(seed, x, pos, b):
+    return float(lib().ref_race_uniform(seed, x, pos, b))
 
 
 def rows_stats(logits2d, temperature=1.0, nthreads=None, V=None):

@@ -74,6 +74,27 @@ double ref_uniform(uint64_t seed, uint32_t x, uint32_t pos, uint32_t b, uint32_t
     return (2.0 * k + 1.0) / 16777216.0;
 }
 
+/* The race's word for id x: two independent draws give its two halves.  The
+ * high half is 16 bits of the screening stream, one Philox block per eight
+ * consecutive ids (half x&1 of word (x>>1)&3 of the block at counter
+ * (x>>3, pos, b, REF_TAG_SCREEN)); the low half is the high half of the race
+ * stream's draw for x.  Independent uniform halves make a uniform word. */
+uint32_t ref_race_u32(uint64_t seed, uint32_t x, uint32_t pos, uint32_t b) {
+    uint32_t ctr[4] = {x >> 3, pos, b, REF_TAG_SCREEN};
+    uint32_t key[2] = {(uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    ref_philox4x32_10(ctr, key, out);
+    uint32_t hi = (out[(x >> 1) & 3u] >> (16u * (x & 1u))) & 0xffffu;
+    uint32_t lo = ref_draw_u32(seed, x, pos, b, REF_TAG_RACE) >> 16;
+    return (hi << 16) | lo;
+}
+
+double ref_race_uniform(uint64_t seed, uint32_t x, uint32_t pos, uint32_t b) {
+    uint32_t r = ref_race_u32(seed, x, pos, b);
+    double k = (double)(r >> 9);
+    return (2.0 * k + 1.0) / 16777216.0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Inputs                                                                    */
 /* ------------------------------------------------------------------------ */
@@ -235,7 +256,7 @@ int64_t ref_race(const double *w, int64_t V, uint64_t seed, uint32_t pos, uint32
     double k1 = 0.0, k2 = 0.0;
     for (int64_t x = 0; x < V; ++x) {
         if (!(w[x] > 0.0)) continue;
-        double u = ref_uniform(seed, (uint32_t)x, pos, b, REF_TAG_RACE);
+        double u = ref_race_uniform(seed, (uint32_t)x, pos, b);
         double E = -log(u);
         double key = w[x] / E;
         if (key > k1) {

@@ -33,6 +33,7 @@ extern "C" {
 /* Philox stream tags: the fourth counter word, keeping draws disjoint. */
 #define REF_TAG_ACCEPT 1u /* uniform u_j of the accept test at position j   */
 #define REF_TAG_RACE 2u   /* per-vocab-id uniforms of the sampling race      */
+#define REF_TAG_SCREEN 3u /* high half of each race word (see ref_race_u32) */
 
 /* Boundary-case bits reported per sequence (near-ties where an fp32 device
  * computation may legitimately decide the other way). */
@@ -54,6 +55,15 @@ uint32_t ref_draw_u32(uint64_t seed, uint32_t x, uint32_t pos, uint32_t b, uint3
 
 /* Uniform on the odd 2^-24 lattice: u = (2*(r>>9)+1) * 2^-24, in (0,1). */
 double ref_uniform(uint64_t seed, uint32_t x, uint32_t pos, uint32_t b, uint32_t tag);
+
+/* The sampling race's 32-bit word for vocabulary id x at (pos, b): high 16
+ * bits = half (x&1) of word (x>>1)&3 of the block at counter
+ * (x>>3, pos, b, REF_TAG_SCREEN); low 16 bits = the high half of
+ * ref_draw_u32(seed, x, pos, b, REF_TAG_RACE). */
+uint32_t ref_race_u32(uint64_t seed, uint32_t x, uint32_t pos, uint32_t b);
+
+/* The race's uniform: ref_race_u32 on the same 2^-24 lattice. */
+double ref_race_uniform(uint64_t seed, uint32_t x, uint32_t pos, uint32_t b);
 
 /* Row statistics of nrows rows of V logits (row r starts at base + r*stride
  * elements).  Every output pointer may be NULL.  Per row, with z = l/T:

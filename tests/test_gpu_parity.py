@@ -719,8 +719,8 @@ def test_boundary_near_race_on_device(path, delta):
     V, seed, ia, ib = 4000, 3, 1234, 3210
     residual = path == "residual"
     pos = 0 if residual else 1
-    Ea = -np.log(ref.uniform(seed, ia, pos, 0, ref.TAG_RACE))
-    Eb = -np.log(ref.uniform(seed, ib, pos, 0, ref.TAG_RACE))
+    Ea = -np.log(ref.race_uniform(seed, ia, pos, 0))
+    Eb = -np.log(ref.race_uniform(seed, ib, pos, 0))
     la = np.float32(np.log(Ea / Eb) + np.log1p(delta))
     t, d, x = _race_pair_rows(ia, ib, la, 0.0, V, residual)
     if path == "raced":
@@ -782,8 +782,8 @@ def test_low_temperature_race_screening():
     c = 1.0 / np.float32(T)
     for pos_pair in ((11, 4000), (4000, 11)):
         ia, ib = pos_pair
-        Ea = -np.log(ref.uniform(seed, ia, 1, 0, ref.TAG_RACE))
-        Eb = -np.log(ref.uniform(seed, ib, 1, 0, ref.TAG_RACE))
+        Ea = -np.log(ref.race_uniform(seed, ia, 1, 0))
+        Eb = -np.log(ref.race_uniform(seed, ib, 1, 0))
         # (la - lb)/T = ln(Ea/Eb) + 1e-3
         lb = np.float32(10.0)
         la = np.float32(lb + (np.log(Ea / Eb) + 1e-3) / c)

@@ -24,7 +24,7 @@ SEED = 11
 
 def _E(oracle, x, pos, b, seed=SEED):
     """E_x = -ln u_x of the race's pinned uniform for id x."""
-    return -math.log(oracle.uniform(seed, x, pos, b, oracle.TAG_RACE))
+    return -math.log(oracle.race_uniform(seed, x, pos, b))
 
 
 # ---------------------------------------------------------------------------

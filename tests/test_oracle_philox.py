@@ -92,3 +92,43 @@ def test_accept_probability_by_lattice_count():
         k = np.arange(2**23, dtype=np.float64)
         frac = np.count_nonzero((2 * k + 1) / 2**24 < r) / 2**23
         assert abs(frac - min(1.0, r)) <= 2**-24
+
+
+def test_race_word_layout(oracle):
+    # The race's word for id x: high 16 bits from the screening stream (half
+    # x&1 of word (x>>1)&3 of the block at counter (x>>3, pos, b, 3)), low 16
+    # bits the high half of the race stream's draw (word x&3 of the block at
+    # counter (x>>2, pos, b, 2)); both blocks from the pinned Philox.
+    seed = 0x0123456789ABCDEF
+    key = [seed & 0xFFFFFFFF, seed >> 32]
+    for x, pos, b in [(0, 0, 0), (1, 0, 0), (7, 3, 9), (8, 3, 9), (13, 8, 1023),
+                      (131071, 2, 77), (152063, 4, 511)]:
+        s = oracle.philox4x32_10([x >> 3, pos, b, oracle.TAG_SCREEN], key)
+        r = oracle.philox4x32_10([x >> 2, pos, b, oracle.TAG_RACE], key)
+        hi = (int(s[(x >> 1) & 3]) >> (16 * (x & 1))) & 0xFFFF
+        assert oracle.race_u32(seed, x, pos, b) == (hi << 16) | (int(r[x & 3]) >> 16)
+        k = oracle.race_u32(seed, x, pos, b) >> 9
+        assert oracle.race_uniform(seed, x, pos, b) == (2 * k + 1) / 2**24
+
+
+def test_race_uniform_is_uniform(oracle):
+    # Made of two independent streams, the race's uniforms are uniform: a KS
+    # test over 200000 ids, leading-one counts with the geometric law the
+    # sampler's bound assumes, and no correlation with either stream alone.
+    n = 200000
+    us = np.array([oracle.race_uniform(5, x, 1, 3) for x in range(n)])
+    assert stats.kstest(us, "uniform").pvalue > 1e-3
+    words = np.array([oracle.race_u32(5, x, 1, 3) for x in range(n)], dtype=np.uint64)
+    ones = np.zeros(n, dtype=np.int64)
+    w = words.copy()
+    for bit in range(31, -1, -1):  # leading one bits, counted from the top
+        still = ones == (31 - bit)
+        ones += (still & (((w >> bit) & 1) == 1)).astype(np.int64)
+    counts = np.bincount(np.minimum(ones, 8), minlength=9)
+    expect = np.array([n * 2.0 ** -(k + 1) for k in range(8)] + [n * 2.0 ** -8])
+    assert stats.chisquare(counts, expect).pvalue > 1e-3
+    plain = np.array([oracle.uniform(5, x, 1, 3, oracle.TAG_RACE) for x in range(20000)])
+    assert abs(np.corrcoef(plain, us[:20000])[0, 1]) < 0.03
+    hi = (words >> 16).astype(np.float64)
+    lo = (words & 0xFFFF).astype(np.float64)
+    assert abs(np.corrcoef(hi, lo)[0, 1]) < 0.01
