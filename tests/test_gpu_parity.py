@@ -773,6 +773,46 @@ def test_boundary_near_gate_on_device(off):
     assert np_(r.accepted_len)[0] == K
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("path", ["bonus", "residual"])
+def test_race_winner_with_saturated_screening_half(dtype, path):
+    # Flat weights: the race's winner is the id with the largest word.  For
+    # the seed taken that id's high 16 bits (its screening half) are all ones, so its
+    # leading ones are known only as "16 or more" until the race stream is
+    # drawn: the device must not screen it out.  The draw from p runs at the
+    # bonus row (row 0 identical in target and draft: accepted), the residual
+    # at row 0 (the draft puts nearly all its mass on the drafted token).
+    V = 131072
+    pos = 1 if path == "bonus" else 0
+
+    def winner(seed):
+        words = np.array([ref.race_u32(seed, x, pos, 0) for x in range(V)], dtype=np.uint64)
+        if path == "residual":
+            words[7] = 0  # the drafted token has no residual weight
+        k = words >> 9  # the lattice index of each id's uniform
+        w = int(np.argmax(k))
+        unique = np.count_nonzero(k == k[w]) == 1
+        return w if unique and int(words[w]) >> 16 == 0xFFFF else None
+
+    # the first seed whose winner has a saturated screening half and no tie
+    seed = next(s for s in range(1, 50) if winner(s) is not None)
+    win = winner(seed)
+    t = np.zeros((1, 2, V), dtype=np.float32)
+    d = np.zeros((1, 1, V), dtype=np.float32)
+    if path == "residual":
+        d[0, 0, 7] = 30.0
+    x = np.array([[7]], dtype=np.int32)
+    tt = torch.from_numpy(t).to(dtype).to(DEV)
+    dd = torch.from_numpy(d).to(dtype).to(DEV)
+    r = sv.verify(tt, dd, torch.from_numpy(x).to(DEV), seed=seed, boundary=True)
+    torch.cuda.synchronize()
+    o = ref.verify(host_logits(tt), host_logits(dd), x, seed, nthreads=NT)
+    compare_decisions(np_(r.accepted_len), np_(r.tokens), o, ALL_NEAR, "constructed",
+                      dev_boundary=np_(r.boundary), tally="constructed")
+    assert np_(r.accepted_len)[0] == pos
+    assert o["tokens"][0, pos] == win and np_(r.tokens)[0, pos] == win
+
+
 def test_low_temperature_race_screening():
     # T = 1e-4 with logits near 10: l*c ~ 1.4e5, where a float carries 1.6e-2
     # of rounding; two ids whose race keys lie 1e-3 apart (within that
