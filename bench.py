@@ -212,7 +212,7 @@ def main():
     pev[1].record(stream)
     torch.cuda.synchronize()
     pms = pev[0].elapsed_time(pev[1]) / n_k
-    ceiling = {"kernel": "read_probe_kernel<512,2> (load-only twin of the row pass)",
+    ceiling = {"kernel": "read_probe_kernel<768,2> (load-only twin of the row pass)",
                "kernel_us": round(pms * 1e3, 2),
                "gbps": round(bytes_per_step / (pms * 1e-3) / 1e9, 1),
                "row_pass_frac_of_ceiling": round(pms / kms, 4)}
@@ -237,7 +237,7 @@ def main():
             valu = {k: va[k] for k in ("valu_insts_per_logit", "valu_busy_frac")}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "row_stats_kernel<bf16,512,2,entropy>", "kernel_us": round(kms * 1e3, 2),
+                "kernel": "row_stats_kernel<bf16,768,2,entropy>", "kernel_us": round(kms * 1e3, 2),
                 "algorithmic_bytes_per_launch": bytes_per_step,
                 "evented_launch_us_p10_p50_p90": _pcts(launch_us),
                 "valu": valu,

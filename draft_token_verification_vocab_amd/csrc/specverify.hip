@@ -126,8 +126,9 @@ spec_status launch_status() {
 // ---------------------------------------------------------------------------
 template <typename T, bool E0, bool CAND>
 void launch_rows_t(const RowArgs &a, int nblocks, hipStream_t st) {
-    row_stats_kernel<T, kRowBlock, RowUnroll<T>::value, E0, CAND>
-        <<<dim3(nblocks), dim3(kRowBlock), 0, st>>>(a);
+    constexpr int kBlock = row_block<T, E0, CAND>();
+    row_stats_kernel<T, kBlock, RowUnroll<T>::value, E0, CAND>
+        <<<dim3(nblocks), dim3(kBlock), 0, st>>>(a);
 }
 
 template <typename T>
@@ -655,8 +656,9 @@ spec_status spec_read_probe(const void *logits, int64_t rows, int64_t row_bytes,
     if (rows > INT32_MAX || row_bytes > INT32_MAX) return SPEC_ERR_UNSUPPORTED;
     if (rows == 0) return SPEC_OK;
     if (!logits || !aligned16(logits) || !sink) return SPEC_ERR_ARG;
-    read_probe_kernel<kRowBlock, RowUnroll<uint16_t>::value>
-        <<<dim3(static_cast<unsigned>(rows)), dim3(kRowBlock), 0, static_cast<hipStream_t>(stream)>>>(
+    read_probe_kernel<kEntropyRowBlock, RowUnroll<uint16_t>::value>
+        <<<dim3(static_cast<unsigned>(rows)), dim3(kEntropyRowBlock), 0,
+           static_cast<hipStream_t>(stream)>>>(
             logits, row_bytes / 16, row_stride_bytes / 16, sink);
     return launch_status();
 }

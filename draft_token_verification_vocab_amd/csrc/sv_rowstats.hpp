@@ -33,8 +33,19 @@
 namespace sv {
 
 // Launch shape: threads per workgroup and 16-byte vectors per thread per
-// chunk.  A chunk holds 16 bfloat16 or 16 float logits.
+// chunk.  A chunk holds 16 bfloat16 or 16 float logits.  The entropy variant
+// on bfloat16 rows without bonus candidates (FLy rows and entropy row
+// statistics) takes 768 threads: at its 76 registers a SIMD holds six waves,
+// two 768-thread workgroups per compute unit, and that shape measured ~1.2 %
+// faster than 512.  Every pass that reads draft rows keeps 512 threads, so
+// that draft statistics are the same bits whichever call produces them (the
+// verify pass, the scorer's pass or the scorer's per-sequence prefix loop).
 constexpr int kRowBlock = 512;
+constexpr int kEntropyRowBlock = 768;
+template <typename T, bool ENT0, bool CAND>
+constexpr int row_block() {
+    return sizeof(T) == 2 && ENT0 && !CAND ? kEntropyRowBlock : kRowBlock;
+}
 template <typename T>
 struct RowUnroll;
 template <>
