@@ -253,12 +253,17 @@ __device__ void race_range(const T *trow, const T *drow, int g_lo, int g_hi, int
     struct Grp {
         uint4 t[G], d[G];
     };
+    // Whole trips are buffer-addressed over the rows' full vectors: the trip's
+    // byte offset is wave-uniform, each lane's offset inside it fixed.
+    const buf_rsrc rt = make_rsrc(trow, static_cast<uint32_t>(nfull) * 16u);
+    const buf_rsrc rd = make_rsrc(RES ? drow : trow, static_cast<uint32_t>(nfull) * 16u);
     auto load_trip = [&](Grp &q, int it) {
-        const int gi = g_lo + it * NT + tid;
+        const uint32_t soff = static_cast<uint32_t>(g_lo + it * NT) * (G * 16u);
 #pragma unroll
         for (int v = 0; v < G; ++v) {
-            q.t[v] = load_stream(tv + gi * G + v);
-            if (RES) q.d[v] = load_stream(dv + gi * G + v);
+            const uint32_t voff = static_cast<uint32_t>(tid * G + v) * 16u;
+            q.t[v] = load_stream_buf(rt, voff, soff);
+            if (RES) q.d[v] = load_stream_buf(rd, voff, soff);
         }
     };
     Grp qa, qb;
