@@ -17,10 +17,12 @@
 // double key; a combine kernel takes the best segment.  Work is pruned by
 // bounds: the key of the target's top token (then the wave's best) bounds
 // the row's best from below; an id's key is at most log2 p plus 23.5 on the
-// 2^-24 lattice, and at most log2 p + 0.5 + (leading one bits of its Philox
-// word) once drawn.  Blocks of ids below the first bound skip their draws
-// (on peaked rows nearly all of them); drawn ids below the second skip their
-// exact weight and logarithms (nearly all ids of any row).
+// 2^-24 lattice, and at most log2 p + 0.5 + (leading one bits of its race
+// word).  Groups of eight ids below the first bound skip their draws (on
+// peaked rows nearly all of them); the others draw one screening block, whose
+// 16 high word bits per id settle the second bound for all but a few ids, and
+// draw the rest of the word only for blocks of four with an id still in;
+// ids below the second bound skip their exact weight and logarithms.
 //
 // FLy (page "Training-Free Loosely Speculative Decoding...", section
 // "2. Metodologia", part A): one wave per sequence; deviations and gate

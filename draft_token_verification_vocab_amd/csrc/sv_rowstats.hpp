@@ -11,7 +11,7 @@
 // adaptive-verification estimator (page "Verificacion Adaptativa sin una
 // cabeza de confianza", section "Puntuar la Distribucion").
 //
-// Rows are streamed with non-temporal 16-byte loads.
+// Rows are streamed with non-temporal 16-byte buffer loads.
 //
 // In a lossless call the target row L_b of each sequence (the only row where a
 // draw from p can happen) also lists the ids such a draw could pick, so that
@@ -20,11 +20,12 @@
 // Arithmetic is in base 2: with c = log2(e)/T every term is 2^(l*c - mc),
 // where mc = m*c and m is the running maximum of the raw logits.  A thread
 // reads its share of the row in chunks of UNROLL vectors (UNROLL*8 bfloat16
-// or UNROLL*4 float logits); a thread sums its terms and its chunk sums in
-// float, and the sums across threads are formed in double.  Each thread keeps
-// the chunk that holds its maximum apart (its sums in registers, its raw data
-// in LDS), so the end can replace that chunk by its terms other than the
-// argmax and form 1 - q_max without cancellation, however peaked the row.
+// or UNROLL*4 float logits); the sums within a thread and within a wave are
+// float (every term has one sign), the sums across waves double.  Each
+// thread keeps the chunk that holds its maximum apart (its sums in registers,
+// its raw data in LDS), so the end can replace that chunk by its terms other
+// than the argmax and form 1 - q_max without cancellation, however peaked the
+// row.
 #pragma once
 
 #include "sv_common.hpp"
