@@ -406,20 +406,24 @@ def run_secondary(sv, W, dev, stream, args, only=None):
                                workspace=ws4, boundary=True, prefix=True) for b in sets]
         res = [cl.verify.out for cl in calls]
 
+        ran = set()
+
         def f4(i):
+            ran.add(i % nsets)
             calls[i % nsets](i % nsets)
         nsteps = nsets if only is None else n
         ms = _timeit(f4, nsteps, warm, stream, torch)
-        # the last step on each input set: its kept lengths; rows read are the
-        # draft rows up to each trim point and the target rows 0..kept
-        kept_all = torch.stack([cl.kept for cl in calls])
+        # the last step on each input set that ran: its kept lengths; rows
+        # read are the draft rows up to each trim point and the target rows
+        # 0..kept
+        kept_all = torch.stack([calls[i].kept for i in sorted(ran)])
         verified = [int((k + 1).sum().item()) for k in kept_all]
         drafts_read = [int(torch.clamp(k + 1, max=K).sum().item()) for k in kept_all]
-        rows = int(round((sum(verified) + sum(drafts_read)) / nsets))
-        line = _line(ms, rows, rows * c["V"] * 2, res, verified)
-        line["draft_rows_read_per_step"] = round(sum(drafts_read) / nsets, 1)
+        rows = int(round((sum(verified) + sum(drafts_read)) / len(ran)))
+        line = _line(ms, rows, rows * c["V"] * 2, [res[i] for i in sorted(ran)], verified)
+        line["draft_rows_read_per_step"] = round(sum(drafts_read) / len(ran), 1)
         line["draft_rows_per_step"] = 1024 * K
-        line["input_sets"] = nsets
+        line["input_sets"] = len(ran)
         line["mean_kept_len"] = round(float(kept_all.float().mean().item()), 4)
         line["kept_len_hist"] = torch.bincount(kept_all.flatten().long(),
                                                minlength=K + 1).tolist()
