@@ -126,7 +126,7 @@ spec_status launch_status() {
 // ---------------------------------------------------------------------------
 template <typename T, bool E0, bool CAND>
 void launch_rows_t(const RowArgs &a, int nblocks, hipStream_t st) {
-    constexpr int kBlock = row_block<T, E0, CAND>();
+    constexpr int kBlock = row_block<T>();
     row_stats_kernel<T, kBlock, RowUnroll<T>::value, E0, CAND>
         <<<dim3(nblocks), dim3(kBlock), 0, st>>>(a);
 }
@@ -392,11 +392,13 @@ spec_status spec_av_score_prefix(const void *draft, const int32_t *draft_tokens,
     pa.qmax = ds.qmax;
     pa.feat = ds.feat;
     if (p.dtype == SPEC_DTYPE_BF16)
-        av_prefix_kernel<uint16_t, kRowBlock, RowUnroll<uint16_t>::value>
-            <<<dim3(B), dim3(kRowBlock), 0, st>>>(pa, omega_beta, tau, conf, keep_mask, kept_len);
+        av_prefix_kernel<uint16_t, row_block<uint16_t>(), RowUnroll<uint16_t>::value>
+            <<<dim3(B), dim3(row_block<uint16_t>()), 0, st>>>(pa, omega_beta, tau, conf, keep_mask,
+                                                              kept_len);
     else
-        av_prefix_kernel<float, kRowBlock, RowUnroll<float>::value>
-            <<<dim3(B), dim3(kRowBlock), 0, st>>>(pa, omega_beta, tau, conf, keep_mask, kept_len);
+        av_prefix_kernel<float, row_block<float>(), RowUnroll<float>::value>
+            <<<dim3(B), dim3(row_block<float>()), 0, st>>>(pa, omega_beta, tau, conf, keep_mask,
+                                                           kept_len);
     return launch_status();
 }
 
@@ -656,8 +658,8 @@ spec_status spec_read_probe(const void *logits, int64_t rows, int64_t row_bytes,
     if (rows > INT32_MAX || row_bytes > INT32_MAX) return SPEC_ERR_UNSUPPORTED;
     if (rows == 0) return SPEC_OK;
     if (!logits || !aligned16(logits) || !sink) return SPEC_ERR_ARG;
-    read_probe_kernel<kEntropyRowBlock, RowUnroll<uint16_t>::value>
-        <<<dim3(static_cast<unsigned>(rows)), dim3(kEntropyRowBlock), 0,
+    read_probe_kernel<kRowBlockBf16, RowUnroll<uint16_t>::value>
+        <<<dim3(static_cast<unsigned>(rows)), dim3(kRowBlockBf16), 0,
            static_cast<hipStream_t>(stream)>>>(
             logits, row_bytes / 16, row_stride_bytes / 16, sink);
     return launch_status();

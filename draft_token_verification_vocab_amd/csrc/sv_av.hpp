@@ -23,6 +23,12 @@ __device__ __forceinline__ double av_confidence(double omega, float f, float bet
     return 1.0 / (1.0 + exp(-z));
 }
 
+// The same behind a call, for a loop over rows (see row_emit_stats).
+__device__ __attribute__((noinline)) double av_confidence_call(double omega, float f,
+                                                               float beta) {
+    return av_confidence(omega, f, beta);
+}
+
 // One thread per sequence.  feat: [B*K] (draft statistics).
 __global__ void av_score_kernel(const float *feat, int B, int K, const float *omega_beta,
                                 float tau, float *conf, uint8_t *keep_mask, int32_t *kept_len) {
@@ -109,11 +115,11 @@ __global__ __launch_bounds__(BLOCK) void av_prefix_kernel(PrefixArgs pa, const f
         a.V = Vi;
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
-        row_one<T, BLOCK, UNROLL, false, false>(a, g, row, sh_saved, tid);
+        row_one<T, BLOCK, UNROLL, false, false, true>(a, g, row, sh_saved, tid);
         if (threadIdx.x == 0) {
-            // thread 0 wrote this row's feature itself (row_emit)
-            const double ci = av_confidence(static_cast<double>(omega_beta[0]), pa.feat[row],
-                                            omega_beta[1 + i]);
+            // thread 0 wrote this row's feature itself (row_emit_stats)
+            const double ci = av_confidence_call(static_cast<double>(omega_beta[0]),
+                                                 pa.feat[row], omega_beta[1 + i]);
             P *= ci;
             const bool keep = t <= 0.0 || P >= t;  // still open: every earlier one was kept
             if (conf) conf[row] = static_cast<float>(ci);

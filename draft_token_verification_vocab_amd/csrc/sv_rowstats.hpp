@@ -34,18 +34,18 @@
 namespace sv {
 
 // Launch shape: threads per workgroup and 16-byte vectors per thread per
-// chunk.  A chunk holds 16 bfloat16 or 16 float logits.  The entropy variant
-// on bfloat16 rows without bonus candidates (FLy rows and entropy row
-// statistics) takes 768 threads: at its 76 registers a SIMD holds six waves,
-// two 768-thread workgroups per compute unit, and that shape measured ~1.2 %
-// faster than 512.  Every pass that reads draft rows keeps 512 threads, so
-// that draft statistics are the same bits whichever call produces them (the
-// verify pass, the scorer's pass or the scorer's per-sequence prefix loop).
-constexpr int kRowBlock = 512;
-constexpr int kEntropyRowBlock = 768;
-template <typename T, bool ENT0, bool CAND>
+// chunk.  A chunk holds 16 bfloat16 or 16 float logits.  bfloat16 rows take
+// 768-thread workgroups, two per compute unit (at the entropy variant's 76
+// registers a SIMD holds six waves), which measured 1-1.5 % faster than 512
+// threads on every bfloat16 pass; float rows keep 512.  Every pass over a
+// dtype has the same shape, so that draft statistics are the same bits
+// whichever call produces them (the verify pass, the scorer's pass or the
+// scorer's per-sequence prefix loop).
+constexpr int kRowBlockF32 = 512;
+constexpr int kRowBlockBf16 = 768;
+template <typename T>
 constexpr int row_block() {
-    return sizeof(T) == 2 && ENT0 && !CAND ? kEntropyRowBlock : kRowBlock;
+    return sizeof(T) == 2 ? kRowBlockBf16 : kRowBlockF32;
 }
 template <typename T>
 struct RowUnroll;
@@ -177,6 +177,28 @@ __device__ __forceinline__ void row_emit(const RowArgs &a, const RowGroup &g, in
         g.logtok2[gidx] = static_cast<double>(ltok) * static_cast<double>(c) - lse2;
 }
 
+// row_emit for a row group that writes only the draft statistics (lse2,
+// logtok2, qmax_int, feat_int), behind a call.  A kernel that runs row_one in
+// a loop over rows calls this: inlined, the double-precision logarithm's and
+// exponential's constants are hoisted out of that loop and each held in a
+// register for the whole kernel (102 registers instead of 63), which halves
+// the workgroups a compute unit holds.  Lane 0 alone makes the call, once per
+// row.
+__device__ __attribute__((noinline)) void row_emit_stats(float c, double *lse2, double *logtok2,
+                                                         float *qmax_int, float *feat_int,
+                                                         int64_t row, float M, int P, double r,
+                                                         double to, bool gather, int gidx,
+                                                         float ltok) {
+    RowArgs a{};
+    a.c = c;
+    RowGroup g{};
+    g.lse2 = lse2;
+    g.logtok2 = logtok2;
+    g.qmax_int = qmax_int;
+    g.feat_int = feat_int;
+    row_emit<false>(a, g, row, M, P, r, to, gather, gidx, ltok);
+}
+
 // CAND: target rows of a lossless call; row L_b of each sequence also lists
 // the ids a race over p at that row could pick.  Each thread tracks, besides
 // its max chunk (saved in LDS), the largest maximum m2 of its other chunks
@@ -185,9 +207,12 @@ __device__ __forceinline__ void row_emit(const RowArgs &a, const RowGroup &g, in
 // incomplete and the race reads the row.
 // tid: threadIdx.x (a caller that loops over rows passes it through an
 // opaque copy, so that values derived from it are not kept live across rows).
-template <typename T, int BLOCK, int UNROLL, bool ENT, bool CAND>
+// STATS_CALL: g writes only the draft statistics, emitted by row_emit_stats
+// (for callers that loop over rows).
+template <typename T, int BLOCK, int UNROLL, bool ENT, bool CAND, bool STATS_CALL = false>
 __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int64_t row,
                                         uint4 (&sh_saved)[UNROLL][BLOCK], const int tid) {
+    static_assert(!STATS_CALL || (!ENT && !CAND), "the statistics call emits a plain row");
     using E = Elem<T>;
     constexpr int EPV = E::kPerVec;
     constexpr int N = UNROLL * EPV;
@@ -536,7 +561,11 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
             r += sh_s[w];
             to += sh_t[w];
         }
-        row_emit<ENT>(a, g, row, M, P, r, to, gather, gidx, ltok);
+        if constexpr (STATS_CALL)
+            row_emit_stats(a.c, g.lse2, g.logtok2, g.qmax_int, g.feat_int, row, M, P, r, to,
+                           gather, gidx, ltok);
+        else
+            row_emit<ENT>(a, g, row, M, P, r, to, gather, gidx, ltok);
     }
 }
 
