@@ -125,36 +125,43 @@ spec_status launch_status() {
 // never needs the entropy numerator.
 // ---------------------------------------------------------------------------
 template <typename T, bool E0, bool CAND>
-void launch_rows_t(const RowArgs &a, int nblocks, hipStream_t st) {
+void launch_rows_t(const RowArgs &a, int nblocks, bool trimmed, hipStream_t st) {
     constexpr int kBlock = row_block<T>();
-    row_stats_kernel<T, kBlock, RowUnroll<T>::value, E0, CAND>
-        <<<dim3(nblocks), dim3(kBlock), 0, st>>>(a);
+    constexpr int kTrimmed = kRowBlockTrimmed;
+    if (trimmed && kTrimmed != kBlock)
+        row_stats_kernel<T, kTrimmed, RowUnroll<T>::value, E0, CAND>
+            <<<dim3(nblocks), dim3(kTrimmed), 0, st>>>(a);
+    else
+        row_stats_kernel<T, kBlock, RowUnroll<T>::value, E0, CAND>
+            <<<dim3(nblocks), dim3(kBlock), 0, st>>>(a);
 }
 
 template <typename T>
-void launch_rows_dt(const RowArgs &a, int nblocks, bool e0, bool cand, hipStream_t st) {
+void launch_rows_dt(const RowArgs &a, int nblocks, bool e0, bool cand, bool trimmed,
+                    hipStream_t st) {
     if (cand) {
         if (e0)
-            launch_rows_t<T, true, true>(a, nblocks, st);
+            launch_rows_t<T, true, true>(a, nblocks, trimmed, st);
         else
-            launch_rows_t<T, false, true>(a, nblocks, st);
+            launch_rows_t<T, false, true>(a, nblocks, trimmed, st);
     } else {
         if (e0)
-            launch_rows_t<T, true, false>(a, nblocks, st);
+            launch_rows_t<T, true, false>(a, nblocks, trimmed, st);
         else
-            launch_rows_t<T, false, false>(a, nblocks, st);
+            launch_rows_t<T, false, false>(a, nblocks, trimmed, st);
     }
 }
 
 // cand: group 0 holds a lossless call's target rows, which also list the
-// bonus candidates (a.seed, a.cand_cnt, a.cand_list set).
+// bonus candidates (a.seed, a.cand_cnt, a.cand_list set).  trimmed: a launch
+// with kept lengths over target rows alone (see kRowBlockTrimmed).
 void launch_rows(int32_t dtype, const RowArgs &a, int nblocks, bool e0, hipStream_t st,
-                 bool cand = false) {
+                 bool cand = false, bool trimmed = false) {
     if (nblocks <= 0) return;
     if (dtype == SPEC_DTYPE_BF16)
-        launch_rows_dt<uint16_t>(a, nblocks, e0, cand, st);
+        launch_rows_dt<uint16_t>(a, nblocks, e0, cand, trimmed, st);
     else
-        launch_rows_dt<float>(a, nblocks, e0, cand, st);
+        launch_rows_dt<float>(a, nblocks, e0, cand, trimmed, st);
 }
 
 RowGroup empty_group() {
@@ -275,7 +282,7 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
         ra.cand_cnt = bonus_cnt;
         ra.cand_list = bonus_list;
     }
-    launch_rows(p.dtype, ra, nrows, ent0, st, lossless);
+    launch_rows(p.dtype, ra, nrows, ent0, st, lossless, kept_len != nullptr && !own_draft);
     if ((s = launch_status()) != SPEC_OK) return s;
 
     if (!lossless) {

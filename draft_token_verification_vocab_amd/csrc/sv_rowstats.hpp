@@ -37,16 +37,23 @@ namespace sv {
 // chunk.  A chunk holds 16 bfloat16 or 16 float logits.  bfloat16 rows take
 // 768-thread workgroups, two per compute unit (at the entropy variant's 76
 // registers a SIMD holds six waves), which measured 1-1.5 % faster than 512
-// threads on every bfloat16 pass; float rows keep 512.  Every pass over a
-// dtype has the same shape, so that draft statistics are the same bits
-// whichever call produces them (the verify pass, the scorer's pass or the
-// scorer's per-sequence prefix loop).
+// threads on the bfloat16 passes that read every row; float rows keep 512.
+// Every pass that reads draft rows takes its dtype's shape, so that draft
+// statistics are the same bits whichever call produces them (the verify pass,
+// the scorer's pass or the scorer's per-sequence prefix loop).
 constexpr int kRowBlockF32 = 512;
 constexpr int kRowBlockBf16 = 768;
 template <typename T>
 constexpr int row_block() {
     return sizeof(T) == 2 ? kRowBlockBf16 : kRowBlockF32;
 }
+// Launches with kept lengths that read target rows alone take 512 threads
+// whatever the dtype: most of their workgroups (rows past a kept length) exit
+// after one load, and the extra waves of a 768-thread workgroup make each
+// such exit dearer (the adaptive pipeline's verify pass, 9216 workgroups of
+// which ~7500 exit: 75-78 us at 512 threads against 83-85 us at 768).  No
+// draft statistics come from such a launch.
+constexpr int kRowBlockTrimmed = 512;
 template <typename T>
 struct RowUnroll;
 template <>
