@@ -33,6 +33,12 @@
 
 namespace sv {
 
+// A count of vectors as a type (the row pass's chunk variants).
+template <int NV>
+struct Vecs {
+    static constexpr int value = NV;
+};
+
 // Launch shape: threads per workgroup and 16-byte vectors per thread per
 // chunk.  A chunk holds 16 bfloat16 or 16 float logits.  bfloat16 rows take
 // 768-thread workgroups, two per compute unit (at the entropy variant's 76
@@ -257,22 +263,27 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
     float m2 = kNoMax;  // CAND: the largest maximum of the other chunks
 
     // it: the chunk's index; thread tid's chunk `it` starts at vector
-    // it*UNROLL*BLOCK + tid.
-    auto consume = [&](const uint4 (&buf)[UNROLL], int it) {
+    // it*UNROLL*BLOCK + tid.  nv (Vecs<NV>): the chunk's first NV vectors are
+    // processed, NV < UNROLL only for a last chunk whose later vectors are
+    // padding in every thread: padding's terms are exactly 0 and its value
+    // lies below every maximum that can change the state, so leaving it out
+    // gives the same bits.
+    auto consume = [&](const uint4 (&buf)[UNROLL], int it, auto nv) {
+        constexpr int NL = decltype(nv)::value * EPV;  // logits processed
         float x[N];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) E::unpack(buf[u], x + u * EPV);
         // the chunk maximum in a chain of three-input maxima
         float cm = max3f(x[0], x[1], x[2]);
 #pragma unroll
-        for (int k = 3; k + 1 < N; k += 2) cm = max3f(cm, x[k], x[k + 1]);
-        if (N % 2 == 0) cm = max3f(cm, x[N - 1], x[N - 1]);
+        for (int k = 3; k + 1 < NL; k += 2) cm = max3f(cm, x[k], x[k + 1]);
+        if (NL % 2 == 0) cm = max3f(cm, x[NL - 1], x[NL - 1]);
         const bool up = cm > m;
         const float mcn = up ? mul_rn(cm, c) : mc;
         // Terms of this chunk against the (possibly new) maximum.
         float s4[4], t4[4];
 #pragma unroll
-        for (int k = 0; k < N; ++k) {
+        for (int k = 0; k < NL; ++k) {
             const float d = fmaf(x[k], c, -mcn);
             const float e = hw_exp2(d);
             if (k < 4) {
@@ -293,7 +304,7 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
             if (!(ctsum == ctsum)) {
                 ctsum = 0.f;
 #pragma unroll
-                for (int k = 0; k < N; ++k) {
+                for (int k = 0; k < NL; ++k) {
                     const float d = fmaxf(fmaf(x[k], c, -mcn), kMinExp2);
                     ctsum = fmaf(hw_exp2(d), d, ctsum);
                 }
@@ -357,6 +368,9 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
             buf[u] = load_stream_buf(rs, static_cast<uint32_t>(vc) * 16u, 0u);
         }
     };
+    // When the last chunks hold at most BLOCK vectors, every thread's vectors
+    // u >= 1 there are padding and only the first is processed.
+    const bool tail_one = nvec - nit * kChunkVecs <= BLOCK;
     auto consume_last = [&](uint4 (&buf)[UNROLL]) {
         if (v < nvec) {
 #pragma unroll
@@ -365,7 +379,10 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
                 if (vi >= nfull)
                     buf[u] = vi < nvec ? E::partial(rp, vi, V) : make_uint4(ni, ni, ni, ni);
             }
-            consume(buf, nit);
+            if (tail_one)
+                consume(buf, nit, Vecs<1>{});
+            else
+                consume(buf, nit, Vecs<UNROLL>{});
         }
     };
     // One chunk in flight: two register buffers take turns.  The loop issues
@@ -378,18 +395,18 @@ __device__ __forceinline__ void row_one(const RowArgs &a, const RowGroup &g, int
         int it = 0;
         for (; it + 3 <= nit; it += 2) {  // loads it+1 and it+2, both < nit
             load_chunk(bufB, it + 1);
-            consume(bufA, it);
+            consume(bufA, it, Vecs<UNROLL>{});
             load_chunk(bufA, it + 2);
-            consume(bufB, it + 1);
+            consume(bufB, it + 1, Vecs<UNROLL>{});
         }
         if (it + 1 < nit) {  // two full chunks left, the first in bufA
             load_chunk(bufB, it + 1);
-            consume(bufA, it);
+            consume(bufA, it, Vecs<UNROLL>{});
             load_last(bufA);
-            consume(bufB, it + 1);
+            consume(bufB, it + 1, Vecs<UNROLL>{});
         } else {  // one full chunk left, in bufA
             load_last(bufB);
-            consume(bufA, it);
+            consume(bufA, it, Vecs<UNROLL>{});
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) bufA[u] = bufB[u];
         }
