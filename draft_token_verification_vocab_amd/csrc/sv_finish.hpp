@@ -323,8 +323,8 @@ __device__ void race_range(const T *trow, const T *drow, int g_lo, int g_hi, int
 #pragma unroll
             for (int qi = 0; qi < 4; ++qi) {
                 const int k = blk * 4 + qi;
-                const int n16 = leading_ones16(screen_half(sw, static_cast<uint32_t>(k)));
-                maybe[qi] = need && (n16 == 16 || static_cast<float>(n16) >= av[k]);
+                // bitwise, so that no lane branches per id
+                maybe[qi] = need & (screen_ones(sw, static_cast<uint32_t>(k)) >= av[k]);
                 any |= maybe[qi];
             }
             if (__ballot(any) == 0ull) continue;

@@ -86,10 +86,18 @@ __device__ __forceinline__ double lattice_u64(uint32_t r) {
 // E = -ln u >= 1 - u, -log2(E / ln 2) <= 1 + n + log2(ln 2) < 0.472 + n.
 // Counts at most 31 (the bound only needs min(., 23)): ~r | 1 is never 0.
 __device__ __forceinline__ int leading_ones(uint32_t r) { return __builtin_clz(~r | 1u); }
-// Leading one bits of a race word known from its high 16 bits alone: exact
-// below 16; 16 means "at least 16".
-__device__ __forceinline__ int leading_ones16(uint32_t hi16) {
-    return __builtin_clz(~(hi16 << 16) | 1u);
+// Leading one bits of id x's 16 screening bits (the high half of its race
+// word) as a float: exact below 16, and 2^32 - 1 when all 16 are ones, i.e.
+// above every count a whole word can have, so that a test "ones >= a" keeps
+// each id whose screening bits alone cannot rule it out.  The field is moved
+// to the top of a word with zeros below, whose leading zeros v_ffbh_u32
+// counts (all ones for a zero word).
+__device__ __forceinline__ float screen_ones(const uint4 &s, uint32_t x) {
+    const uint32_t w = ~pick_word(s, (x >> 1) & 3u);
+    const uint32_t y = (x & 1u) ? (w & 0xFFFF0000u) : (w << 16);
+    uint32_t n;
+    asm("v_ffbh_u32 %0, %1" : "=v"(n) : "v"(y));
+    return static_cast<float>(n);
 }
 
 }  // namespace sv
