@@ -393,12 +393,12 @@ spec_status spec_row_stats(const void *logits, int64_t rows, int32_t vocab, int6
  * spec_read_probe -- a measurement aid, not part of verification: streams
  * `rows` rows of `row_bytes` bytes each (consecutive rows `row_stride_bytes`
  * apart) with the same loads, workgroup shape and one-workgroup-per-row grid
- * as the entropy row pass on bfloat16 rows (the FLy pass), but with almost no
- * arithmetic, and stores the XOR of each row's 32-bit words in sink[row].  Its bandwidth is the ceiling the row pass
- * can reach on the same rows.  logits: device, 16-byte aligned; row_bytes and
- * row_stride_bytes: multiples of 16, row_bytes <= row_stride_bytes
- * (row_bytes beyond 2^31 - 1: SPEC_ERR_UNSUPPORTED);
- * sink: device uint32 [rows].  Asynchronous on `stream`.
+ * as the row pass on bfloat16 rows, but with almost no arithmetic, and stores
+ * the XOR of each row's 32-bit words in sink[row].  Its bandwidth is the
+ * ceiling the row pass can reach on the same rows.  logits: device, 16-byte
+ * aligned; row_bytes and row_stride_bytes: multiples of 16, row_bytes <=
+ * row_stride_bytes (row_bytes beyond 2^31 - 1: SPEC_ERR_UNSUPPORTED); sink:
+ * device uint32 [rows].  Asynchronous on `stream`.
  */
 spec_status spec_read_probe(const void *logits, int64_t rows, int64_t row_bytes,
                             int64_t row_stride_bytes, uint32_t *sink, void *stream);
