@@ -62,6 +62,10 @@ _SIGNATURES = {
     "spec_verify": (ctypes.c_int32, [_P, _P, _P, _P, _P, ctypes.c_uint64, ctypes.c_int32,
                                      ctypes.POINTER(_Params), ctypes.POINTER(_VerifyOut), _P,
                                      ctypes.c_size_t, _P]),
+    "spec_verify_update": (ctypes.c_int32, [_P, _P, _P, _P, _P, ctypes.c_uint64,
+                                            ctypes.POINTER(_Params), ctypes.POINTER(_VerifyOut),
+                                            ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                            _P]),
     "spec_verify_noalloc": (ctypes.c_int32, [_P, _P, _P, _P, _P, ctypes.c_uint64,
                                              ctypes.c_int32, ctypes.POINTER(_Params),
                                              ctypes.POINTER(_VerifyOut), _P]),
@@ -244,6 +248,54 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
     return out
 
 
+def verify_update(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                  omega_beta: torch.Tensor, lr: float, *, seed: int = 0,
+                  temperature: float = 1.0, vocab: Optional[int] = None,
+                  kept_len: Optional[torch.Tensor] = None,
+                  draft_stats: Optional[torch.Tensor] = None, score: bool = False,
+                  boundary: bool = False, workspace: Optional[torch.Tensor] = None):
+    """spec_verify_update: lossless verification and the estimator's update
+    in one call.  score=True (no kept_len, no draft_stats) also returns the
+    confidences at the coefficients before the update, as av_score_update.
+    Returns (VerifyResult, conf, keep_mask, kept_len_out); the last three are
+    None unless score.  omega_beta is updated in place."""
+    _need_cuda(target, "target")
+    _need_cuda(draft, "draft")
+    _need_cuda(draft_tokens, "draft_tokens")
+    _need_cuda(omega_beta, "omega_beta")
+    B, K1, S = target.shape
+    K = K1 - 1
+    V = S if vocab is None else int(vocab)
+    if draft.shape != (B, K, S) or draft.dtype != target.dtype:
+        raise ValueError("draft must be [B, K, S] with the target's dtype")
+    if draft_tokens.dtype != torch.int32 or draft_tokens.shape != (B, K):
+        raise ValueError("draft_tokens must be int32 [B, K]")
+    if omega_beta.dtype != torch.float32 or omega_beta.numel() != K + 1:
+        raise ValueError("omega_beta must be float32 [K+1]")
+    dev = target.device
+    p = _params(B, K, V, S, _dtype_code(target), temperature)
+    L = load()
+    out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
+                       torch.empty(B, K + 1, dtype=torch.int32, device=dev))
+    if boundary:
+        out.boundary = torch.empty(B, dtype=torch.int32, device=dev)
+    conf = mask = kept = None
+    if score:
+        conf = torch.empty(B, K, dtype=torch.float32, device=dev)
+        mask = torch.empty(B, K, dtype=torch.uint8, device=dev)
+        kept = torch.empty(B, dtype=torch.int32, device=dev)
+    o = out.fields()
+    need = int(L.spec_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(L.spec_verify_update(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(kept_len),
+                                _ptr(draft_stats), ctypes.c_uint64(int(seed) & (2**64 - 1)),
+                                ctypes.byref(p), ctypes.byref(o), float(lr), _ptr(omega_beta),
+                                _ptr(conf), _ptr(mask), _ptr(kept), _ptr(workspace),
+                                workspace.numel(), _stream(dev)), "spec_verify_update")
+    return out, conf, mask, kept
+
+
 class VerifyCall:
     """A verification call with its arguments marshalled once, for loops that
     verify the same buffers again and again (a serving step, a benchmark):
@@ -355,12 +407,16 @@ class AvStepCall:
     be trimmed, so spec_verify reads target and draft rows in one pass and
     exports the draft statistics, and spec_av_score_update scores from them
     and takes the SGD step in one launch: the same results with one row pass
-    instead of two, and four launches instead of five."""
+    instead of two.
+
+    The verification and the update are one call, spec_verify_update, whose
+    last launch picks the tokens and takes the update side by side; split=True
+    makes them the separate calls above instead (the same results)."""
 
     def __init__(self, target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
                  omega_beta: torch.Tensor, tau: float, lr: float, *, temperature: float = 1.0,
                  vocab: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                 boundary: bool = False, prefix: bool = False):
+                 boundary: bool = False, prefix: bool = False, split: bool = False):
         _need_cuda(draft, "draft")
         B, K, S = draft.shape
         V = S if vocab is None else int(vocab)
@@ -395,16 +451,28 @@ class AvStepCall:
                                      workspace=workspace, boundary=boundary)
         self.update_args = (_ptr(self.stats), _ptr(self.verify.out.accepted_len),
                             _ptr(self.kept), int(B), int(K), float(lr), _ptr(omega_beta), st)
+        self.split = bool(split)
+        va = self.verify.args
+        if self.fused:  # scores and update from the verify pass's own statistics
+            self.vu_args = va[:3] + [None, None, va[5], va[7], va[8], float(lr), _ptr(omega_beta),
+                                     _ptr(self.conf), _ptr(self.mask), _ptr(self.kept)] + va[9:]
+        else:
+            self.vu_args = va[:6] + [va[7], va[8], float(lr), _ptr(omega_beta), None, None,
+                                     None] + va[9:]
         self._keep = (target, draft, draft_tokens, omega_beta)
 
     def __call__(self, seed: int = 0) -> VerifyResult:
-        if self.fused:
-            r = self.verify(seed)
-            _check(self.L.spec_av_score_update(*self.score_update_args), "spec_av_score_update")
-            return r
-        _check(self.score_fn(*self.score_args), "spec_av_score")
+        if not self.fused:
+            _check(self.score_fn(*self.score_args), "spec_av_score")
+        if not self.split:
+            self.vu_args[5] = ctypes.c_uint64(int(seed) & (2**64 - 1))
+            _check(self.L.spec_verify_update(*self.vu_args), "spec_verify_update")
+            return self.verify.out
         r = self.verify(seed)
-        _check(self.L.spec_av_update(*self.update_args), "spec_av_update")
+        if self.fused:
+            _check(self.L.spec_av_score_update(*self.score_update_args), "spec_av_score_update")
+        else:
+            _check(self.L.spec_av_update(*self.update_args), "spec_av_update")
         return r
 
 

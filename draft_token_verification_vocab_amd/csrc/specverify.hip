@@ -13,6 +13,7 @@
 #include "sv_finish.hpp"
 #include "sv_next.hpp"
 #include "sv_rowstats.hpp"
+#include "sv_step.hpp"
 
 namespace {
 
@@ -36,6 +37,8 @@ constexpr int kSmallBlock = 64;
 constexpr int kFlyBlock = 256;
 // Label reductions (SGD step, Newton accumulation): a wave per position.
 constexpr int kLabelBlock = 512;
+// Sequences per token-picking workgroup of race_step_kernel (a wave each).
+constexpr int kStepSeqs = kLabelBlock / kWave;
 // Diagnostics: labels per call, bins, label-kernel workgroup.
 constexpr int64_t kDiagMaxLabels = 1 << 16;
 constexpr int kDiagMaxBins = 64;
@@ -201,10 +204,12 @@ size_t spec_draft_stats_bytes(int32_t batch, int32_t num_draft) {
     return 24 * static_cast<size_t>(batch) * static_cast<size_t>(num_draft);
 }
 
-spec_status spec_verify(const void *target, const void *draft, const int32_t *draft_tokens,
-                        const int32_t *kept_len, const void *draft_stats, uint64_t seed,
-                        int32_t mode, const spec_params *params, const spec_verify_out *out,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+// spec_verify, and with upd the step's update in its last launch.
+static spec_status verify_impl(const void *target, const void *draft, const int32_t *draft_tokens,
+                               const int32_t *kept_len, const void *draft_stats, uint64_t seed,
+                               int32_t mode, const spec_params *params,
+                               const spec_verify_out *out, void *workspace,
+                               size_t workspace_bytes, void *stream, StepUpdate *upd) {
     spec_status s = check_params(params);
     if (s != SPEC_OK) return s;
     if (mode != SPEC_MODE_LOSSLESS && mode != SPEC_MODE_FLY) return SPEC_ERR_ARG;
@@ -320,16 +325,61 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
     rg.bonus_cnt = bonus_cnt;
     rg.bonus_list = bonus_list;
     const dim3 grid(static_cast<unsigned>(rg.segs) * static_cast<unsigned>(B));
-    if (p.dtype == SPEC_DTYPE_BF16) {
+    const bool bf16 = p.dtype == SPEC_DTYPE_BF16;
+    if (bf16)
         race_kernel<uint16_t, kRaceBlock><<<grid, dim3(kRaceBlock), 0, st>>>(rg);
+    else
+        race_kernel<float, kRaceBlock><<<grid, dim3(kRaceBlock), 0, st>>>(rg);
+    if (upd) {
+        // the tokens and the update in one launch: a workgroup per kStepSeqs
+        // sequences, then one for the update
+        upd->feat = ds.feat;
+        upd->B = B;
+        const dim3 sgrid(static_cast<unsigned>((B + kStepSeqs - 1) / kStepSeqs + 1));
+        if (bf16)
+            race_step_kernel<uint16_t, kLabelBlock><<<sgrid, dim3(kLabelBlock), 0, st>>>(
+                rg, draft_tokens, out->accepted_len, out->tokens, out->boundary, *upd);
+        else
+            race_step_kernel<float, kLabelBlock><<<sgrid, dim3(kLabelBlock), 0, st>>>(
+                rg, draft_tokens, out->accepted_len, out->tokens, out->boundary, *upd);
+    } else if (bf16) {
         race_combine_kernel<uint16_t, kSmallBlock><<<dim3(B), dim3(kSmallBlock), 0, st>>>(
             rg, draft_tokens, out->accepted_len, out->tokens, out->boundary);
     } else {
-        race_kernel<float, kRaceBlock><<<grid, dim3(kRaceBlock), 0, st>>>(rg);
         race_combine_kernel<float, kSmallBlock><<<dim3(B), dim3(kSmallBlock), 0, st>>>(
             rg, draft_tokens, out->accepted_len, out->tokens, out->boundary);
     }
     return launch_status();
+}
+
+spec_status spec_verify(const void *target, const void *draft, const int32_t *draft_tokens,
+                        const int32_t *kept_len, const void *draft_stats, uint64_t seed,
+                        int32_t mode, const spec_params *params, const spec_verify_out *out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    return verify_impl(target, draft, draft_tokens, kept_len, draft_stats, seed, mode, params, out,
+                       workspace, workspace_bytes, stream, nullptr);
+}
+
+spec_status spec_verify_update(const void *target, const void *draft, const int32_t *draft_tokens,
+                               const int32_t *kept_len, const void *draft_stats, uint64_t seed,
+                               const spec_params *params, const spec_verify_out *out, float lr,
+                               float *omega_beta, float *conf, uint8_t *keep_mask,
+                               int32_t *kept_len_out, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    const bool score = conf || keep_mask || kept_len_out;
+    if (!std::isfinite(lr)) return SPEC_ERR_ARG;
+    if (score && (kept_len || draft_stats)) return SPEC_ERR_ARG;  // scores need an untrimmed step
+    if (params && params->batch > 0 && !omega_beta) return SPEC_ERR_ARG;
+    StepUpdate u{};
+    u.kept_len = kept_len;
+    u.omega_beta = omega_beta;
+    u.conf = conf;
+    u.keep_mask = keep_mask;
+    u.kept_out = kept_len_out;
+    u.lr = lr;
+    u.score = score ? 1 : 0;
+    return verify_impl(target, draft, draft_tokens, kept_len, draft_stats, seed,
+                       SPEC_MODE_LOSSLESS, params, out, workspace, workspace_bytes, stream, &u);
 }
 
 spec_status spec_av_score(const void *draft, const int32_t *draft_tokens,

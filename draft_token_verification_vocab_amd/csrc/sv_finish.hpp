@@ -562,14 +562,18 @@ __global__ __launch_bounds__(NT) void race_kernel(RaceArgs a) {
 // the winner and the second largest key.  A residual that vanished in
 // floating point (no candidate anywhere; only possible within rounding of
 // u_j = p/q) falls back to a race over p at the same row.
-template <typename T, int NT>
-__global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int32_t *tokens,
-                                                         int32_t *accepted_len,
-                                                         int32_t *out_tokens,
-                                                         uint32_t *boundary) {
-    static_assert(NT == kWave, "one wave per sequence");
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
+struct SeqPick {
+    double k1, k2;   // the winner's key and the second largest
+    int y;           // the winner, -1 when no segment has a candidate
+    int jstar;       // accepted drafts (the first rejected position, or L)
+    int tk;          // this lane's draft token (lane j holds token j)
+    uint32_t flags;  // boundary bits from the race
+};
+
+// The reduction of sequence b's segment candidates by one wave (every lane
+// ends with the result).
+__device__ __forceinline__ SeqPick combine_reduce(const RaceArgs &a, const int32_t *tokens, int b,
+                                                  int lane) {
     const int K = a.K;
     const RaceCand cnd = lane < a.segs ? a.cand[b * a.segs + lane]
                                        : RaceCand{-__builtin_inf(), -__builtin_inf(), -1, 0u};
@@ -589,35 +593,67 @@ __global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int3
         t.merge(ok1, ox, ok2);
     }
     const uint32_t info = __shfl(cnd.info, 0);  // the same in every segment
-    const int jstar = static_cast<int>(info & 0xFFu);
-    uint32_t flags = info >> 8;
-    int y = t.x1 == INT_MAX ? -1 : t.x1;  // every lane holds the reduction's result
-    double k1 = t.k1, k2 = t.k2;
-    if (y < 0) {
-        const T *trow = static_cast<const T *>(a.target) +
-                        (static_cast<int64_t>(b) * (K + 1) + jstar) * a.stride;
-        const int ngroups = (a.V + kRaceGroup - 1) / kRaceGroup;
-        const double lt = a.t_lse2[b * (K + 1) + jstar];
-        const PhiloxKey key = philox_key(a.seed);
+    SeqPick s;
+    s.jstar = static_cast<int>(info & 0xFFu);
+    s.flags = info >> 8;
+    s.y = t.x1 == INT_MAX ? -1 : t.x1;
+    s.k1 = t.k1;
+    s.k2 = t.k2;
+    s.tk = tk;
+    return s;
+}
+
+// The fallback race over p at row jstar of sequence b, by a whole workgroup
+// of NT threads; the key, id and second key land in thread 0.
+template <typename T, int NT>
+__device__ __forceinline__ void combine_fallback(const RaceArgs &a, int b, int jstar, double *k,
+                                                 int *x, double *k2) {
+    const int K = a.K;
+    const T *trow = static_cast<const T *>(a.target) +
+                    (static_cast<int64_t>(b) * (K + 1) + jstar) * a.stride;
+    const int ngroups = (a.V + kRaceGroup - 1) / kRaceGroup;
+    const double lt = a.t_lse2[b * (K + 1) + jstar];
+    const PhiloxKey key = philox_key(a.seed);
+    const int am = a.t_am[b * (K + 1) + jstar];
+    race_range<T, NT, false>(trow, nullptr, 0, ngroups, a.V, a.c, static_cast<double>(a.c),
+                             a.inv_t, lt, 0.0, key, jstar, b, am, k, x, k2);
+}
+
+// Sequence b's outputs from its pick, by one wave.
+__device__ __forceinline__ void combine_emit(const RaceArgs &a, int b, int lane, SeqPick s,
+                                             int32_t *accepted_len, int32_t *out_tokens,
+                                             uint32_t *boundary) {
+    const int K = a.K;
+    if (near_race(s.k1, s.k2)) s.flags |= kNearRace;
+    if (lane == 0) {
+        accepted_len[b] = s.jstar;
+        if (boundary) boundary[b] = s.flags;
+    }
+    for (int j = lane; j <= K; j += kWave) {
+        // j < jstar <= 64 only on the first pass, where j == lane holds token j
+        out_tokens[b * (K + 1) + j] = j < s.jstar ? s.tk : (j == s.jstar ? s.y : -1);
+    }
+}
+
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void race_combine_kernel(RaceArgs a, const int32_t *tokens,
+                                                         int32_t *accepted_len,
+                                                         int32_t *out_tokens,
+                                                         uint32_t *boundary) {
+    static_assert(NT == kWave, "one wave per sequence");
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    SeqPick s = combine_reduce(a, tokens, b, lane);
+    if (s.y < 0) {
         double k = -__builtin_inf(), kk2 = -__builtin_inf();
         int x = -1;
-        const int am = a.t_am[b * (K + 1) + jstar];
-        race_range<T, NT, false>(trow, nullptr, 0, ngroups, a.V, a.c, static_cast<double>(a.c),
-                                 a.inv_t, lt, 0.0, key, jstar, b, am, &k, &x, &kk2);
-        y = __shfl(x, 0);
-        k1 = __shfl(k, 0);
-        k2 = __shfl(kk2, 0);
-        flags |= kResidualEmpty;
+        combine_fallback<T, NT>(a, b, s.jstar, &k, &x, &kk2);
+        s.y = __shfl(x, 0);
+        s.k1 = __shfl(k, 0);
+        s.k2 = __shfl(kk2, 0);
+        s.flags |= kResidualEmpty;
     }
-    if (near_race(k1, k2)) flags |= kNearRace;
-    if (lane == 0) {
-        accepted_len[b] = jstar;
-        if (boundary) boundary[b] = flags;
-    }
-    for (int j = lane; j <= K; j += NT) {
-        // j < jstar <= 64 only on the first pass, where j == lane holds token j
-        out_tokens[b * (K + 1) + j] = j < jstar ? tk : (j == jstar ? y : -1);
-    }
+    combine_emit(a, b, lane, s, accepted_len, out_tokens, boundary);
 }
 
 // FLy: a deviation is a draft token different from the target's top token.

@@ -53,10 +53,17 @@ struct LabelSums {
     double n, r, rf, w, wf, wff;
 };
 
-template <int NT, bool CURV>
-__device__ void label_sums(const float *feat, const int32_t *accepted_len,
-                           const int32_t *kept_len, int B, int K, const float *omega_beta,
-                           LabelSums *out) {
+// Accepted lengths as the label sums read them: acc(b) for sequence b, from an
+// array here; the launch that also picks each step's tokens reads them from
+// the race's candidates instead.
+struct AcceptedArray {
+    const int32_t *p;
+    __device__ int operator()(int b) const { return p[b]; }
+};
+
+template <int NT, bool CURV, class ACC>
+__device__ void label_sums(const float *feat, ACC acc, const int32_t *kept_len, int B, int K,
+                           const float *omega_beta, LabelSums *out) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = threadIdx.x / kWave;
     const double omega = static_cast<double>(omega_beta[0]);
@@ -72,7 +79,7 @@ __device__ void label_sums(const float *feat, const int32_t *accepted_len,
                 const int b = b0 + u * kWave;
                 const int bc = b < B ? b : B - 1;  // in range; masked out below
                 La[u] = kept_len ? kept_len[bc] : K;
-                aa[u] = accepted_len[bc];
+                aa[u] = acc(bc);
                 fa[u] = feat[static_cast<int64_t>(bc) * K + i];
             }
 #pragma unroll
@@ -111,12 +118,11 @@ __device__ void label_sums(const float *feat, const int32_t *accepted_len,
 
 // One SGD step on the mean log-loss of the batch's labels (the update the
 // adaptive-verification workloads run every step), by the whole workgroup.
-template <int NT>
-__device__ __forceinline__ void sgd_step(const float *feat, const int32_t *accepted_len,
-                                         const int32_t *kept_len, int B, int K, float lr,
-                                         float *omega_beta) {
+template <int NT, class ACC>
+__device__ __forceinline__ void sgd_step(const float *feat, ACC acc, const int32_t *kept_len, int B,
+                                         int K, float lr, float *omega_beta) {
     __shared__ LabelSums sums[64];
-    label_sums<NT, false>(feat, accepted_len, kept_len, B, K, omega_beta, sums);
+    label_sums<NT, false>(feat, acc, kept_len, B, K, omega_beta, sums);
     __shared__ double s_n, s_go;
     if (threadIdx.x == 0) {
         double n = 0.0, go = 0.0;
@@ -144,7 +150,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void av_sgd_kernel(const float *feat, const int32_t *accepted_len,
                                                    const int32_t *kept_len, int B, int K, float lr,
                                                    float *omega_beta) {
-    sgd_step<NT>(feat, accepted_len, kept_len, B, K, lr, omega_beta);
+    sgd_step<NT>(feat, AcceptedArray{accepted_len}, kept_len, B, K, lr, omega_beta);
 }
 
 // A step with nothing trimmed, scored after its verification: the
@@ -153,11 +159,9 @@ __global__ __launch_bounds__(NT) void av_sgd_kernel(const float *feat, const int
 // launch.  The scores read omega_beta before sgd_step's first barrier, and
 // sgd_step writes it only after that barrier.
 template <int NT>
-__global__ __launch_bounds__(NT) void av_score_update_kernel(const float *feat,
-                                                            const int32_t *accepted_len, int B,
-                                                            int K, float lr, float *omega_beta,
-                                                            float *conf, uint8_t *keep_mask,
-                                                            int32_t *kept_len) {
+__device__ __forceinline__ void score_untrimmed(const float *feat, int B, int K,
+                                                const float *omega_beta, float *conf,
+                                                uint8_t *keep_mask, int32_t *kept_len) {
     const double omega = static_cast<double>(omega_beta[0]);
     const int n = B * K;
     for (int f = threadIdx.x; f < n; f += NT) {
@@ -167,7 +171,16 @@ __global__ __launch_bounds__(NT) void av_score_update_kernel(const float *feat,
     }
     if (kept_len)
         for (int b = threadIdx.x; b < B; b += NT) kept_len[b] = K;
-    sgd_step<NT>(feat, accepted_len, nullptr, B, K, lr, omega_beta);
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void av_score_update_kernel(const float *feat,
+                                                            const int32_t *accepted_len, int B,
+                                                            int K, float lr, float *omega_beta,
+                                                            float *conf, uint8_t *keep_mask,
+                                                            int32_t *kept_len) {
+    score_untrimmed<NT>(feat, B, K, omega_beta, conf, keep_mask, kept_len);
+    sgd_step<NT>(feat, AcceptedArray{accepted_len}, nullptr, B, K, lr, omega_beta);
 }
 
 // --------------------------------------------------------------------------
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(NT) void irls_accumulate_kernel(const float *feat,
                                                             const int32_t *kept_len, int B, int K,
                                                             const float *omega_beta, double *state) {
     __shared__ LabelSums sums[64];
-    label_sums<NT, true>(feat, accepted_len, kept_len, B, K, omega_beta, sums);
+    label_sums<NT, true>(feat, AcceptedArray{accepted_len}, kept_len, B, K, omega_beta, sums);
     const IrlsView v = irls_view(state, K);
     const int t = threadIdx.x;
     if (t == 0) {

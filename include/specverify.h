@@ -283,6 +283,31 @@ spec_status spec_av_score_update(const void *draft_stats, const int32_t *accepte
                                  void *stream);
 
 /*
+ * spec_verify_update -- one adaptive-verification step's verification and
+ * update in one call ([SD] section "Математика верификации" for the lossless
+ * rule, [AV] section "Ajuste de los Coeficientes" for the update): the
+ * results of spec_verify in lossless mode with these arguments followed by
+ *   - spec_av_update(draft statistics, accepted_len, kept_len, lr), or
+ *   - when any of conf, keep_mask, kept_len_out is non-NULL (an untrimmed
+ *     step: kept_len and draft_stats must then be NULL, else SPEC_ERR_ARG),
+ *     spec_av_score_update(draft statistics, accepted_len, lr, conf,
+ *     keep_mask, kept_len_out),
+ * bit for bit.  The draft statistics are draft_stats when given, else those
+ * the verify pass computes from the draft rows (written to
+ * out->draft_stats_out as well when that is set).  The update's labels need
+ * only the accepted lengths, which the race already holds, so the update runs
+ * in the same launch as the choice of each sequence's token, beside it.
+ * omega_beta: device float [K+1], updated in place; lr finite.  Other
+ * arguments, workspace and errors as spec_verify.
+ */
+spec_status spec_verify_update(const void *target, const void *draft, const int32_t *draft_tokens,
+                               const int32_t *kept_len, const void *draft_stats, uint64_t seed,
+                               const spec_params *params, const spec_verify_out *out, float lr,
+                               float *omega_beta, float *conf, uint8_t *keep_mask,
+                               int32_t *kept_len_out, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
  * Newton (IRLS) refit of the estimator ([AV] section "Ajuste de los
  * Coeficientes").  The pages refit omega and the beta_i after every round of
  * N decoding steps: each step adds its labelled drafts (the same labels as

@@ -506,18 +506,21 @@ def test_av_score_update_parity_c1_full_size():
     assert np.allclose(got, want, rtol=0, atol=1e-5), (got, want)
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("tau", [0.0, 0.2])
-def test_av_step_call_matches_separate_calls(tau):
+def test_av_step_call_matches_separate_calls(tau, split):
     # AvStepCall with tau <= 0 verifies first (one row pass over target and
     # draft rows, exporting the draft statistics) and scores from them; with
-    # tau > 0 it scores, trims and verifies.  Either way: bit-identical to the
-    # separate calls, over three steps with carried parameters.
+    # tau > 0 it scores, trims and verifies.  Either way, and whether the
+    # update shares the verification's last launch (spec_verify_update) or
+    # not: bit-identical to the separate calls, over three steps with carried
+    # parameters.
     batch = W.make(1, B=20, K=5, V=7001, stride=7008)
     t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
     B, K = tok.shape
     ob_a = torch.tensor(W.av_init(1), dtype=torch.float32, device=DEV)
     ob_b = ob_a.clone()
-    call = sv.AvStepCall(t, d, tok, ob_a, tau, 0.05, vocab=batch.V)
+    call = sv.AvStepCall(t, d, tok, ob_a, tau, 0.05, vocab=batch.V, split=split)
     assert call.fused == (tau <= 0.0)
     for step in range(3):
         r_a = call(step)
@@ -531,6 +534,79 @@ def test_av_step_call_matches_separate_calls(tau):
         assert torch.equal(call.mask, mask)
         assert torch.equal(call.stats[:24 * B * K], ds[:24 * B * K])
         assert torch.equal(ob_a, ob_b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,K,trim", [(300, 7, False), (300, 7, True), (13, 64, False),
+                                      (1, 3, True)])
+def test_verify_update_matches_separate_calls(B, K, trim, dtype):
+    # spec_verify_update against spec_verify followed by spec_av_update (or,
+    # untrimmed, spec_av_score_update): the tokens, accepted lengths, boundary
+    # bits, scores and coefficients bit for bit.  B not a multiple of the
+    # token workgroup's eight sequences; K = 64 fills a wave with positions.
+    batch = W.make(1, B=B, K=K, V=3001, stride=3008)
+    t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
+    if dtype == "f32":
+        t, d = t.float(), d.float()
+    ob0 = torch.tensor(W.av_init(1, K=K), dtype=torch.float32, device=DEV)
+    for step in range(2):
+        ob_a, ob_b = ob0.clone(), ob0.clone()
+        if trim:
+            _, _, kept, ds = sv.av_score(d, tok, ob0, 0.2, vocab=batch.V)
+            ra, ca, ma, ka = sv.verify_update(t, d, tok, ob_a, 0.05, seed=step, vocab=batch.V,
+                                              kept_len=kept, draft_stats=ds, boundary=True)
+            rb = sv.verify(t, d, tok, seed=step, vocab=batch.V, kept_len=kept, draft_stats=ds,
+                           boundary=True)
+            sv.av_update(ds, rb.accepted_len, kept, ob_b, 0.05, B, K)
+        else:
+            ra, ca, ma, ka = sv.verify_update(t, d, tok, ob_a, 0.05, seed=step, vocab=batch.V,
+                                              score=True, boundary=True)
+            out = sv.VerifyResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                                  torch.empty(B, K + 1, dtype=torch.int32, device=DEV))
+            out.boundary = torch.empty(B, dtype=torch.int32, device=DEV)
+            out.draft_stats_out = torch.empty(sv.draft_stats_bytes(B, K), dtype=torch.uint8,
+                                              device=DEV)
+            rb = sv.verify(t, d, tok, seed=step, vocab=batch.V, out=out)
+            cb, mb, kb = sv.av_score_update(out.draft_stats_out, rb.accepted_len, ob_b, 0.05,
+                                            B, K)
+        torch.cuda.synchronize()
+        assert torch.equal(ra.accepted_len, rb.accepted_len)
+        assert torch.equal(ra.tokens, rb.tokens)
+        assert torch.equal(ra.boundary, rb.boundary)
+        assert torch.equal(ob_a, ob_b)
+        if B > 1:  # labels exist, so the step moved the coefficients
+            assert not torch.equal(ob_a, ob0)
+        if not trim:
+            assert torch.equal(ca, cb) and torch.equal(ma, mb) and torch.equal(ka, kb)
+        ob0 = ob_a
+
+
+def test_verify_update_residual_empty():
+    # the residual-empty construction below through spec_verify_update: the
+    # fallback race runs in the token workgroup's whole 512 threads; tokens,
+    # bits and coefficients as spec_verify and spec_av_score_update give
+    rng = np.random.default_rng(2)
+    B, K, V = 24, 2, 4000
+    t = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    t[:, :, ::4] = -np.inf
+    d = t[:, :K].copy()
+    x = np.full((B, K), V + 3, dtype=np.int32)
+    x[::3, 0] = -1
+    tt, dd, xx = (torch.from_numpy(a).to(DEV) for a in (t, d, x))
+    ob_a = torch.tensor(W.av_init(1, K=K), dtype=torch.float32, device=DEV)
+    ob_b = ob_a.clone()
+    ra, ca, _, _ = sv.verify_update(tt, dd, xx, ob_a, 0.05, seed=4, score=True, boundary=True)
+    out = sv.VerifyResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                          torch.empty(B, K + 1, dtype=torch.int32, device=DEV))
+    out.boundary = torch.empty(B, dtype=torch.int32, device=DEV)
+    out.draft_stats_out = torch.empty(sv.draft_stats_bytes(B, K), dtype=torch.uint8, device=DEV)
+    rb = sv.verify(tt, dd, xx, seed=4, out=out)
+    cb, _, _ = sv.av_score_update(out.draft_stats_out, rb.accepted_len, ob_b, 0.05, B, K)
+    torch.cuda.synchronize()
+    assert np.all(np_(ra.boundary) & sv.RESIDUAL_EMPTY)
+    assert torch.equal(ra.tokens, rb.tokens) and torch.equal(ra.boundary, rb.boundary)
+    assert torch.equal(ra.accepted_len, rb.accepted_len)
+    assert torch.equal(ca, cb) and torch.equal(ob_a, ob_b)
 
 
 @pytest.mark.parametrize("B,K", [(20, 5), (300, 7), (64, 64)])
