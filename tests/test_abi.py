@@ -45,7 +45,7 @@ def test_header_declares_the_entry_points():
               "spec_read_probe", "spec_irls_state_bytes", "spec_irls_reset",
               "spec_irls_accumulate", "spec_irls_solve", "spec_av_diagnostics",
               "spec_av_diagnostics_workspace_bytes", "spec_av_budget",
-              "spec_av_budget_workspace_bytes", "spec_ngram_propose"):
+              "spec_av_budget_workspace_bytes", "spec_ngram_propose", "spec_verify_update"):
         assert n in names
 
 
@@ -125,6 +125,27 @@ def test_empty_inputs_are_noops_on_host(L):
     assert L.spec_row_stats(None, 0, 1024, 1024, 1, 1.0, None, None, None, None, None,
                             None) == 0
     assert L.spec_av_update(None, None, None, 0, 4, 0.05, None, None) == 0
+
+
+@host_only
+def test_verify_update_validates_on_host(L):
+    p = _params()
+    out = sv._VerifyOut(16, 16, None, None, None, None, None, None)
+    v16 = ctypes.c_void_p(16)
+
+    def call(kept=None, stats=None, lr=0.05, omega=16, conf=None, pp=p, target=16):
+        return L.spec_verify_update(ctypes.c_void_p(target), v16, v16, kept, stats, 0,
+                                    ctypes.byref(pp), ctypes.byref(out), lr,
+                                    ctypes.c_void_p(omega) if omega else None, conf, None, None,
+                                    v16, 1 << 30, None)
+    assert call(lr=float("nan")) == -1
+    assert call(lr=float("inf")) == -1
+    assert call(omega=0) == -1                          # no coefficients to update
+    assert call(conf=v16, kept=v16) == -1               # scores need an untrimmed step
+    assert call(conf=v16, stats=v16) == -1
+    assert call(target=8) == -1                         # spec_verify's own checks
+    assert call(pp=_params(num_draft=65)) == -2
+    assert call(pp=_params(batch=0), omega=0) == 0      # empty batch: nothing to do
 
 
 @host_only
