@@ -148,3 +148,38 @@ def test_av_step_untrimmed_replays():
         torch.cuda.synchronize()
         assert torch.equal(ob, want_ob) and torch.equal(out.accepted_len, want_acc)
         assert torch.equal(res["conf"], want_conf)
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.2])
+def test_av_step_call_replays(tau):
+    # AvStepCall, whose verification and update are one spec_verify_update
+    # call (the update in the token-picking launch), recorded and replayed.
+    # The call binds its stream when it is built, so it is built, warmed up
+    # and captured on one side stream.
+    b = W.make(1, B=40, V=5000, stride=5000)
+    t, d, tok = b.target.to(DEV), b.draft.to(DEV), b.tokens.to(DEV)
+    ob0 = torch.tensor(W.av_init(1), dtype=torch.float32, device=DEV)
+    ob = ob0.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call = sv.AvStepCall(t, d, tok, ob, tau, 0.05, vocab=5000)
+        call(3)
+    torch.cuda.synchronize()
+    out = call.verify.out
+    want_ob, want_acc, want_tok = ob.clone(), out.accepted_len.clone(), out.tokens.clone()
+    with torch.cuda.stream(s):
+        ob.copy_(ob0)
+        call(3)  # warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(3)
+    for _ in range(3):
+        ob.copy_(ob0)
+        out.tokens.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ob, want_ob) and torch.equal(out.accepted_len, want_acc)
+        assert torch.equal(out.tokens, want_tok)
