@@ -437,6 +437,25 @@ def test_batch_beyond_grid_y_limit(mode):
         _fly_check(batch, theta=0.3, window=0)
 
 
+def test_verify_update_batch_beyond_grid_y_limit():
+    # spec_verify_update at B = 70000: its last launch has 8751 token-picking
+    # workgroups and the update's; results as spec_verify + spec_av_score_update
+    B, K, V = 70000, 2, 72
+    batch = W.make(1, B=B, K=K, V=V)
+    t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
+    ob_a = torch.tensor(W.av_init(1, K=K), dtype=torch.float32, device=DEV)
+    ob_b = ob_a.clone()
+    ra, ca, _, _ = sv.verify_update(t, d, tok, ob_a, 0.05, seed=5, score=True)
+    out = sv.VerifyResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                          torch.empty(B, K + 1, dtype=torch.int32, device=DEV))
+    out.draft_stats_out = torch.empty(sv.draft_stats_bytes(B, K), dtype=torch.uint8, device=DEV)
+    rb = sv.verify(t, d, tok, seed=5, out=out)
+    cb, _, _ = sv.av_score_update(out.draft_stats_out, rb.accepted_len, ob_b, 0.05, B, K)
+    torch.cuda.synchronize()
+    assert torch.equal(ra.accepted_len, rb.accepted_len) and torch.equal(ra.tokens, rb.tokens)
+    assert torch.equal(ca, cb) and torch.equal(ob_a, ob_b)
+
+
 def test_lossless_deterministic_across_streams():
     batch = W.make(3, B=16, K=4, V=20000)
     t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
