@@ -184,12 +184,12 @@ spec_status spec_verify(const void *target, const void *draft, const int32_t *dr
  * from the caller's workspace lives instead in a fixed device array of
  * SPEC_NOALLOC_SCRATCH_BYTES (16 MiB) that each GPU the library runs on holds
  * until the process ends.  A problem whose spec_workspace_bytes exceeds it
- * returns SPEC_ERR_UNSUPPORTED before anything is enqueued (at K = 8 that is
- * about 12000 sequences).  No hipMalloc, hipFree or other allocating call is
- * made.  The array belongs to the current device, which must be the stream's
- * device; every call on one GPU shares it, so calls that overlap on one GPU
- * (other streams, other host threads) race and must be serialised by the
- * caller.  Nothing in it needs clearing between calls.
+ * returns SPEC_ERR_UNSUPPORTED before anything is enqueued (at K = 8 and
+ * V = 128256 that is about 17800 sequences).  No hipMalloc, hipFree or other
+ * allocating call is made.  The array belongs to the current device, which
+ * must be the stream's device; every call on one GPU shares it, so calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  Nothing in it needs clearing between calls.
  */
 #define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 spec_status spec_verify_noalloc(const void *target, const void *draft,
