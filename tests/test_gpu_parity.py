@@ -474,19 +474,25 @@ def test_lossless_deterministic_across_streams():
 # ---------------------------------------------------------------------------
 # Adaptive verification
 # ---------------------------------------------------------------------------
-def _av_step(batch, ob_host, tau, lr, seed, prefix=False):
+def _av_step(batch, ob_host, tau, lr, seed, prefix=False, fused=False):
     """One GPU step (score, verify, update) and the oracle's step on the same
     inputs and the same starting parameters.  prefix: score with
-    spec_av_score_prefix (confidences past each trim point are not read)."""
+    spec_av_score_prefix (confidences past each trim point are not read).
+    fused: verify and update in one spec_verify_update call."""
     K = batch.tokens.shape[1]
     T = batch.temperature
     t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
     ob = torch.tensor(ob_host, dtype=torch.float32, device=DEV)
     conf, mask, kept, ds = sv.av_score(d, tok, ob, tau, temperature=T, vocab=batch.V,
                                        prefix=prefix)
-    r = sv.verify(t, d, tok, seed=seed, temperature=T, vocab=batch.V, kept_len=kept,
-                  draft_stats=ds, boundary=True)
-    sv.av_update(ds, r.accepted_len, kept, ob, lr, tok.shape[0], K)
+    if fused:
+        r, _, _, _ = sv.verify_update(t, d, tok, ob, lr, seed=seed, temperature=T,
+                                      vocab=batch.V, kept_len=kept, draft_stats=ds,
+                                      boundary=True)
+    else:
+        r = sv.verify(t, d, tok, seed=seed, temperature=T, vocab=batch.V, kept_len=kept,
+                      draft_stats=ds, boundary=True)
+        sv.av_update(ds, r.accepted_len, kept, ob, lr, tok.shape[0], K)
     torch.cuda.synchronize()
     dh = host_logits(batch.draft)
     B = dh.shape[0]
@@ -721,14 +727,16 @@ def test_av_pipeline_twenty_steps_full_size():
     # the pipeline does; the oracle starts each step from the same values).
     # After every step omega and beta match the oracle's step to 1e-5.  The
     # steps score as the benchmark does, reading draft rows up to each trim
-    # point only (even steps) and every draft row (odd steps).
+    # point only (even steps) and every draft row (odd steps); the verify and
+    # update are one spec_verify_update call in steps 0, 1 mod 4, separate
+    # calls otherwise.
     ob = W.av_init(4)
     hist = np.zeros(9, dtype=np.int64)
     for step in range(20):
         batch = W.make(4, device=DEV, step=step)
         assert batch.tokens.shape == (1024, 8)
         got, want, o, okept = _av_step(batch, ob, tau=0.2, lr=0.05, seed=step,
-                                       prefix=step % 2 == 0)
+                                       prefix=step % 2 == 0, fused=step % 4 < 2)
         assert np.allclose(got, want, rtol=0, atol=1e-5), (step, got, want)
         hist += np.bincount(okept, minlength=9)
         ob = got.tolist()
@@ -1027,5 +1035,5 @@ def test_random_av_steps(case):
     tau = 0.0 if rng.random() < 0.3 else float(rng.uniform(0.02, 0.6))
     lr = float(rng.uniform(0.01, 0.2))
     ob0 = [float(rng.uniform(0.3, 1.5))] + [float(v) for v in rng.uniform(-1.0, 1.0, K)]
-    got, want, _, okept = _av_step(batch, ob0, tau=tau, lr=lr, seed=case)
+    got, want, _, okept = _av_step(batch, ob0, tau=tau, lr=lr, seed=case, fused=case % 2 == 1)
     assert np.allclose(got, want, rtol=0, atol=1e-5), (got, want)
