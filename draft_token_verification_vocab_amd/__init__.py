@@ -272,6 +272,11 @@ def verify_update(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch
         raise ValueError("draft_tokens must be int32 [B, K]")
     if omega_beta.dtype != torch.float32 or omega_beta.numel() != K + 1:
         raise ValueError("omega_beta must be float32 [K+1]")
+    for t, n in ((kept_len, "kept_len"), (draft_stats, "draft_stats")):
+        if t is not None:
+            _need_cuda(t, n)
+    if score and (kept_len is not None or draft_stats is not None):
+        raise ValueError("score needs an untrimmed step: no kept_len, no draft_stats")
     dev = target.device
     p = _params(B, K, V, S, _dtype_code(target), temperature)
     L = load()
