@@ -1018,6 +1018,56 @@ def test_random_configurations(case):
         _fly_check(batch, theta=theta, window=window, kept=kept, kept_ref=kept_ref)
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_random_verify_update(case):
+    # spec_verify_update on random shapes against the separate calls, bit for
+    # bit: untrimmed steps (scores and SGD step from the verify pass's own
+    # statistics) and trimmed ones (statistics and kept lengths from
+    # spec_av_score), both dtypes, padded strides, random temperatures
+    rng = np.random.default_rng(9100 + case)
+    K = int(rng.integers(1, 13)) if case % 5 else 64
+    B = int(rng.integers(1, 300)) if K < 64 else int(rng.integers(1, 20))
+    V = int(np.exp(rng.uniform(np.log(8), np.log(40000))))
+    dtype = "bf16" if case % 2 else "f32"
+    unit = 8 if dtype == "bf16" else 4
+    stride = V + int(rng.integers(0, 3)) * unit
+    stride = (stride + unit - 1) // unit * unit
+    T = float(np.exp(rng.uniform(np.log(0.5), np.log(2.0))))
+    batch = W.gaussian(B, K, V, dtype, T, seed=int(rng.integers(0, 1 << 30)), token_seed=3,
+                       stride=stride)
+    t, d, tok = batch.target.to(DEV), batch.draft.to(DEV), batch.tokens.to(DEV)
+    ob0 = torch.tensor([float(rng.uniform(0.3, 1.5))] + [float(v) for v in
+                                                        rng.uniform(-1.0, 1.0, K)],
+                       dtype=torch.float32, device=DEV)
+    lr = float(rng.uniform(0.01, 0.2))
+    ob_a, ob_b = ob0.clone(), ob0.clone()
+    if case % 3 == 0:  # untrimmed: scores from the verify pass's statistics
+        ra, ca, ma, ka = sv.verify_update(t, d, tok, ob_a, lr, seed=case, temperature=T,
+                                          vocab=V, score=True, boundary=True)
+        out = sv.VerifyResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                              torch.empty(B, K + 1, dtype=torch.int32, device=DEV))
+        out.boundary = torch.empty(B, dtype=torch.int32, device=DEV)
+        out.draft_stats_out = torch.empty(sv.draft_stats_bytes(B, K), dtype=torch.uint8,
+                                          device=DEV)
+        rb = sv.verify(t, d, tok, seed=case, temperature=T, vocab=V, out=out)
+        cb, mb, kb = sv.av_score_update(out.draft_stats_out, rb.accepted_len, ob_b, lr, B, K)
+        torch.cuda.synchronize()
+        assert torch.equal(ca, cb) and torch.equal(ma, mb) and torch.equal(ka, kb)
+    else:
+        tau = float(rng.uniform(0.02, 0.6))
+        _, _, kept, ds = sv.av_score(d, tok, ob0, tau, temperature=T, vocab=V,
+                                     prefix=case % 2 == 0)
+        ra, _, _, _ = sv.verify_update(t, d, tok, ob_a, lr, seed=case, temperature=T, vocab=V,
+                                       kept_len=kept, draft_stats=ds, boundary=True)
+        rb = sv.verify(t, d, tok, seed=case, temperature=T, vocab=V, kept_len=kept,
+                       draft_stats=ds, boundary=True)
+        sv.av_update(ds, rb.accepted_len, kept, ob_b, lr, B, K)
+        torch.cuda.synchronize()
+    assert torch.equal(ra.accepted_len, rb.accepted_len)
+    assert torch.equal(ra.tokens, rb.tokens) and torch.equal(ra.boundary, rb.boundary)
+    assert torch.equal(ob_a, ob_b)
+
+
 @pytest.mark.parametrize("case", range(12))
 def test_random_av_steps(case):
     # adaptive-verification steps (score, trim at a random tau, verify the kept
