@@ -108,6 +108,27 @@ def test_row_stats_reproducible_and_ordered_ties():
     assert np.array_equal(np_(a["argmax"]), o["argmax"])
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_row_stats_ties_inside_one_thread(dtype):
+    # equal maxima held by one thread: in different chunks of its row and in
+    # different vectors of one chunk (thread 5 and thread 9 at the row pass's
+    # shapes: 768 threads x 2 vectors of 8 bfloat16, 512 threads x 4 vectors
+    # of 4 floats); the lowest id must win
+    block, unroll, epv = (768, 2, 8) if dtype == torch.bfloat16 else (512, 4, 4)
+    chunk = block * unroll
+    V = 3 * chunk * epv + 96  # rows a multiple of 16 bytes
+    x = torch.zeros(3, V, dtype=dtype)
+    ids = [(5 + it * chunk) * epv + 3 for it in range(3)]       # chunks 0, 1, 2 of thread 5
+    x[0, ids[::-1]] = 2.0
+    x[1, [(9 + block) * epv + 1, 9 * epv + 1]] = 2.0             # vectors u = 1 and 0
+    x[2, [ids[2], (9 + block) * epv + 1]] = 2.0                  # two threads, later chunks
+    r = sv.row_stats(x.to(DEV))
+    torch.cuda.synchronize()
+    assert np_(r["argmax"]).tolist() == [ids[0], 9 * epv + 1, (9 + block) * epv + 1]
+    o = ref.rows_stats(host_logits(x), temperature=1.0, V=V, nthreads=NT)
+    assert np.array_equal(np_(r["argmax"]), o["argmax"])
+
+
 def test_read_probe_folds_every_word():
     # the load-only ceiling kernel reads each row's bytes exactly: XOR per row
     g = torch.Generator().manual_seed(3)
