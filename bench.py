@@ -334,7 +334,7 @@ def run_secondary(sv, W, dev, stream, args, only=None):
         ms = _timeit(f, n, warm, stream, torch)
         rows = 256 * 17
         byt = rows * 128256 * 2
-        out["lossless_b256_k8_v128256_bf16"] = _line(ms, rows, byt, res, [256 * 9] * 2)
+        out["lossless_b256_k8_v128256_bf16"] = _line(ms, rows, byt, res, [256 * 9] * 2, n)
         del bs, b0, b1
 
     # lossless, B=1 K=4 V=32000 float32 (latency: a handful of rows)
@@ -349,9 +349,12 @@ def run_secondary(sv, W, dev, stream, args, only=None):
 
         def f0(i):
             calls[i % 4](i)
-        ms = _timeit(f0, n, warm, stream, torch)
+        # a step of a few microseconds: ten times the steps (when not --only),
+        # so that the queue is full and the first calls' launch cost is amortised
+        n0 = n if only else 10 * n
+        ms = _timeit(f0, n0, warm if only else 10 * warm, stream, torch)
         rows = 2 * c["K"] + 1
-        out[c["name"]] = _line(ms, rows, rows * c["V"] * 4, res, [c["K"] + 1] * 4)
+        out[c["name"]] = _line(ms, rows, rows * c["V"] * 4, res, [c["K"] + 1] * 4, n0)
         del sets
 
     # lossless + AV score + one SGD step, B=64 K=5
@@ -367,9 +370,10 @@ def run_secondary(sv, W, dev, stream, args, only=None):
 
         def f1(i):
             calls[i % 4](0)
-        ms = _timeit(f1, n, warm, stream, torch)
+        n1 = n if only else 5 * n
+        ms = _timeit(f1, n1, warm if only else 5 * warm, stream, torch)
         rows = 64 * (2 * K + 1)
-        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res, [64 * (K + 1)] * 4)
+        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res, [64 * (K + 1)] * 4, n1)
         del sets
 
     # lossless at T = 0.7 on V = 152064, B = 512 K = 4
@@ -386,7 +390,7 @@ def run_secondary(sv, W, dev, stream, args, only=None):
             calls[i % 2](0)
         ms = _timeit(f3, n, warm, stream, torch)
         rows = 512 * 9
-        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res, [512 * 5] * 2)
+        out[c["name"]] = _line(ms, rows, rows * c["V"] * 2, res, [512 * 5] * 2, n)
         del sets
 
     # full AV pipeline (score, trimmed verify, update), B=1024 K=8: 20 steps,
@@ -420,7 +424,8 @@ def run_secondary(sv, W, dev, stream, args, only=None):
         verified = [int((k + 1).sum().item()) for k in kept_all]
         drafts_read = [int(torch.clamp(k + 1, max=K).sum().item()) for k in kept_all]
         rows = int(round((sum(verified) + sum(drafts_read)) / len(ran)))
-        line = _line(ms, rows, rows * c["V"] * 2, [res[i] for i in sorted(ran)], verified)
+        line = _line(ms, rows, rows * c["V"] * 2, [res[i] for i in sorted(ran)], verified,
+                     nsteps)
         line["draft_rows_read_per_step"] = round(sum(drafts_read) / len(ran), 1)
         line["draft_rows_per_step"] = 1024 * K
         line["input_sets"] = len(ran)
@@ -500,10 +505,10 @@ def run_next_rows(sv, W, dev, stream, args):
     return out
 
 
-def _line(ms, rows, byt, res, verified_rows):
+def _line(ms, rows, byt, res, verified_rows, steps):
     import torch
     acc = torch.cat([r.accepted_len for r in res if r is not None]).float().mean().item()
-    return {"us_per_step": round(ms * 1e3, 2), "rows_per_step": rows,
+    return {"us_per_step": round(ms * 1e3, 2), "timed_steps": steps, "rows_per_step": rows,
             "rows_per_s": round(rows / (ms * 1e-3), 1), "gbps": round(byt / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "mean_accepted_len": round(acc, 4),
