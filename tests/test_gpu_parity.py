@@ -1019,15 +1019,20 @@ def _random_batch(rng):
     return mode, batch, kept, rng
 
 
-# 24 by default; SPECVERIFY_RANDOM_CASES=N runs the first N of the same seeds
+# The randomised tests run 24, 16 and 12 cases by default.
+# SPECVERIFY_RANDOM_CASES=N runs the first N configuration cases and
+# SPECVERIFY_RANDOM_STEP_CASES=N the first N of each step test; their seeds are
+# a per-test base + SPECVERIFY_RANDOM_OFFSET (default 0) + the case number.
 RANDOM_CASES = int(os.environ.get("SPECVERIFY_RANDOM_CASES", "24"))
+RANDOM_STEP_CASES = os.environ.get("SPECVERIFY_RANDOM_STEP_CASES")
+RANDOM_OFFSET = int(os.environ.get("SPECVERIFY_RANDOM_OFFSET", "0"))
 
 
 @pytest.mark.parametrize("case", range(RANDOM_CASES))
 def test_random_configurations(case):
     # mode, recipe, dtype, B, K (up to 64), V (2 to 200000), padded stride,
     # temperature, kept lengths (some outside [0, K]), FLy threshold and window
-    mode, batch, kept, rng = _random_batch(np.random.default_rng(9000 + case))
+    mode, batch, kept, rng = _random_batch(np.random.default_rng(9000 + RANDOM_OFFSET + case))
     K = batch.tokens.shape[1]
     kept_ref = None if kept is None else kept.clamp(0, K)  # the library clamps into [0, K]
     if mode == "lossless":
@@ -1039,13 +1044,13 @@ def test_random_configurations(case):
         _fly_check(batch, theta=theta, window=window, kept=kept, kept_ref=kept_ref)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(int(RANDOM_STEP_CASES or 16)))
 def test_random_verify_update(case):
     # spec_verify_update on random shapes against the separate calls, bit for
     # bit: untrimmed steps (scores and SGD step from the verify pass's own
     # statistics) and trimmed ones (statistics and kept lengths from
     # spec_av_score), both dtypes, padded strides, random temperatures
-    rng = np.random.default_rng(9100 + case)
+    rng = np.random.default_rng(9100 + RANDOM_OFFSET + case)
     K = int(rng.integers(1, 13)) if case % 5 else 64
     B = int(rng.integers(1, 300)) if K < 64 else int(rng.integers(1, 20))
     V = int(np.exp(rng.uniform(np.log(8), np.log(40000))))
@@ -1089,11 +1094,11 @@ def test_random_verify_update(case):
     assert torch.equal(ob_a, ob_b)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(int(RANDOM_STEP_CASES or 12)))
 def test_random_av_steps(case):
     # adaptive-verification steps (score, trim at a random tau, verify the kept
     # drafts, SGD update) on random shapes, dtypes and temperatures
-    rng = np.random.default_rng(7000 + case)
+    rng = np.random.default_rng(7000 + RANDOM_OFFSET + case)
     K = int(rng.integers(1, 13)) if case % 4 else 64
     B = int(rng.integers(1, 65)) if K < 64 else int(rng.integers(1, 6))
     V = int(np.exp(rng.uniform(np.log(8), np.log(60000))))
