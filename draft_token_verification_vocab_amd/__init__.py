@@ -150,11 +150,52 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError("logits must be bfloat16 or float32, got %s" % t.dtype)
 
 
-def _need_cuda(t: torch.Tensor, name: str):
+def _need_cuda(t: torch.Tensor, name: str, device=None, dtype=None, shape=None,
+               nbytes: Optional[int] = None):
+    """Raise unless t is a contiguous GPU tensor (on device, of dtype and
+    shape, holding at least nbytes bytes, where given): the library reads and
+    writes through raw device pointers, so a host tensor, another GPU's or a
+    short buffer would fault the kernel instead of failing here."""
     if not t.is_cuda:
         raise ValueError("%s must be a GPU tensor" % name)
+    if device is not None and t.device != torch.device(device):
+        raise ValueError("%s must be on %s, not %s" % (name, device, t.device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, not %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s must hold at least %d bytes" % (name, nbytes))
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_labels(dev, B, K, draft_stats, accepted_len, kept_len, omega_beta):
+    """The estimator's inputs for a batch of B sequences of K drafts on dev."""
+    _need_cuda(draft_stats, "draft_stats", dev, nbytes=draft_stats_bytes(B, K))
+    if accepted_len is not None:
+        _need_cuda(accepted_len, "accepted_len", dev, torch.int32, (B,))
+    if kept_len is not None:
+        _need_cuda(kept_len, "kept_len", dev, torch.int32, (B,))
+    _need_cuda(omega_beta, "omega_beta", dev, torch.float32, (K + 1,))
+
+
+def _check_inputs(dev, B, K, S, dtype, draft, draft_tokens, kept_len, draft_stats, workspace):
+    """The verification inputs besides the target logits, against a batch of
+    B sequences of K drafts with row stride S on device dev."""
+    if draft is not None:
+        _need_cuda(draft, "draft", dev, dtype, (B, K, S))
+    _need_cuda(draft_tokens, "draft_tokens", dev, torch.int32, (B, K))
+    if kept_len is not None:
+        _need_cuda(kept_len, "kept_len", dev, torch.int32, (B,))
+    if draft_stats is not None:
+        _need_cuda(draft_stats, "draft_stats", dev, nbytes=draft_stats_bytes(B, K))
+    if workspace is not None:
+        _need_cuda(workspace, "workspace", dev)
 
 
 def _params(B, K, V, stride, dtype, temperature, theta=0.0, window=0) -> _Params:
@@ -187,6 +228,22 @@ class VerifyResult:
     # uint32 [B] (as int32): each sequence's boundary-case bits (NEAR_* above)
     boundary: Optional[torch.Tensor] = None
 
+    def check(self, B: int, K: int, device):
+        """Raise unless every output given fits a batch of B sequences of K drafts."""
+        i32, f32 = torch.int32, torch.float32
+        for name, dt, shape in (("accepted_len", i32, (B,)), ("tokens", i32, (B, K + 1)),
+                                ("target_lse", f32, (B, K + 1)),
+                                ("target_entropy", f32, (B, K + 1)),
+                                ("target_argmax", i32, (B, K + 1)), ("draft_lse", f32, (B, K)),
+                                ("draft_qmax", f32, (B, K)), ("draft_feat", f32, (B, K)),
+                                ("boundary", i32, (B,))):
+            t = getattr(self, name)
+            if t is not None:
+                _need_cuda(t, name, device, dt, shape)
+        if self.draft_stats_out is not None:
+            _need_cuda(self.draft_stats_out, "draft_stats_out", device,
+                       nbytes=draft_stats_bytes(B, K))
+
     def fields(self):
         """The output pointers in the order of spec_verify_out."""
         return _VerifyOut(*[None if t is None else t.data_ptr() for t in (
@@ -211,17 +268,9 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
     K = K1 - 1
     V = S if vocab is None else int(vocab)
     dt = _dtype_code(target)
-    if draft is not None:
-        _need_cuda(draft, "draft")
-        if draft.shape != (B, K, S) or draft.dtype != target.dtype:
-            raise ValueError("draft must be [B, K, S] with the target's dtype")
-    _need_cuda(draft_tokens, "draft_tokens")
-    if draft_tokens.dtype != torch.int32 or draft_tokens.shape != (B, K):
-        raise ValueError("draft_tokens must be int32 [B, K]")
-    for t, n in ((kept_len, "kept_len"), (draft_stats, "draft_stats")):
-        if t is not None:
-            _need_cuda(t, n)
     dev = target.device
+    _check_inputs(dev, B, K, S, target.dtype, draft, draft_tokens, kept_len, draft_stats,
+                  workspace)
     p = _params(B, K, V, S, dt, temperature, fly_theta, fly_window)
     L = load()
     if out is None:
@@ -237,6 +286,8 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
                 out.draft_feat = torch.empty(B, K, dtype=torch.float32, device=dev)
         if boundary:
             out.boundary = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        out.check(B, K, dev)
     o = out.fields()
     need = int(L.spec_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
@@ -244,7 +295,7 @@ def verify(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: to
     _check(L.spec_verify(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(kept_len),
                          _ptr(draft_stats), ctypes.c_uint64(int(seed) & (2**64 - 1)), int(mode),
                          ctypes.byref(p), ctypes.byref(o), _ptr(workspace),
-                         workspace.numel(), _stream(dev)), "spec_verify")
+                         _nbytes(workspace), _stream(dev)), "spec_verify")
     return out
 
 
@@ -260,24 +311,17 @@ def verify_update(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch
     Returns (VerifyResult, conf, keep_mask, kept_len_out); the last three are
     None unless score.  omega_beta is updated in place."""
     _need_cuda(target, "target")
-    _need_cuda(draft, "draft")
-    _need_cuda(draft_tokens, "draft_tokens")
-    _need_cuda(omega_beta, "omega_beta")
     B, K1, S = target.shape
     K = K1 - 1
     V = S if vocab is None else int(vocab)
-    if draft.shape != (B, K, S) or draft.dtype != target.dtype:
-        raise ValueError("draft must be [B, K, S] with the target's dtype")
-    if draft_tokens.dtype != torch.int32 or draft_tokens.shape != (B, K):
-        raise ValueError("draft_tokens must be int32 [B, K]")
-    if omega_beta.dtype != torch.float32 or omega_beta.numel() != K + 1:
-        raise ValueError("omega_beta must be float32 [K+1]")
-    for t, n in ((kept_len, "kept_len"), (draft_stats, "draft_stats")):
-        if t is not None:
-            _need_cuda(t, n)
+    dev = target.device
+    if draft is None:
+        raise ValueError("verify_update is lossless: it needs the draft logits")
+    _check_inputs(dev, B, K, S, target.dtype, draft, draft_tokens, kept_len, draft_stats,
+                  workspace)
+    _need_cuda(omega_beta, "omega_beta", dev, torch.float32, (K + 1,))
     if score and (kept_len is not None or draft_stats is not None):
         raise ValueError("score needs an untrimmed step: no kept_len, no draft_stats")
-    dev = target.device
     p = _params(B, K, V, S, _dtype_code(target), temperature)
     L = load()
     out = VerifyResult(torch.empty(B, dtype=torch.int32, device=dev),
@@ -297,7 +341,7 @@ def verify_update(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch
                                 _ptr(draft_stats), ctypes.c_uint64(int(seed) & (2**64 - 1)),
                                 ctypes.byref(p), ctypes.byref(o), float(lr), _ptr(omega_beta),
                                 _ptr(conf), _ptr(mask), _ptr(kept), _ptr(workspace),
-                                workspace.numel(), _stream(dev)), "spec_verify_update")
+                                _nbytes(workspace), _stream(dev)), "spec_verify_update")
     return out, conf, mask, kept
 
 
@@ -319,6 +363,8 @@ class VerifyCall:
         K = K1 - 1
         V = S if vocab is None else int(vocab)
         dev = target.device
+        _check_inputs(dev, B, K, S, target.dtype, draft, draft_tokens, kept_len, draft_stats,
+                      workspace)
         self.L = load()
         self.params = _params(B, K, V, S, _dtype_code(target), temperature, fly_theta,
                               fly_window)
@@ -327,6 +373,7 @@ class VerifyCall:
                                torch.empty(B, K + 1, dtype=torch.int32, device=dev))
         if boundary and out.boundary is None:
             out.boundary = torch.empty(B, dtype=torch.int32, device=dev)
+        out.check(B, K, dev)
         self.out = out
         self.vout = out.fields()
         need = int(self.L.spec_workspace_bytes(ctypes.byref(self.params)))
@@ -335,7 +382,7 @@ class VerifyCall:
         self._keep = (target, draft, draft_tokens, kept_len, draft_stats, workspace)
         self.args = [_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(kept_len),
                      _ptr(draft_stats), ctypes.c_uint64(0), int(mode), ctypes.byref(self.params),
-                     ctypes.byref(self.vout), _ptr(workspace), workspace.numel(), _stream(dev)]
+                     ctypes.byref(self.vout), _ptr(workspace), _nbytes(workspace), _stream(dev)]
 
     def __call__(self, seed: int = 0) -> VerifyResult:
         self.args[5] = ctypes.c_uint64(int(seed) & (2**64 - 1))
@@ -354,12 +401,8 @@ def av_score(draft: torch.Tensor, draft_tokens: torch.Tensor, omega_beta: torch.
     B, K, S = draft.shape
     V = S if vocab is None else int(vocab)
     dev = draft.device
-    _need_cuda(omega_beta, "omega_beta")
-    if omega_beta.dtype != torch.float32 or omega_beta.numel() != K + 1:
-        raise ValueError("omega_beta must be float32 [K+1]")
-    _need_cuda(draft_tokens, "draft_tokens")
-    if draft_tokens.dtype != torch.int32 or draft_tokens.shape != (B, K):
-        raise ValueError("draft_tokens must be int32 [B, K]")
+    _need_cuda(omega_beta, "omega_beta", dev, torch.float32, (K + 1,))
+    _need_cuda(draft_tokens, "draft_tokens", dev, torch.int32, (B, K))
     p = _params(B, K, V, S, _dtype_code(draft), temperature)
     L = load()
     conf = torch.empty(B, K, dtype=torch.float32, device=dev)
@@ -368,8 +411,8 @@ def av_score(draft: torch.Tensor, draft_tokens: torch.Tensor, omega_beta: torch.
     need = int(L.spec_draft_stats_bytes(B, K))
     if draft_stats is None:
         draft_stats = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    elif draft_stats.numel() * draft_stats.element_size() < need:
-        raise ValueError("draft_stats must hold spec_draft_stats_bytes(B, K) = %d bytes" % need)
+    else:
+        _need_cuda(draft_stats, "draft_stats", dev, nbytes=need)
     fn = L.spec_av_score_prefix if prefix else L.spec_av_score
     _check(fn(_ptr(draft), _ptr(draft_tokens), ctypes.byref(p), _ptr(omega_beta), float(tau),
               _ptr(conf), _ptr(mask), _ptr(kept), _ptr(draft_stats), _stream(dev)),
@@ -382,11 +425,9 @@ def av_score_stats(draft_stats: torch.Tensor, B: int, K: int, omega_beta: torch.
     """Confidences and trimming from an already filled draft-statistics buffer
     (no row is read).  Returns (conf [B,K] float, keep_mask [B,K] uint8,
     kept_len [B] int32)."""
-    for t, n in ((draft_stats, "draft_stats"), (omega_beta, "omega_beta")):
-        _need_cuda(t, n)
-    if draft_stats.numel() * draft_stats.element_size() < draft_stats_bytes(B, K):
-        raise ValueError("draft_stats must hold spec_draft_stats_bytes(B, K) bytes")
+    _need_cuda(draft_stats, "draft_stats")
     dev = draft_stats.device
+    _check_labels(dev, B, K, draft_stats, None, None, omega_beta)
     conf = torch.empty(B, K, dtype=torch.float32, device=dev)
     mask = torch.empty(B, K, dtype=torch.uint8, device=dev)
     kept = torch.empty(B, dtype=torch.int32, device=dev)
@@ -426,6 +467,9 @@ class AvStepCall:
         B, K, S = draft.shape
         V = S if vocab is None else int(vocab)
         dev = draft.device
+        _need_cuda(target, "target", dev, draft.dtype, (B, K + 1, S))
+        _check_inputs(dev, B, K, S, draft.dtype, None, draft_tokens, None, None, workspace)
+        _need_cuda(omega_beta, "omega_beta", dev, torch.float32, (K + 1,))
         L = load()
         self.L = L
         self.conf = torch.empty(B, K, dtype=torch.float32, device=dev)
@@ -496,12 +540,9 @@ def av_score_update(draft_stats: torch.Tensor, accepted_len: torch.Tensor,
     at the current coefficients (every draft kept), then one SGD step, in one
     launch.  Returns (conf [B,K] float, keep_mask [B,K] uint8, kept_len [B]
     int32); omega_beta is updated in place."""
-    for t, n in ((draft_stats, "draft_stats"), (accepted_len, "accepted_len"),
-                 (omega_beta, "omega_beta")):
-        _need_cuda(t, n)
-    if draft_stats.numel() * draft_stats.element_size() < draft_stats_bytes(B, K):
-        raise ValueError("draft_stats must hold spec_draft_stats_bytes(B, K) bytes")
+    _need_cuda(draft_stats, "draft_stats")
     dev = draft_stats.device
+    _check_labels(dev, B, K, draft_stats, accepted_len, None, omega_beta)
     conf = torch.empty(B, K, dtype=torch.float32, device=dev)
     mask = torch.empty(B, K, dtype=torch.uint8, device=dev)
     kept = torch.empty(B, dtype=torch.int32, device=dev)
@@ -515,11 +556,8 @@ def av_update(draft_stats: torch.Tensor, accepted_len: torch.Tensor,
               kept_len: Optional[torch.Tensor], omega_beta: torch.Tensor, lr: float, B: int,
               K: int) -> torch.Tensor:
     """One SGD step of the estimator; omega_beta (float32 [K+1]) is updated in place."""
-    for t, n in ((draft_stats, "draft_stats"), (accepted_len, "accepted_len"),
-                 (omega_beta, "omega_beta")):
-        _need_cuda(t, n)
-    if kept_len is not None:
-        _need_cuda(kept_len, "kept_len")
+    _need_cuda(draft_stats, "draft_stats")
+    _check_labels(draft_stats.device, B, K, draft_stats, accepted_len, kept_len, omega_beta)
     _check(load().spec_av_update(_ptr(draft_stats), _ptr(accepted_len), _ptr(kept_len), int(B),
                                  int(K), float(lr), _ptr(omega_beta),
                                  _stream(omega_beta.device)), "spec_av_update")
@@ -559,6 +597,8 @@ def read_probe(logits: torch.Tensor, *, row_bytes: Optional[int] = None,
     rb = stride_b if row_bytes is None else int(row_bytes)
     if sink is None:
         sink = torch.empty(rows, dtype=torch.int32, device=x.device)
+    else:
+        _need_cuda(sink, "sink", x.device, torch.int32, (rows,))
     _check(load().spec_read_probe(_ptr(x), rows, rb, stride_b, _ptr(sink), _stream(x.device)),
            "spec_read_probe")
     return sink
@@ -578,9 +618,8 @@ def irls_accumulate(state: torch.Tensor, draft_stats: torch.Tensor, accepted_len
                     kept_len: Optional[torch.Tensor], omega_beta: torch.Tensor, B: int,
                     K: int) -> torch.Tensor:
     """Add one step's labels to the round's gradient and Hessian."""
-    for t, n in ((state, "state"), (draft_stats, "draft_stats"), (accepted_len, "accepted_len"),
-                 (omega_beta, "omega_beta")):
-        _need_cuda(t, n)
+    _need_cuda(state, "state", nbytes=load().spec_irls_state_bytes(int(K)))
+    _check_labels(state.device, B, K, draft_stats, accepted_len, kept_len, omega_beta)
     _check(load().spec_irls_accumulate(_ptr(draft_stats), _ptr(accepted_len), _ptr(kept_len),
                                        int(B), int(K), _ptr(omega_beta), _ptr(state),
                                        _stream(state.device)), "spec_irls_accumulate")
@@ -590,8 +629,10 @@ def irls_accumulate(state: torch.Tensor, draft_stats: torch.Tensor, accepted_len
 def irls_solve(state: torch.Tensor, omega_beta: torch.Tensor, K: int, c_damp: float,
                flags: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Solve the round's Newton system, update omega_beta in place, zero the state."""
-    _need_cuda(state, "state")
-    _need_cuda(omega_beta, "omega_beta")
+    _need_cuda(state, "state", nbytes=load().spec_irls_state_bytes(int(K)))
+    _need_cuda(omega_beta, "omega_beta", state.device, torch.float32, (K + 1,))
+    if flags is not None:
+        _need_cuda(flags, "flags", state.device, torch.int32, nbytes=4)
     _check(load().spec_irls_solve(_ptr(state), int(K), float(c_damp), _ptr(omega_beta),
                                   _ptr(flags), _stream(state.device)), "spec_irls_solve")
     return omega_beta
@@ -603,15 +644,21 @@ def av_diagnostics(draft_stats: torch.Tensor, accepted_len: torch.Tensor,
                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """AUC, mean log-loss, ECE and label count of the estimator on one batch
     (float64 device tensor of 4)."""
+    _need_cuda(draft_stats, "draft_stats")
     dev = draft_stats.device
+    _check_labels(dev, B, K, draft_stats, accepted_len, kept_len, omega_beta)
     if out is None:
         out = torch.empty(4, dtype=torch.float64, device=dev)
+    else:
+        _need_cuda(out, "out", dev, torch.float64, (4,))
     n = load().spec_av_diagnostics_workspace_bytes(int(B), int(K), int(nbins))
     if workspace is None:
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    else:
+        _need_cuda(workspace, "workspace", dev)
     _check(load().spec_av_diagnostics(_ptr(draft_stats), _ptr(accepted_len), _ptr(kept_len),
                                       int(B), int(K), _ptr(omega_beta), int(nbins), _ptr(out),
-                                      _ptr(workspace), workspace.numel(), _stream(dev)),
+                                      _ptr(workspace), _nbytes(workspace), _stream(dev)),
            "spec_av_diagnostics")
     return out
 
@@ -620,10 +667,10 @@ def av_budget(conf: torch.Tensor, cost: torch.Tensor, n_requests: Optional[float
               mask: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
     """Budgeted trimming of a [B, K] confidence tensor against a float64 cost
     table of B*K+1 entries: kept_len [B], keep mask, budget and best ratio."""
-    _need_cuda(conf, "conf")
-    _need_cuda(cost, "cost")
+    _need_cuda(conf, "conf", dtype=torch.float32)
     B, K = conf.shape
     dev = conf.device
+    _need_cuda(cost, "cost", dev, torch.float64, (B * K + 1,))
     res = {"kept_len": torch.empty(B, dtype=torch.int32, device=dev),
            "mask": torch.empty(B, K, dtype=torch.uint8, device=dev) if mask else None,
            "budget": torch.empty(1, dtype=torch.int64, device=dev),
@@ -632,9 +679,11 @@ def av_budget(conf: torch.Tensor, cost: torch.Tensor, n_requests: Optional[float
     if workspace is None:
         n = load().spec_av_budget_workspace_bytes(int(B), int(K))
         workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+    else:
+        _need_cuda(workspace, "workspace", dev)
     _check(load().spec_av_budget(_ptr(conf), int(B), int(K), _ptr(cost), nr,
                                  _ptr(res["kept_len"]), _ptr(res["mask"]), _ptr(res["budget"]),
-                                 _ptr(res["best_ratio"]), _ptr(workspace), workspace.numel(),
+                                 _ptr(res["best_ratio"]), _ptr(workspace), _nbytes(workspace),
                                  _stream(dev)), "spec_av_budget")
     return res
 
@@ -642,10 +691,10 @@ def av_budget(conf: torch.Tensor, cost: torch.Tensor, n_requests: Optional[float
 def ngram_propose(context: torch.Tensor, lengths: torch.Tensor, n_min: int, n_max: int,
                   K: int) -> dict:
     """Prompt-lookup drafts for int32 contexts [B, S] of the given lengths."""
-    _need_cuda(context, "context")
-    _need_cuda(lengths, "lengths")
+    _need_cuda(context, "context", dtype=torch.int32)
     B, S = context.shape
     dev = context.device
+    _need_cuda(lengths, "lengths", dev, torch.int32, (B,))
     res = {"draft": torch.empty(B, K, dtype=torch.int32, device=dev),
            "draft_len": torch.empty(B, dtype=torch.int32, device=dev),
            "match_pos": torch.empty(B, dtype=torch.int32, device=dev),

@@ -985,6 +985,57 @@ def test_invalid_arguments_raise():
         sv.verify(t[:, :, :62].contiguous(), d[:, :, :62].contiguous(), tok, seed=0)  # 248 B rows
 
 
+def test_binding_rejects_buffers_the_kernels_would_overrun():
+    # the library takes raw device pointers: a host tensor, a short buffer or
+    # another element type must fail in the binding, before any launch
+    B, K, V = 2, 2, 64
+    t = torch.zeros(B, K + 1, V, device=DEV)
+    d = torch.zeros(B, K, V, device=DEV)
+    tok = torch.zeros(B, K, dtype=torch.int32, device=DEV)
+    ob = torch.zeros(K + 1, dtype=torch.float32, device=DEV)
+    need = sv.workspace_bytes(B, K, V, dtype=sv.DTYPE_F32)
+    bad = [
+        dict(workspace=torch.empty(need, dtype=torch.uint8)),                  # host memory
+        dict(kept_len=torch.zeros(B, dtype=torch.int64, device=DEV)),          # int64
+        dict(kept_len=torch.zeros(B - 1, dtype=torch.int32, device=DEV)),      # short
+        dict(draft_stats=torch.zeros(sv.draft_stats_bytes(B, K) - 1, dtype=torch.uint8,
+                                     device=DEV)),                             # short
+        dict(out=sv.VerifyResult(torch.empty(B, dtype=torch.int32, device=DEV),
+                                 torch.empty(B, K, dtype=torch.int32, device=DEV))),  # [B, K]
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            sv.verify(t, d, tok, seed=0, **kw)
+    with pytest.raises(ValueError):
+        sv.verify(t, d, tok.long(), seed=0)
+    with pytest.raises(ValueError):
+        sv.verify_update(t, d, tok, ob[:K], 0.1)                               # [K] coefficients
+    with pytest.raises(ValueError):
+        sv.VerifyCall(t, d, tok, draft_stats=torch.zeros(8, dtype=torch.uint8, device=DEV))
+    ds = torch.zeros(sv.draft_stats_bytes(B, K), dtype=torch.uint8, device=DEV)
+    acc = torch.zeros(B, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        sv.av_update(ds, acc.long(), None, ob, 0.1, B, K)
+    with pytest.raises(ValueError):
+        sv.av_update(ds[:-1], acc, None, ob, 0.1, B, K)
+    with pytest.raises(ValueError):
+        sv.av_score_update(ds, acc, ob.double(), 0.1, B, K)
+    st = sv.irls_state(K, DEV)
+    with pytest.raises(ValueError):
+        sv.irls_accumulate(st[:-1], ds, acc, None, ob, B, K)
+    with pytest.raises(ValueError):
+        sv.av_diagnostics(ds, acc, None, ob, B, K, out=torch.empty(4, device=DEV))  # float32
+    conf = torch.full((B, K), 0.5, device=DEV)
+    cost = torch.from_numpy(W.budget_costs(B, K)).to(DEV)
+    with pytest.raises(ValueError):
+        sv.av_budget(conf, cost.float())
+    with pytest.raises(ValueError):
+        sv.av_budget(conf, cost[:-1])
+    with pytest.raises(ValueError):
+        sv.ngram_propose(tok, torch.zeros(B, dtype=torch.int64, device=DEV), 1, 2, 3)
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------------------
 # Randomised configurations: every option at once, drawn from fixed seeds
 # ---------------------------------------------------------------------------
