@@ -21,6 +21,9 @@
  *  - Pointers named as device pointers must point to HIP device memory (or
  *    memory the device can read).  The library allocates nothing: every
  *    buffer, including scratch ("workspace"), belongs to the caller.
+ *  - Apart from the workspaces, whose sizes are arguments, the library cannot
+ *    see a device buffer's size: each must hold the elements its description
+ *    gives, or a kernel reads or writes past its end.
  *  - Logits are rows of `vocab` values, row r of a tensor starting at
  *    base + r*row_stride elements.  dtype SPEC_DTYPE_F32 (float) or
  *    SPEC_DTYPE_BF16 (bfloat16 bit patterns).  The base pointer must be
@@ -42,7 +45,11 @@
  * Randomness: Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit seed,
  * counter (x>>2, position, sequence, stream tag), output word x&3; a draw r
  * becomes u = (2*(r>>9)+1) * 2^-24.  The accept test at position j uses
- * x = 0 and tag 1; the sampling race uses x = the vocabulary id and tag 2.
+ * x = 0 and tag 1.  The sampling race gives vocabulary id x the 32-bit word
+ * whose high 16 bits are half x&1 (the low half for even x) of word
+ * (x>>1)&3 of the block at counter (x>>3, position, sequence, 3), and whose
+ * low 16 bits are the high half of the tag-2 draw for x; u is formed from
+ * that word the same way.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
