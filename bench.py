@@ -254,6 +254,9 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(sets[0], cfg, args.cpu_seconds)
+        if not args.no_secondary:
+            log("timing the oracle beside the other workloads")
+            cpu["beside"] = oracle_beside(W, cpu["cores"], args.cpu_seconds / 12)
 
     res = {
         "metric": METRIC, "value": round(rows_per_s, 1), "unit": "rows/s", "n_gpus": 1,
@@ -567,6 +570,97 @@ def cpu_baseline(batch, cfg, budget_s):
             "gbps": round(rows * reps * row_bytes / total / 1e9, 3),
             "single_thread_rows_per_s": round(n1 * (cfg["K"] + 1) / dt1, 1),
             "host_cpu": _cpu_model(), "host_logical_cpus": os.cpu_count()}
+
+
+def oracle_beside(W, threads, budget_s):
+    """The oracle (as it stands) timed beside the other figures of this line:
+    one step of each secondary workload on a sample of its sequences
+    (generated on the host with the same recipe), scaled to the whole batch,
+    and the estimator calls of `secondary.next_rows` at their own shapes.
+    Each is repeated for about budget_s seconds."""
+    import numpy as np
+    import torch
+    from oracle import ref
+
+    def host(x):  # bfloat16 logits go to the oracle as their bit patterns
+        x = x.contiguous()
+        return x.view(torch.int16).numpy().view("uint16") if x.dtype == torch.bfloat16 \
+            else x.numpy()
+
+    def step_seconds(make_batch, run, B):
+        # at most 32 sequences (generating more on the host would cost more
+        # than timing them), repeated until budget_s; seconds per run
+        n = min(B, 32)
+        b = make_batch(n)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            run(b)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s:
+                return n, dt / reps
+
+    def lossless(b):
+        return ref.verify(host(b.target), host(b.draft), b.tokens.numpy(), 0,
+                          temperature=b.temperature, V=b.V, nthreads=threads)
+
+    def av_step(cfg):
+        a = W.CONFIGS[cfg]["av"]
+        ob = np.asarray(W.av_init(cfg), dtype=np.float64)
+
+        def run(b):
+            Bn, K = b.tokens.shape
+            d = host(b.draft)
+            st = ref.rows_stats(d.reshape(Bn * K, -1), temperature=b.temperature, V=b.V,
+                                nthreads=threads)
+            feat = st["feat"].reshape(Bn, K)
+            _, _, kept, _ = ref.av_score(feat, ob, a["tau"])
+            o = ref.verify(host(b.target), d, b.tokens.numpy(), 0, temperature=b.temperature,
+                           V=b.V, kept_len=kept, nthreads=threads)
+            ref.av_update(feat, o["accepted_len"], kept, ob, a["lr"])
+        return run
+
+    out = {}
+    cases = [("lossless_b256_k8_v128256_bf16", 256,
+              lambda n: W.gaussian(n, 8, 128256, "bf16", 1.0, seed=77, token_seed=0), lossless)]
+    for ci, run in ((0, lossless), (1, av_step(1)), (3, lossless), (4, av_step(4))):
+        c = W.CONFIGS[ci]
+        cases.append((c["name"], c["B"], lambda n, ci=ci: W.make(ci, B=n), run))
+    for name, B, make_batch, run in cases:
+        n, dt = step_seconds(make_batch, run, B)
+        out[name] = {"sample_sequences": n, "batch_sequences": B,
+                     "oracle_us_per_step": round(dt * B / n * 1e6, 1)}
+
+    # the estimator calls at the shapes bench.py times them on the GPU
+    B, K = 1024, 8
+    rng = np.random.default_rng(4242)
+    feat = rng.normal(-1.2, 1.3, (B, K))
+    kept = rng.integers(0, K + 1, B).astype(np.int32)
+    acc = np.minimum(rng.integers(0, K + 1, B), kept).astype(np.int32)
+    ob = np.asarray(W.av_init(4), dtype=np.float64)
+
+    def per_call(fn):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s / 4 or reps >= 1000:
+                return round(dt / reps * 1e6, 1)
+    st = ref.IrlsState(K)
+    calls = {"irls_accumulate_b1024_k8": lambda: ref.irls_accumulate(st, feat, acc, kept, ob),
+             "irls_solve_k8": lambda: ref.irls_solve(st, ob, 10.0),
+             "sgd_update_b1024_k8": lambda: ref.av_update(feat, acc, kept, ob, 0.05),
+             "diagnostics_b1024_k8": lambda: ref.av_diagnostics(feat, acc, kept, ob, 10)}
+    for Bb in (1024, 2048):
+        conf = rng.uniform(0.02, 1.0, (Bb, K)).astype(np.float32)
+        cost = W.budget_costs(Bb, K)
+        calls["budget_b%d_k8" % Bb] = lambda conf=conf, cost=cost: ref.av_budget(conf, cost)
+    ctx, lens = W.ngram_contexts(256, 8192, 128256, seed=7, device="cpu")
+    ctx, lens = ctx.numpy(), lens.numpy()
+    calls["ngram_b256_s8192_n2to4_k8"] = lambda: ref.ngram_propose(ctx, lens, 2, 4, 8)
+    out["next_rows_oracle_us_per_call"] = {k: per_call(f) for k, f in calls.items()}
+    return out
 
 
 def _cpu_model():
